@@ -1,0 +1,375 @@
+"""Plain fp64 CPU oracle for the KVSlimmer asymmetric KV-merge path.
+
+TEST INFRASTRUCTURE ONLY.  This module is imported by ``tests/``, by
+``__graft_entry__.smoke()`` and by the ``cpu_baseline`` leg of ``bench.py``;
+nothing in the product package may import or call it.  It shares no code with
+the HIP path: no kernels, no helpers, no constants.  Everything here is plain
+NumPy in float64, written straight from the pages, slow on purpose so that a
+reader can check every step against the formulas by eye.
+
+Sources (cited by page title and section; the pages print no equation numbers
+except the figure-2 caption's "Eq. 8"):
+
+* [DD]  "论文专题讲解：KVSlimmer：非对称 KV 合并的数学与工程"
+        (charles2530.github.io deep-dive).  Sections used:
+        数学主线一 (spectral asymmetry), 数学主线二 (why a Hessian),
+        数学主线三 (exact Hessian), 数学主线四 (forward-only weights),
+        算一遍 (KV size arithmetic), 实验设置 (setting table),
+        工程上怎么用 (sinks and recent window), 局限与边界 (uniform ratio,
+        local adjacent merging).
+* [ABS] KVSlimmer abstract, arXiv 2603.00907 (fugumt.com and
+        thelatestinai.com pages), and the figure-2 caption there ("Eq. 8").
+* [ASYM] AsymKV abstract ("Homogeneous Keys, Heterogeneous Values"), in the
+        related-papers list of the fugumt.com page: keys are merged, values
+        are compressed losslessly.
+
+Readings of points the pages leave open are listed next to the function that
+takes them; the same list sits in the design doc.
+
+Pinned functions (tests/test_oracle_pins.py): every public function below is
+checked against something other than itself: finite differences, brute-force
+minimisation, closed forms, textbook/library routines, exact invariants or the
+numbers the pages print.  Parity unpinned (true to the pages only by argument):
+the multi-query aggregation of the Hessian norms (reading O2), the pair
+selection policy (O6/O7) and the degenerate-denominator threshold (O10); each
+is marked "parity unpinned" below.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F64 = np.float64
+
+# Relative size below which the closed-form denominator is treated as
+# degenerate and the plain average is used instead (reading O10).
+DEGENERATE_REL = 1e-6
+
+
+# ---------------------------------------------------------------------------
+# 数学主线一: spectral view of adjacent similarity
+# ---------------------------------------------------------------------------
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    """Cosine similarity of two vectors, the quantity whose per-mode split is
+    [DD] 数学主线一 (the cos(y_t, y_{t+1}) equation) and [ABS] figure-2 "Eq. 8".
+
+    Reading O9 (pages silent): if either norm is zero the cosine is 1 when the
+    two vectors are equal (both zero) and 0 otherwise.
+    """
+    a = np.asarray(a, F64)
+    b = np.asarray(b, F64)
+    na = math.sqrt(float(a @ a))
+    nb = math.sqrt(float(b @ b))
+    if na == 0.0 or nb == 0.0:
+        return 1.0 if np.array_equal(a, b) else 0.0
+    return float(a @ b) / (na * nb)
+
+
+def spectral_mode_contributions(x_t: np.ndarray, x_t1: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Per-mode contributions c_i to cos(y_t, y_{t+1}) for y = x W.
+
+    [DD] 数学主线一: M = W Wᵀ = U Λ Uᵀ, p_{t,i} = x_t u_i,
+    x_t M x_{t+1}ᵀ = Σ_i λ_i p_{t,i} p_{t+1,i}, and
+    cos(y_t, y_{t+1}) = Σ_i λ_i p_{t,i} p_{t+1,i} /
+                        (sqrt(Σ_i λ_i p_{t,i}²) sqrt(Σ_i λ_i p_{t+1,i}²)) = Σ_i c_i.
+    Returns c (one entry per eigen-mode, ordered as numpy.linalg.eigh returns
+    them).  The identity Σ c_i = cosine(x_t W, x_{t+1} W) is a pin.
+    """
+    x_t = np.asarray(x_t, F64)
+    x_t1 = np.asarray(x_t1, F64)
+    W = np.asarray(W, F64)
+    M = W @ W.T
+    lam, U = np.linalg.eigh(M)
+    p_t = x_t @ U
+    p_t1 = x_t1 @ U
+    den = math.sqrt(float(np.sum(lam * p_t * p_t))) * math.sqrt(float(np.sum(lam * p_t1 * p_t1)))
+    return lam * p_t * p_t1 / den
+
+
+# ---------------------------------------------------------------------------
+# 数学主线三: single-query attention, gradient and exact Hessian blocks
+# ---------------------------------------------------------------------------
+def attention_forward(K: np.ndarray, V: np.ndarray, q: np.ndarray, scale: float,
+                      n: np.ndarray | None = None):
+    """Single-query softmax attention, [DD] 数学主线三 first equation:
+    e_i = q k_iᵀ / sqrt(d_k), α = softmax(e), o = Σ_t α_t v_t.
+
+    ``scale`` is 1/sqrt(d_k) (reading O5: d_k = head_dim).  With slot counts
+    ``n`` (reading O1, see ``merge_values``) the logit of slot i gets + ln n_i
+    and v_i is the slot's mean value; n = None means every slot holds one
+    token.  Returns (e, alpha, o).
+    """
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    q = np.asarray(q, F64)
+    e = scale * (K @ q)
+    if n is not None:
+        e = e + np.log(np.asarray(n, F64))
+    mx = np.max(e)
+    w = np.exp(e - mx)
+    alpha = w / np.sum(w)
+    o = alpha @ V
+    return e, alpha, o
+
+
+def key_gradient(alpha: np.ndarray, V: np.ndarray, o: np.ndarray, q: np.ndarray,
+                 E: np.ndarray, i: int, scale: float) -> np.ndarray:
+    """g_i = ∇_{k_i} L = (1/sqrt(d_k)) α_i [Eᵀ(v_i − o)] q, with E = ∂L/∂o
+    ([DD] 数学主线三, key-gradient equation).  Test pin only: needs E."""
+    V = np.asarray(V, F64)
+    return scale * alpha[i] * float(np.asarray(E, F64) @ (V[i] - o)) * np.asarray(q, F64)
+
+
+def ds_de(alpha: np.ndarray, V: np.ndarray, o: np.ndarray, i: int, j: int) -> np.ndarray:
+    """∂s_i/∂e_j for s_i = α_i (v_i − o), [DD] 数学主线三:
+    diagonal  ∂s_i/∂e_i = α_i (1 − 2α_i)(v_i − o);
+    off-diag  ∂s_i/∂e_j = −α_i α_j (v_i + v_j − 2o), i ≠ j."""
+    V = np.asarray(V, F64)
+    if i == j:
+        return alpha[i] * (1.0 - 2.0 * alpha[i]) * (V[i] - o)
+    return -alpha[i] * alpha[j] * (V[i] + V[j] - 2.0 * o)
+
+
+def hessian_block(alpha: np.ndarray, V: np.ndarray, o: np.ndarray, q: np.ndarray,
+                  E: np.ndarray, i: int, j: int, scale: float) -> np.ndarray:
+    """h_ij = ∂g_i/∂k_jᵀ = (1/d_k) [Eᵀ ∂s_i/∂e_j] q qᵀ ([DD] 数学主线三,
+    unified Hessian-block form; scale² = 1/d_k).  Test pin only."""
+    q = np.asarray(q, F64)
+    return scale * scale * float(np.asarray(E, F64) @ ds_de(alpha, V, o, i, j)) * np.outer(q, q)
+
+
+# ---------------------------------------------------------------------------
+# 数学主线四: forward-only vectors and the closed-form key merge
+# ---------------------------------------------------------------------------
+def c_vectors(alpha: np.ndarray, V: np.ndarray, o: np.ndarray, m: int):
+    """The three forward-only vectors of [DD] 数学主线四 for the pair (m, m+1):
+    c11 = α_m (1 − 2α_m)(v_m − o), c22 = α_{m+1}(1 − 2α_{m+1})(v_{m+1} − o),
+    c12 = −α_m α_{m+1} (v_m + v_{m+1} − 2o)."""
+    V = np.asarray(V, F64)
+    a0, a1 = alpha[m], alpha[m + 1]
+    c11 = a0 * (1.0 - 2.0 * a0) * (V[m] - o)
+    c22 = a1 * (1.0 - 2.0 * a1) * (V[m + 1] - o)
+    c12 = -a0 * a1 * (V[m] + V[m + 1] - 2.0 * o)
+    return c11, c22, c12
+
+
+def merge_objective(k: np.ndarray, k_m: np.ndarray, k_m1: np.ndarray,
+                    g11: float, g12: float, g22: float) -> float:
+    """Second-order merge loss in the effective scalars g11, g12, g22
+    ([DD] 数学主线二):
+    g11 ‖k − k_m‖² + 2 g12 (k − k_m)ᵀ(k − k_{m+1}) + g22 ‖k − k_{m+1}‖²."""
+    k = np.asarray(k, F64)
+    d0 = k - np.asarray(k_m, F64)
+    d1 = k - np.asarray(k_m1, F64)
+    return float(g11 * (d0 @ d0) + 2.0 * g12 * (d0 @ d1) + g22 * (d1 @ d1))
+
+
+def hessian_weights(g11: float, g12: float, g22: float):
+    """Stationary point of ``merge_objective`` ([DD] 数学主线二, setting the
+    derivative to zero): k* = [(g11+g12) k_m + (g12+g22) k_{m+1}] /
+    (g11 + 2 g12 + g22).  Returns (w_m, w_{m+1}); [DD] 数学主线四 writes the
+    same pair as the weights of k* = w_m k_m + w_{m+1} k_{m+1}."""
+    den = g11 + 2.0 * g12 + g22
+    return (g11 + g12) / den, (g12 + g22) / den
+
+
+def forward_only_weights(n11: float, n12: float, n22: float):
+    """Closed-form, forward-only weights of [DD] 数学主线四 (last equation):
+    k* = (‖c11‖ − 2‖c12‖ + ‖c22‖)⁻¹ [(‖c11‖ − ‖c12‖) k_m + (‖c22‖ − ‖c12‖) k_{m+1}].
+
+    Arguments are the (window-summed, reading O2) norms ‖c11‖, ‖c12‖, ‖c22‖.
+    Reading O10 (pages silent on a vanishing or negative denominator): if
+    A = n11 − 2 n12 + n22 is not finite or A <= 1e-6 (n11 + n22 + 2 n12) the
+    plain average (½, ½) of [DD] 数学主线二 is used.  No clamping otherwise.
+    Returns (w_m, w_{m+1}, used_fallback).  The threshold is parity unpinned.
+    """
+    A = n11 - 2.0 * n12 + n22
+    scale = n11 + n22 + 2.0 * n12
+    if not math.isfinite(A) or A <= DEGENERATE_REL * scale:
+        return 0.5, 0.5, True
+    return (n11 - n12) / A, (n22 - n12) / A, False
+
+
+def merge_values(v_m: np.ndarray, v_m1: np.ndarray, n_m: int, n_m1: int):
+    """Lossless value handling (reading O1).
+
+    [DD] 数学主线一 and the 本页结论 summary say values are heterogeneous and
+    must not follow the key-merge rule; [ASYM] compresses values losslessly.
+    Once both positions share the merged key k*, they get identical logits, so
+    one slot holding the count-weighted mean value and the count n_m + n_{m+1}
+    (whose logit carries + ln n) gives exactly the attention output of the two
+    separate values.  Returns (v̄*, n*)."""
+    v_m = np.asarray(v_m, F64)
+    v_m1 = np.asarray(v_m1, F64)
+    n_tot = int(n_m) + int(n_m1)
+    return (n_m * v_m + n_m1 * v_m1) / n_tot, n_tot
+
+
+# ---------------------------------------------------------------------------
+# Cache policy: candidate pairs and selection
+# ---------------------------------------------------------------------------
+def num_pairs(n_slots: int, n_sink: int, n_recent: int) -> int:
+    """Aligned candidate pairs (S+2p, S+2p+1) inside [S, N−R) (reading O6:
+    "adjacent" pairs of [DD] 数学主线二, disjoint so that one round is a
+    matching; the sinks and recent window of [DD] 实验设置 / 工程上怎么用
+    are never merged).  An odd leftover slot is kept."""
+    return max(0, (n_slots - n_sink - n_recent) // 2)
+
+
+def select_pairs(cos: np.ndarray, n_merge: int) -> np.ndarray:
+    """Boolean flags of the n_merge pairs to merge in one round.
+
+    Reading O7 (parity unpinned: the pages give only "homogeneous adjacent
+    keys" and a uniform ratio, [DD] 局限与边界): the pairs with the highest
+    adjacent-key cosine, ties to the lower pair index.  Implemented as a stable
+    sort on −cos."""
+    P = len(cos)
+    if n_merge > P or n_merge < 0:
+        raise ValueError("infeasible merge count")
+    order = np.argsort(-np.asarray(cos, F64), kind="stable")
+    sel = np.zeros(P, dtype=bool)
+    sel[order[:n_merge]] = True
+    return sel
+
+
+# ---------------------------------------------------------------------------
+# One merge round on one (batch, layer, kv-head) slice
+# ---------------------------------------------------------------------------
+@dataclass
+class RoundResult:
+    lse: np.ndarray        # [GW]
+    O: np.ndarray          # [GW, D]
+    g_self: np.ndarray     # [N]
+    g_cross: np.ndarray    # [P]
+    cos: np.ndarray        # [P]
+    selected: np.ndarray   # [P] bool
+    w: np.ndarray          # [P, 2]
+    fallback: np.ndarray   # [P] bool
+    K: np.ndarray          # [T, D]
+    V: np.ndarray          # [T, D]
+    n: np.ndarray          # [T] int64
+    src: np.ndarray        # [T] int64
+    extras: dict = field(default_factory=dict)
+
+
+def window_statistics(K, V, n, Qw, scale):
+    """Step 1: for every window query w (the W queries of each of the G query
+    heads of this KV head, reading O3; no causal mask, reading O4), the
+    attention of [DD] 数学主线三 over all N slots with the + ln n slot bias.
+    Returns lse [GW], alpha [GW, N], O [GW, D]."""
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    Qw = np.asarray(Qw, F64)
+    GW = Qw.shape[0]
+    N = K.shape[0]
+    lse = np.empty(GW)
+    alpha = np.empty((GW, N))
+    O = np.empty((GW, V.shape[1]))
+    for w in range(GW):
+        e, a, o = attention_forward(K, V, Qw[w], scale, n)
+        mx = np.max(e)
+        lse[w] = mx + math.log(float(np.sum(np.exp(e - mx))))
+        alpha[w] = a
+        O[w] = o
+    return lse, alpha, O
+
+
+def hessian_norm_sums(V, alpha, O, n_sink, P):
+    """Step 2 ([DD] 数学主线四 norms, aggregated over the window by reading
+    O2, parity unpinned): g_self[i] = Σ_w ‖α_{w,i}(1 − 2α_{w,i})(v_i − o_w)‖,
+    which is Σ_w ‖c11^{(w)}‖ when i is the first slot of a pair and
+    Σ_w ‖c22^{(w)}‖ when it is the second; and, for the pair p with first slot
+    m = S + 2p, g_cross[p] = Σ_w ‖c12^{(w)}‖.  Norms by direct subtraction."""
+    V = np.asarray(V, F64)
+    GW, N = alpha.shape
+    g_self = np.zeros(N)
+    g_cross = np.zeros(P)
+    m = n_sink + 2 * np.arange(P)
+    for w in range(GW):
+        a = alpha[w]
+        o = O[w]
+        r = np.sqrt(np.sum((V - o) ** 2, axis=1))                 # ‖v_i − o_w‖
+        g_self += np.abs(a * (1.0 - 2.0 * a)) * r
+        if P:
+            rc = np.sqrt(np.sum((V[m] + V[m + 1] - 2.0 * o) ** 2, axis=1))
+            g_cross += a[m] * a[m + 1] * rc
+    return g_self, g_cross
+
+
+def merge_round(K, V, n, Qw, scale, n_sink, n_recent, n_merge) -> RoundResult:
+    """One KVSlimmer merge round on one slice, steps 1-7 in page order.
+
+    K, V: [N, D] (V holds slot mean values), n: [N] counts or None (all ones),
+    Qw: [GW, D] window queries.  Output length T = N − n_merge.
+    """
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    N, D = K.shape
+    nn = np.ones(N, dtype=np.int64) if n is None else np.asarray(n, dtype=np.int64)
+    P = num_pairs(N, n_sink, n_recent)
+    if not (0 <= n_merge <= P):
+        raise ValueError("infeasible merge count")
+
+    # 1. window attention statistics
+    lse, alpha, O = window_statistics(K, V, None if n is None else nn, Qw, scale)
+    # 2. Hessian-norm sums
+    g_self, g_cross = hessian_norm_sums(V, alpha, O, n_sink, P)
+    # 3. adjacent-key similarity
+    cos = np.array([cosine(K[n_sink + 2 * p], K[n_sink + 2 * p + 1]) for p in range(P)])
+    # 4. selection
+    selected = select_pairs(cos, n_merge)
+    # 5. closed-form weights (for every candidate pair; only selected ones are used)
+    w = np.empty((P, 2))
+    fb = np.zeros(P, dtype=bool)
+    for p in range(P):
+        m = n_sink + 2 * p
+        w0, w1, f = forward_only_weights(g_self[m], g_cross[p], g_self[m + 1])
+        w[p] = (w0, w1)
+        fb[p] = f
+    # 6 + 7. merge and compaction, walking the slots in order
+    out_k, out_v, out_n, out_src = [], [], [], []
+    i = 0
+    while i < N:
+        p = (i - n_sink) // 2
+        first_of_pair = (i >= n_sink and (i - n_sink) % 2 == 0 and p < P)
+        if first_of_pair and selected[p]:
+            k_star = w[p, 0] * K[i] + w[p, 1] * K[i + 1]
+            v_star, n_star = merge_values(V[i], V[i + 1], nn[i], nn[i + 1])
+            out_k.append(k_star)
+            out_v.append(v_star)
+            out_n.append(n_star)
+            out_src.append(i)
+            i += 2
+        else:
+            out_k.append(K[i])
+            out_v.append(V[i])
+            out_n.append(int(nn[i]))
+            out_src.append(i)
+            i += 1
+    return RoundResult(lse=lse, O=O, g_self=g_self, g_cross=g_cross, cos=cos,
+                       selected=selected, w=w, fallback=fb,
+                       K=np.array(out_k).reshape(-1, D), V=np.array(out_v).reshape(-1, D),
+                       n=np.array(out_n, dtype=np.int64), src=np.array(out_src, dtype=np.int64),
+                       extras={"alpha": alpha})
+
+
+def decode(K, V, n, q, scale) -> np.ndarray:
+    """Decode attention over a (merged) cache: the attention of [DD] 数学主线三
+    with the + ln n slot bias of reading O1; returns o = Σ_j α_j v̄_j."""
+    _, _, o = attention_forward(K, V, q, scale, n)
+    return o
+
+
+def compose_src(prev_src: np.ndarray, src: np.ndarray) -> np.ndarray:
+    """Map the src indices of a later round back to the original slots."""
+    return np.asarray(prev_src)[np.asarray(src)]
+
+
+# ---------------------------------------------------------------------------
+# 算一遍: KV bytes
+# ---------------------------------------------------------------------------
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, dtype_bytes: int) -> int:
+    """[DD] 算一遍: layers × 2 (K and V) × kv_heads × head_dim × bytes."""
+    return layers * 2 * kv_heads * head_dim * dtype_bytes
