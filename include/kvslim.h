@@ -1,0 +1,206 @@
+/*
+ * kvslim.h — C ABI of the KVSlimmer asymmetric KV-merge path for AMD MI355X (gfx950).
+ *
+ * One merge round on a KV cache, per (batch, kv-head), then decode attention over the
+ * merged cache:
+ *
+ *   kvs_score          window attention statistics (lse, o) and the forward-only
+ *                      Hessian-norm sums g_self / g_cross, plus adjacent-key cosine
+ *   kvs_merge_weights  pair selection (top-M adjacent pairs by cosine) and the
+ *                      closed-form key-merge weights
+ *   kvs_merge_compact  key merge, lossless value-slot merge, stream compaction
+ *   kvs_decode_attn    GQA decode attention over a (merged) cache
+ *
+ * Sources.  The operations follow the KVSlimmer deep-dive "论文专题讲解：KVSlimmer：
+ * 非对称 KV 合并的数学与工程" (charles2530.github.io), sections 数学主线二 (merging an adjacent
+ * key pair by a second-order objective), 数学主线三 (single-query attention and its exact
+ * Hessian), 数学主线四 (forward-only vectors c11, c22, c12 and the closed-form k*),
+ * 实验设置 / 工程上怎么用 (preserved initial "sink" tokens and a recent window) and
+ * 局限与边界 (local adjacent merging, one uniform ratio for every head); and the AsymKV
+ * abstract ("Homogeneous Keys, Heterogeneous Values", in the related-papers list of the
+ * fugumt.com KVSlimmer page) for lossless value handling.
+ *
+ * Conventions for every entry point.
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The kvs_cache and
+ *    kvs_round structs are host memory, read during the call only.
+ *  - The library allocates no memory and keeps no state: scratch space is the caller's
+ *    `workspace` (size from kvs_workspace_bytes).  Calls on different streams are
+ *    independent; outputs must not alias inputs.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *    returns without synchronising.  Output lengths are host-computable up front.
+ *  - Arguments are validated before anything is enqueued; on a validation error nothing is
+ *    written.  A failed kernel launch returns KVS_ERR_HIP; outputs are then undefined.
+ *    kvs_last_error() gives a message for the last failure on the calling thread.
+ *  - Floating point: inputs bf16 or fp32, all arithmetic and every statistic in fp32.
+ *
+ * Cache layout (kvs_cache).  K and V of one (batch b, kv-head h) are n_slots rows of
+ * head_dim contiguous elements, starting at element offset b*stride_b + h*stride_h.
+ * Slot counts n and compaction indices src use the same row indexing with strides
+ * stride_b/head_dim and stride_h/head_dim (one int32 per row).  A slot holds a key, the
+ * MEAN of the values it stands for and the count n of raw tokens merged into it; its
+ * attention logit carries + ln n.  n == NULL means every count is 1.
+ */
+#ifndef KVSLIM_H
+#define KVSLIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVS_OK = 0,
+  KVS_ERR_NULL = 1,        /* a required pointer is NULL */
+  KVS_ERR_SHAPE = 2,       /* bad sizes: head_dim not 64/128, n_q_heads % n_kv_heads, group > 8, ... */
+  KVS_ERR_DTYPE = 3,       /* unknown dtype or unsupported dtype combination */
+  KVS_ERR_STRIDE = 4,      /* strides not multiples of head_dim, or negative */
+  KVS_ERR_ALIGN = 5,       /* K/V/output base pointers not 16-byte aligned */
+  KVS_ERR_INFEASIBLE = 6,  /* n_merge < 0 or n_merge > number of candidate pairs */
+  KVS_ERR_WORKSPACE = 7,   /* workspace / selection-state buffer missing or too small */
+  KVS_ERR_HIP = 8          /* a HIP launch failed */
+} kvs_status;
+
+typedef enum { KVS_BF16 = 0, KVS_F32 = 1 } kvs_dtype;
+
+typedef struct {
+  int32_t batch;       /* B */
+  int32_t n_kv_heads;  /* H_kv */
+  int32_t n_q_heads;   /* H_q, a multiple of H_kv; query head hq reads kv head hq / (H_q/H_kv) */
+  int32_t head_dim;    /* D: 64 or 128 */
+  int64_t n_slots;     /* N: slots per (batch, kv-head) */
+  int64_t stride_b;    /* elements between batch items of K and V (multiple of head_dim) */
+  int64_t stride_h;    /* elements between kv heads of K and V (multiple of head_dim) */
+} kvs_cache;
+
+typedef struct {
+  int32_t window;      /* W: observation-window queries per query head */
+  int64_t n_sink;      /* S: leading slots never merged */
+  int64_t n_recent;    /* R: trailing slots never merged */
+  int64_t n_merge;     /* M: pairs merged in this round, the same for every (b, h); 0 <= M <= P */
+  float sm_scale;      /* softmax scale, 1/sqrt(head_dim) for standard attention */
+} kvs_round;
+
+/* Operation ids for kvs_workspace_bytes. */
+typedef enum {
+  KVS_OP_SCORE = 0,      /* workspace of kvs_score */
+  KVS_OP_SELECT = 1,     /* workspace of kvs_merge_weights */
+  KVS_OP_SEL_STATE = 2,  /* size of the selection-state buffer (kvs_merge_weights -> kvs_merge_compact) */
+  KVS_OP_DECODE = 3      /* workspace of kvs_decode_attn */
+} kvs_op;
+
+/* Number of candidate pairs P = floor((N - S - R) / 2) (0 if negative).  Pair p is the
+ * adjacent, disjoint slot pair (S + 2p, S + 2p + 1); an odd leftover slot before the
+ * recent window is kept.  Adjacent merging: deep-dive section 数学主线二; sinks and recent
+ * window: sections 实验设置 and 工程上怎么用. */
+int64_t kvs_num_pairs(int64_t n_slots, int64_t n_sink, int64_t n_recent);
+
+/* Bytes of workspace (or of the selection state) `op` needs for these shapes; 0 if none.
+ * `round` may be NULL for KVS_OP_DECODE. */
+size_t kvs_workspace_bytes(kvs_op op, const kvs_cache* cache, const kvs_round* round);
+
+/*
+ * kvs_score — window attention statistics and forward-only Hessian-norm sums.
+ *
+ * For every batch b and query head hq (kv head h = hq / G, G = H_q / H_kv), and every
+ * window query w of Qw[b, hq, w, :] ([B, H_q, W, D], dtype `dtype`), over all N slots of
+ * kv head h (deep-dive 数学主线三, single-query attention, with the + ln n slot bias):
+ *   e_{w,i} = sm_scale * (q_w . k_i) + ln n_i
+ *   lse[b, hq, w]   = log sum_i exp(e_{w,i})                     (fp32, [B, H_q, W])
+ *   O[b, hq, w, :]  = sum_i exp(e_{w,i} - lse) v_i               (fp32, [B, H_q, W, D])
+ * With alpha_{w,i} = exp(e_{w,i} - lse_w), summed over the G*W window queries of kv head h
+ * (deep-dive 数学主线四, norms of c11, c22 and c12):
+ *   g_self[b, h, i]  = sum_w alpha_{w,i} |1 - 2 alpha_{w,i}| ||v_i - o_w||       ([B, H_kv, N])
+ *   g_cross[b, h, p] = sum_w alpha_{w,m} alpha_{w,m+1} ||v_m + v_{m+1} - 2 o_w||, m = S + 2p
+ *                                                                                ([B, H_kv, P])
+ *   cos[b, h, p]     = k_m . k_{m+1} / (||k_m|| ||k_{m+1}||)  (nullable output; 1 if both
+ *                      keys are equal and a norm is 0, else 0 when a norm is 0)   ([B, H_kv, P])
+ * All statistics arrays are dense row-major fp32.  Requires N >= 1 and W >= 1.
+ * `n` is NULL or int32 counts >= 1 (cache row indexing).  K, V, Qw 16-byte aligned.
+ */
+kvs_status kvs_score(const kvs_cache* cache, kvs_dtype dtype,
+                     const void* K, const void* V, const int32_t* n,
+                     const void* Qw, const kvs_round* round,
+                     float* lse, float* O, float* g_self, float* g_cross, float* cos,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_merge_weights — pair selection and closed-form weights.
+ *
+ * Selection (deep-dive 数学主线二 "adjacent" pairs; 局限与边界: one uniform ratio): in every
+ * (b, h) independently, the round->n_merge candidate pairs with the largest cos[b, h, p],
+ * ties to the smaller p.  The result is written to `sel_state` (an opaque device buffer of
+ * kvs_workspace_bytes(KVS_OP_SEL_STATE) bytes) that kvs_merge_compact consumes; optionally
+ * also as one flag byte per pair, selected[b, h, p] in {0, 1} ([B, H_kv, P], nullable).
+ * `cos` may be NULL only when n_merge is 0 or P (nothing to choose).
+ *
+ * Weights (deep-dive 数学主线四, closed-form forward-only k*), for every pair p, m = S + 2p:
+ *   A = g_self[m] - 2 g_cross[p] + g_self[m+1]
+ *   w[b, h, p, 0] = (g_self[m]   - g_cross[p]) / A
+ *   w[b, h, p, 1] = (g_self[m+1] - g_cross[p]) / A
+ * and the plain average (1/2, 1/2) of section 数学主线二 when A is not finite or
+ * A <= 1e-6 (g_self[m] + g_self[m+1] + 2 g_cross[p]).  `w` ([B, H_kv, P, 2] fp32) is nullable.
+ */
+kvs_status kvs_merge_weights(const kvs_cache* cache, const kvs_round* round,
+                             const float* g_self, const float* g_cross, const float* cos,
+                             float* w, uint8_t* selected,
+                             void* sel_state, size_t sel_state_bytes,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_merge_compact — key merge, lossless value merge and stream compaction.
+ *
+ * For each selected pair p (m = S + 2p), with the weights of kvs_merge_weights computed
+ * inline from g_self and g_cross:
+ *   k* = w_0 k_m + w_1 k_{m+1}                                (deep-dive 数学主线四)
+ *   v* = (n_m v_m + n_{m+1} v_{m+1}) / (n_m + n_{m+1}),   n* = n_m + n_{m+1}
+ * (values are not merged by the key rule: the merged slot keeps the count-weighted mean
+ * value and the count, so attention with + ln n reproduces the two separate values
+ * exactly — the lossless value handling of the AsymKV abstract).  Every other slot is
+ * copied unchanged.  Slots keep their order: the output has T = N - M slots and
+ * src_out[j] is the input slot of the first token of output slot j.
+ *
+ * `sel_state` comes from kvs_merge_weights for the same shapes and round; it may be NULL
+ * when n_merge == P (every pair merges) or n_merge == 0 (plain copy).  The kernel
+ * recomputes each pair's cosine with the same routine kvs_score uses and tests it
+ * against the selection threshold.  `out` describes the K_out/V_out layout: same batch,
+ * heads and head_dim as `cache`, n_slots == N - M, its own strides.  n_out and src_out
+ * (int32, required) use the row indexing of `out`.  in_dtype/out_dtype: any of
+ * bf16/fp32 (fp32 output keeps the full fp32 result; bf16 output is its round-to-nearest-
+ * even).
+ */
+kvs_status kvs_merge_compact(const kvs_cache* cache, kvs_dtype in_dtype,
+                             const void* K, const void* V, const int32_t* n,
+                             const float* g_self, const float* g_cross,
+                             const kvs_round* round, const void* sel_state,
+                             const kvs_cache* out, kvs_dtype out_dtype,
+                             void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
+                             void* stream);
+
+/*
+ * kvs_decode_attn — decode attention over a (merged) cache (deep-dive 数学主线三
+ * attention with the + ln n slot bias):
+ *   out[b, hq, :] = sum_j softmax_j(sm_scale * q[b, hq] . k_j + ln n_j) v_j
+ * over the cache->n_slots slots of kv head hq / G.  q: [B, H_q, D] in `dtype`;
+ * out: [B, H_q, D] fp32.  Requires N >= 1 and G = H_q / H_kv in {1, 2, 4, 8}.
+ */
+kvs_status kvs_decode_attn(const kvs_cache* cache, kvs_dtype dtype,
+                           const void* K, const void* V, const int32_t* n,
+                           const void* q, float sm_scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* kvs_status_str(kvs_status s);
+
+/* Message describing the last non-OK status returned on the calling thread. */
+const char* kvs_last_error(void);
+
+/* ABI version of this library (major * 100 + minor). */
+int32_t kvs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSLIM_H */

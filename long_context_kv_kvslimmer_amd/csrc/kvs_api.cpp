@@ -1,0 +1,217 @@
+// C ABI of libkvslim (declared in include/kvslim.h): argument validation, workspace
+// sizing and launches on the caller's stream.  No device memory is allocated here and no
+// state is kept besides a per-thread message for the last error.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/kvslim.h"
+#include "kvs_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+kvs_status fail(kvs_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kvs_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KVS_OK;
+  return fail(KVS_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t pairs_of(int64_t N, int64_t S, int64_t R) {
+  const int64_t r = N - S - R;
+  return r > 0 ? r / 2 : 0;
+}
+
+// Validates the cache description; fills the kernel shape.
+kvs_status check_cache(const kvs_cache* c, int dtype, kvs::Shape& s) {
+  if (!c) return fail(KVS_ERR_NULL, "cache is NULL");
+  if (dtype != KVS_BF16 && dtype != KVS_F32) return fail(KVS_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1)
+    return fail(KVS_ERR_SHAPE, "batch, n_kv_heads and n_q_heads must be >= 1");
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(KVS_ERR_SHAPE, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", c->n_q_heads, c->n_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(KVS_ERR_SHAPE, "head_dim %d not in {64, 128}", c->head_dim);
+  if (c->n_slots < 0) return fail(KVS_ERR_SHAPE, "n_slots < 0");
+  if (c->n_slots > (int64_t)INT32_MAX) return fail(KVS_ERR_SHAPE, "n_slots above 2^31 - 1");
+  if (c->stride_b < 0 || c->stride_h < 0 || c->stride_b % c->head_dim || c->stride_h % c->head_dim)
+    return fail(KVS_ERR_STRIDE, "strides must be non-negative multiples of head_dim");
+  s.B = c->batch;
+  s.Hkv = c->n_kv_heads;
+  s.Hq = c->n_q_heads;
+  s.G = c->n_q_heads / c->n_kv_heads;
+  s.D = c->head_dim;
+  s.N = c->n_slots;
+  s.sb = c->stride_b;
+  s.sh = c->stride_h;
+  s.bf16 = dtype == KVS_BF16;
+  return KVS_OK;
+}
+
+kvs_status check_round(const kvs_round* r, const kvs::Shape& s, kvs::RoundP& rp, bool need_window) {
+  if (!r) return fail(KVS_ERR_NULL, "round is NULL");
+  if (need_window && r->window < 1) return fail(KVS_ERR_SHAPE, "window must be >= 1");
+  if (r->n_sink < 0 || r->n_recent < 0) return fail(KVS_ERR_SHAPE, "n_sink and n_recent must be >= 0");
+  if (!std::isfinite(r->sm_scale)) return fail(KVS_ERR_SHAPE, "sm_scale is not finite");
+  rp.W = r->window;
+  rp.S = r->n_sink;
+  rp.R = r->n_recent;
+  rp.M = r->n_merge;
+  rp.P = pairs_of(s.N, r->n_sink, r->n_recent);
+  rp.scale = r->sm_scale;
+  if (rp.M < 0 || rp.M > rp.P)
+    return fail(KVS_ERR_INFEASIBLE, "n_merge %lld outside [0, P = %lld]", (long long)rp.M, (long long)rp.P);
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t kvs_num_pairs(int64_t n_slots, int64_t n_sink, int64_t n_recent) {
+  if (n_slots < 0 || n_sink < 0 || n_recent < 0) return 0;
+  return pairs_of(n_slots, n_sink, n_recent);
+}
+
+size_t kvs_workspace_bytes(kvs_op op, const kvs_cache* cache, const kvs_round* round) {
+  kvs::Shape s;
+  if (check_cache(cache, KVS_BF16, s) != KVS_OK) return 0;
+  kvs::RoundP r{};
+  switch (op) {
+    case KVS_OP_SCORE:
+      if (!round || check_round(round, s, r, true) != KVS_OK) return 0;
+      return kvs::score_workspace_bytes(s, r);
+    case KVS_OP_SELECT:
+      return 0;
+    case KVS_OP_SEL_STATE:
+      if (!round) return 0;
+      r.P = pairs_of(s.N, round->n_sink, round->n_recent);
+      return (size_t)s.B * s.Hkv * kvs::sel_stride_ints(r.P) * sizeof(int32_t);
+    case KVS_OP_DECODE:
+      return kvs::decode_workspace_bytes(s);
+  }
+  return 0;
+}
+
+kvs_status kvs_score(const kvs_cache* cache, kvs_dtype dtype, const void* K, const void* V, const int32_t* n,
+                     const void* Qw, const kvs_round* round, float* lse, float* O, float* g_self, float* g_cross,
+                     float* cos, void* workspace, size_t workspace_bytes, void* stream) {
+  kvs::Shape s;
+  kvs::RoundP r;
+  kvs_status st = check_cache(cache, dtype, s);
+  if (st) return st;
+  if ((st = check_round(round, s, r, true))) return st;
+  if (s.N < 1) return fail(KVS_ERR_SHAPE, "kvs_score needs n_slots >= 1");
+  if (!K || !V || !Qw || !lse || !O || !g_self || (r.P > 0 && !g_cross))
+    return fail(KVS_ERR_NULL, "kvs_score: K, V, Qw, lse, O, g_self and g_cross are required");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(Qw)) return fail(KVS_ERR_ALIGN, "K, V, Qw must be 16-byte aligned");
+  const size_t need = kvs::score_workspace_bytes(s, r);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(KVS_ERR_WORKSPACE, "kvs_score needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  return hip_status(kvs::launch_score(s, r, K, V, n, Qw, lse, O, g_self, g_cross, cos, workspace,
+                                      static_cast<hipStream_t>(stream)),
+                    "kvs_score");
+}
+
+kvs_status kvs_merge_weights(const kvs_cache* cache, const kvs_round* round, const float* g_self,
+                             const float* g_cross, const float* cos, float* w, uint8_t* selected, void* sel_state,
+                             size_t sel_state_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  kvs::Shape s;
+  kvs::RoundP r;
+  kvs_status st = check_cache(cache, KVS_BF16, s);
+  if (st) return st;
+  if ((st = check_round(round, s, r, false))) return st;
+  if (!sel_state) return fail(KVS_ERR_NULL, "kvs_merge_weights: sel_state is required");
+  const bool choose = r.M != 0 && r.M != r.P;
+  if (choose && !cos) return fail(KVS_ERR_NULL, "kvs_merge_weights: cos is required when 0 < n_merge < P");
+  if (w && (!g_self || (r.P > 0 && !g_cross)))
+    return fail(KVS_ERR_NULL, "kvs_merge_weights: weights need g_self and g_cross");
+  const size_t need = (size_t)s.B * s.Hkv * kvs::sel_stride_ints(r.P) * sizeof(int32_t);
+  if (sel_state_bytes < need)
+    return fail(KVS_ERR_WORKSPACE, "sel_state needs %zu bytes, got %zu", need, sel_state_bytes);
+  return hip_status(kvs::launch_select(s, r, g_self, g_cross, choose ? cos : nullptr, w, selected,
+                                       static_cast<int32_t*>(sel_state), static_cast<hipStream_t>(stream)),
+                    "kvs_merge_weights");
+}
+
+kvs_status kvs_merge_compact(const kvs_cache* cache, kvs_dtype in_dtype, const void* K, const void* V,
+                             const int32_t* n, const float* g_self, const float* g_cross, const kvs_round* round,
+                             const void* sel_state, const kvs_cache* out, kvs_dtype out_dtype, void* K_out,
+                             void* V_out, int32_t* n_out, int32_t* src_out, void* stream) {
+  kvs::Shape s, so;
+  kvs::RoundP r;
+  kvs_status st = check_cache(cache, in_dtype, s);
+  if (st) return st;
+  if ((st = check_round(round, s, r, false))) return st;
+  if (!out) return fail(KVS_ERR_NULL, "kvs_merge_compact: out layout is NULL");
+  if ((st = check_cache(out, out_dtype, so))) return st;
+  if (so.B != s.B || so.Hkv != s.Hkv || so.D != s.D)
+    return fail(KVS_ERR_SHAPE, "out layout must match batch, n_kv_heads and head_dim of the input");
+  if (so.N != s.N - r.M)
+    return fail(KVS_ERR_SHAPE, "out n_slots %lld != N - M = %lld", (long long)so.N, (long long)(s.N - r.M));
+  if (s.N == 0) return KVS_OK;
+  if (!K || !V || !K_out || !V_out || !n_out || !src_out)
+    return fail(KVS_ERR_NULL, "kvs_merge_compact: K, V, K_out, V_out, n_out, src_out are required");
+  if (r.M > 0 && (!g_self || !g_cross)) return fail(KVS_ERR_NULL, "kvs_merge_compact: g_self and g_cross are required");
+  if (!sel_state && r.M != r.P && r.M != 0)
+    return fail(KVS_ERR_NULL, "kvs_merge_compact: sel_state is required when 0 < n_merge < P");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out))
+    return fail(KVS_ERR_ALIGN, "K, V, K_out, V_out must be 16-byte aligned");
+  kvs::OutP op{so.sb, so.sh, so.bf16};
+  return hip_status(kvs::launch_merge(s, r, K, V, n, g_self, g_cross, static_cast<const int32_t*>(sel_state), op, K_out,
+                                      V_out, n_out, src_out, static_cast<hipStream_t>(stream)),
+                    "kvs_merge_compact");
+}
+
+kvs_status kvs_decode_attn(const kvs_cache* cache, kvs_dtype dtype, const void* K, const void* V, const int32_t* n,
+                           const void* q, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  kvs::Shape s;
+  kvs_status st = check_cache(cache, dtype, s);
+  if (st) return st;
+  if (s.N < 1) return fail(KVS_ERR_SHAPE, "kvs_decode_attn needs n_slots >= 1");
+  if (s.G != 1 && s.G != 2 && s.G != 4 && s.G != 8)
+    return fail(KVS_ERR_SHAPE, "kvs_decode_attn supports n_q_heads / n_kv_heads in {1, 2, 4, 8}, got %d", s.G);
+  if (!std::isfinite(sm_scale)) return fail(KVS_ERR_SHAPE, "sm_scale is not finite");
+  if (!K || !V || !q || !out) return fail(KVS_ERR_NULL, "kvs_decode_attn: K, V, q, out are required");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(q)) return fail(KVS_ERR_ALIGN, "K, V, q must be 16-byte aligned");
+  const size_t need = kvs::decode_workspace_bytes(s);
+  if (workspace_bytes < need || !workspace)
+    return fail(KVS_ERR_WORKSPACE, "kvs_decode_attn needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  return hip_status(kvs::launch_decode(s, K, V, n, q, sm_scale, out, workspace, static_cast<hipStream_t>(stream)),
+                    "kvs_decode_attn");
+}
+
+const char* kvs_status_str(kvs_status s) {
+  switch (s) {
+    case KVS_OK: return "KVS_OK";
+    case KVS_ERR_NULL: return "KVS_ERR_NULL";
+    case KVS_ERR_SHAPE: return "KVS_ERR_SHAPE";
+    case KVS_ERR_DTYPE: return "KVS_ERR_DTYPE";
+    case KVS_ERR_STRIDE: return "KVS_ERR_STRIDE";
+    case KVS_ERR_ALIGN: return "KVS_ERR_ALIGN";
+    case KVS_ERR_INFEASIBLE: return "KVS_ERR_INFEASIBLE";
+    case KVS_ERR_WORKSPACE: return "KVS_ERR_WORKSPACE";
+    case KVS_ERR_HIP: return "KVS_ERR_HIP";
+  }
+  return "KVS_ERR_UNKNOWN";
+}
+
+const char* kvs_last_error(void) { return g_msg; }
+
+int32_t kvs_version(void) { return 100; }
+
+}  // extern "C"

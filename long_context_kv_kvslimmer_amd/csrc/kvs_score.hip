@@ -1,0 +1,349 @@
+// Scorer (kvs_score): window attention statistics and forward-only Hessian-norm sums.
+//
+// KVSlimmer deep-dive (charles2530.github.io):
+//   section 数学主线三 — single-query attention e_i = q k_i^T / sqrt(d_k), alpha = softmax(e),
+//     o = sum alpha_t v_t (here every slot's logit carries + ln n_i, n_i tokens per slot);
+//   section 数学主线四 — forward-only vectors c11 = a_m (1 - 2 a_m)(v_m - o),
+//     c22 = a_{m+1}(1 - 2 a_{m+1})(v_{m+1} - o), c12 = -a_m a_{m+1}(v_m + v_{m+1} - 2o), whose
+//     norms (summed over the window queries) fix the closed-form merge weights.
+//
+// Two passes over K/V, because alpha and ||v - o|| need the final lse and o:
+//   pass 1: split-N online softmax per window query -> partial (max, sum, o) records,
+//           then a log-sum-exp combine -> lse, O.  Pass 1 also writes the adjacent-key
+//           cosine of every candidate pair (pair_cos, the routine the merge pass reuses).
+//   pass 2: alpha, residual norms, g_self / g_cross.
+// This file holds the portable VALU kernels (any element type); the bf16 MFMA kernels
+// live in kvs_score_mfma.hip.
+#include "kvs_common.h"
+#include "kvs_internal.h"
+#include "kvs_score_impl.h"
+
+namespace kvs {
+
+// ------------------------------------------------------------------ pass 1 (VALU) --
+// grid: x = slot split, y = block of 128 window queries, z = (b, kv-head).
+// Two threads per query, each owning half of the head dimension.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pass1_valu_kernel(P1Args a) {
+  constexpr int DH = D / 2;
+  constexpr int TS = 32;
+  constexpr int E = Elt<T>::kPerChunk;
+  __shared__ float Ks[TS][D];
+  __shared__ float Vs[TS][D];
+  __shared__ float lg[TS];
+
+  const int tid = threadIdx.x;
+  const int qi = tid >> 1, half = tid & 1;
+  const int64_t bh = blockIdx.z;
+  const int64_t b = bh / a.Hkv, h = bh - b * a.Hkv;
+  const int64_t w = (int64_t)blockIdx.y * 128 + qi;
+  const bool qvalid = w < a.GW;
+  const T* Kp = static_cast<const T*>(a.K) + b * a.sb + h * a.sh;
+  const T* Vp = static_cast<const T*>(a.V) + b * a.sb + h * a.sh;
+  const int32_t* np = a.n ? a.n + (b * a.sb + h * a.sh) / D : nullptr;
+  // window queries of kv head h: query heads h*G .. h*G+G-1, W rows each, contiguous
+  const T* Qp = static_cast<const T*>(a.Qw) + ((b * a.Hq + h * a.G) * (int64_t)a.W) * D;
+
+  float qs[DH];
+  {
+    const float c = a.scale * kLog2e;
+    for (int d0 = 0; d0 < DH; d0 += E) {
+      float f[E];
+      if (qvalid) unpack<T>(load16(Qp + w * D + half * DH + d0), f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) qs[d0 + e] = qvalid ? f[e] * c : 0.f;
+    }
+  }
+  float o[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) o[d] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int64_t s_begin = (int64_t)blockIdx.x * a.chunk;
+  const int64_t s_end = min(a.N, s_begin + a.chunk);
+  for (int64_t t0 = s_begin; t0 < s_end; t0 += TS) {
+    const int nt = (int)min((int64_t)TS, s_end - t0);
+    __syncthreads();
+    for (int idx = tid; idx < TS * (D / E); idx += 256) {
+      const int s = idx / (D / E), cch = idx % (D / E);
+      float fk[E], fv[E];
+      if (s < nt) {
+        unpack<T>(load16(Kp + (t0 + s) * D + cch * E), fk);
+        unpack<T>(load16(Vp + (t0 + s) * D + cch * E), fv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) fk[e] = fv[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        Ks[s][cch * E + e] = fk[e];
+        Vs[s][cch * E + e] = fv[e];
+      }
+    }
+    if (tid < TS) lg[tid] = (tid < nt && np) ? __log2f((float)np[t0 + tid]) : 0.f;
+    __syncthreads();
+    float ev[TS];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < TS; ++s) {
+      float d = 0.f;
+#pragma unroll
+      for (int k = 0; k < DH; ++k) d = __builtin_fmaf(qs[k], Ks[s][half * DH + k], d);
+      d += __shfl_xor(d, 1, 64);
+      ev[s] = s < nt ? d + lg[s] : -INFINITY;
+      mx = fmaxf(mx, ev[s]);
+    }
+    const float mn = fmaxf(m, mx);
+    const float corr = exp2f(m - mn);
+    l *= corr;
+#pragma unroll
+    for (int k = 0; k < DH; ++k) o[k] *= corr;
+#pragma unroll
+    for (int s = 0; s < TS; ++s) {
+      const float p = exp2f(ev[s] - mn);
+      l += p;
+#pragma unroll
+      for (int k = 0; k < DH; ++k) o[k] = __builtin_fmaf(p, Vs[s][half * DH + k], o[k]);
+    }
+    m = mn;
+  }
+  if (qvalid) {
+    float* rec = a.part + ((bh * a.GW + w) * a.nsplit + blockIdx.x) * (int64_t)(D + 4);
+    if (half == 0) {
+      rec[0] = m;
+      rec[1] = l;
+    }
+#pragma unroll
+    for (int k = 0; k < DH; ++k) rec[4 + half * DH + k] = o[k];
+  }
+}
+
+// --------------------------------------------------------- log-sum-exp combine --
+// One block of D threads per unit; partial records {m (log2 units), l, -, -, o[D]}.
+// Writes lse (natural log, nullable) and the normalised output row.
+__global__ void combine_kernel(const float* __restrict__ part, int nsplit, int D, float* __restrict__ lse,
+                               float* __restrict__ out) {
+  const int64_t u = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* r = part + u * nsplit * (int64_t)(D + 4);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, r[s * (int64_t)(D + 4)]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* q = r + s * (int64_t)(D + 4);
+    const float f = exp2f(q[0] - M);
+    L = __builtin_fmaf(q[1], f, L);
+    acc = __builtin_fmaf(q[4 + d], f, acc);
+  }
+  out[u * D + d] = acc / L;
+  if (lse && d == 0) lse[u] = (M + __log2f(L)) * kLn2;
+}
+
+hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, float* lse, float* out,
+                          hipStream_t st) {
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(units), dim3(D), 0, st, part, nsplit, D, lse, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ pass 2 (VALU) --
+// Four threads (a quad) per unit; a unit is a candidate pair (m, m+1) or a single slot
+// outside the pair region.  Each thread owns a quarter of the head dimension.
+template <typename T, int D, bool HAS_N>
+__global__ __launch_bounds__(256) void pass2_valu_kernel(P2Args a) {
+  constexpr int DQ = D / 4;
+  constexpr int E = Elt<T>::kPerChunk;
+  const int tid = threadIdx.x;
+  const int ql = tid & 3;
+  const int64_t u = (int64_t)blockIdx.x * 64 + (tid >> 2);
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / a.Hkv, h = bh - b * a.Hkv;
+  const int64_t n_units = a.S + a.P + (a.N - a.S - 2 * a.P);
+  if (u >= n_units) return;  // whole quads leave together; only quad shuffles follow
+  bool pair;
+  int64_t m, p = 0;
+  if (u < a.S) {
+    pair = false;
+    m = u;
+  } else if (u < a.S + a.P) {
+    pair = true;
+    p = u - a.S;
+    m = a.S + 2 * p;
+  } else {
+    pair = false;
+    m = a.S + 2 * a.P + (u - a.S - a.P);
+  }
+  const T* Kp = static_cast<const T*>(a.K) + b * a.sb + h * a.sh;
+  const T* Vp = static_cast<const T*>(a.V) + b * a.sb + h * a.sh;
+  const int32_t* np = HAS_N ? a.n + (b * a.sb + h * a.sh) / D : nullptr;
+  const T* Qp = static_cast<const T*>(a.Qw) + ((b * a.Hq + h * a.G) * (int64_t)a.W) * D;
+  const float* Op = a.O + bh * a.GW * (int64_t)D;
+  const float* Lp = a.lse + bh * a.GW;
+
+  float k0[DQ], k1[DQ], v0[DQ], v1[DQ];
+  for (int d0 = 0; d0 < DQ; d0 += E) {
+    unpack<T>(load16(Kp + m * D + ql * DQ + d0), k0 + d0);
+    unpack<T>(load16(Vp + m * D + ql * DQ + d0), v0 + d0);
+    if (pair) {
+      unpack<T>(load16(Kp + (m + 1) * D + ql * DQ + d0), k1 + d0);
+      unpack<T>(load16(Vp + (m + 1) * D + ql * DQ + d0), v1 + d0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) k1[d0 + e] = v1[d0 + e] = 0.f;
+    }
+  }
+  const float b0 = HAS_N ? logf((float)np[m]) : 0.f;
+  const float b1 = (HAS_N && pair) ? logf((float)np[m + 1]) : 0.f;
+  float gs0 = 0.f, gs1 = 0.f, gx = 0.f;
+  for (int64_t w = 0; w < a.GW; ++w) {
+    float d0 = 0.f, d1 = 0.f, r0 = 0.f, r1 = 0.f, rc = 0.f;
+    for (int c0 = 0; c0 < DQ; c0 += E) {
+      float q[E];
+      unpack<T>(load16(Qp + w * D + ql * DQ + c0), q);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float o = Op[w * D + ql * DQ + c0 + e];
+        const float x0 = v0[c0 + e] - o, x1 = v1[c0 + e] - o, xc = x0 + x1;
+        d0 = __builtin_fmaf(q[e], k0[c0 + e], d0);
+        d1 = __builtin_fmaf(q[e], k1[c0 + e], d1);
+        r0 = __builtin_fmaf(x0, x0, r0);
+        r1 = __builtin_fmaf(x1, x1, r1);
+        rc = __builtin_fmaf(xc, xc, rc);
+      }
+    }
+    d0 = group_sum<4>(d0);
+    r0 = group_sum<4>(r0);
+    d1 = group_sum<4>(d1);
+    r1 = group_sum<4>(r1);
+    rc = group_sum<4>(rc);
+    const float lw = Lp[w];
+    const float a0 = expf(__builtin_fmaf(a.scale, d0, b0) - lw);
+    gs0 = __builtin_fmaf(a0 * fabsf(1.f - 2.f * a0), sqrtf(r0), gs0);
+    if (pair) {
+      const float a1 = expf(__builtin_fmaf(a.scale, d1, b1) - lw);
+      gs1 = __builtin_fmaf(a1 * fabsf(1.f - 2.f * a1), sqrtf(r1), gs1);
+      gx = __builtin_fmaf(a0 * a1, sqrtf(rc), gx);
+    }
+  }
+  if (ql == 0) {
+    float* gsp = a.g_self + bh * a.N;
+    gsp[m] = gs0;
+    if (pair) {
+      gsp[m + 1] = gs1;
+      a.g_cross[bh * a.P + p] = gx;
+    }
+  }
+}
+
+// --------------------------------------------------------- adjacent-key cosine --
+// Row layout (LPR lanes per row); every candidate pair of one (b, head) per group step.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pair_cos_kernel(CosArgs a) {
+  constexpr int E = Elt<T>::kPerChunk;
+  constexpr int LPR = D / E;
+  constexpr int GPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int grp = tid / LPR, j = tid % LPR;
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / a.Hkv, h = bh - b * a.Hkv;
+  const T* Kp = static_cast<const T*>(a.K) + b * a.sb + h * a.sh;
+  const int64_t p = (int64_t)blockIdx.x * GPB + grp;
+  const bool valid = p < a.P;
+  float k0[E], k1[E];
+  if (valid) {
+    const int64_t m = a.S + 2 * p;
+    unpack<T>(load16(Kp + m * D + j * E), k0);
+    unpack<T>(load16(Kp + (m + 1) * D + j * E), k1);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) k0[e] = k1[e] = 0.f;
+  }
+  const float c = pair_cos<E, LPR>(k0, k1);
+  if (valid && j == 0) a.cos[bh * a.P + p] = c;
+}
+
+// ------------------------------------------------------------------- launchers --
+template <typename T, int D>
+static hipError_t launch_score_valu(const Shape& s, const RoundP& r, const P1Args& p1, const P2Args& p2,
+                                    const CosArgs& ca, float* lse, float* O, hipStream_t st) {
+  const int64_t BH = (int64_t)s.B * s.Hkv;
+  const int nqb = (int)((p1.GW + 127) / 128);
+  hipLaunchKernelGGL((pass1_valu_kernel<T, D>), dim3(p1.nsplit, nqb, BH), dim3(256), 0, st, p1);
+  hipLaunchKernelGGL(combine_kernel, dim3(BH * p1.GW), dim3(D), 0, st, p1.part, p1.nsplit, D, lse, O);
+  if (ca.cos && r.P > 0) {
+    constexpr int GPB = 256 / (D / Elt<T>::kPerChunk);
+    hipLaunchKernelGGL((pair_cos_kernel<T, D>), dim3((r.P + GPB - 1) / GPB, BH), dim3(256), 0, st, ca);
+  }
+  const int64_t units = r.S + r.P + (s.N - r.S - 2 * r.P);
+  if (p2.n)
+    hipLaunchKernelGGL((pass2_valu_kernel<T, D, true>), dim3((units + 63) / 64, BH), dim3(256), 0, st, p2);
+  else
+    hipLaunchKernelGGL((pass2_valu_kernel<T, D, false>), dim3((units + 63) / 64, BH), dim3(256), 0, st, p2);
+  return hipGetLastError();
+}
+
+size_t score_workspace_bytes(const Shape& s, const RoundP& r) {
+  if (use_mfma_scorer(s)) return mfma_score_workspace_bytes(s, r);
+  const int64_t GW = (int64_t)s.G * r.W;
+  int64_t chunk;
+  int nsplit;
+  valu_pass1_plan(s.N, chunk, nsplit);
+  return (size_t)s.B * s.Hkv * GW * nsplit * (s.D + 4) * sizeof(float);
+}
+
+hipError_t launch_score(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                        const void* Qw, float* lse, float* O, float* g_self, float* g_cross, float* cos,
+                        void* ws, hipStream_t st) {
+  if (use_mfma_scorer(s)) return launch_score_mfma(s, r, K, V, n, Qw, lse, O, g_self, g_cross, cos, ws, st);
+  P1Args p1;
+  p1.K = K;
+  p1.V = V;
+  p1.n = n;
+  p1.Qw = Qw;
+  p1.part = static_cast<float*>(ws);
+  p1.N = s.N;
+  p1.sb = s.sb;
+  p1.sh = s.sh;
+  p1.Hkv = s.Hkv;
+  p1.Hq = s.Hq;
+  p1.G = s.G;
+  p1.W = r.W;
+  p1.GW = (int64_t)s.G * r.W;
+  p1.scale = r.scale;
+  valu_pass1_plan(s.N, p1.chunk, p1.nsplit);
+  P2Args p2;
+  p2.K = K;
+  p2.V = V;
+  p2.n = n;
+  p2.Qw = Qw;
+  p2.lse = lse;
+  p2.O = O;
+  p2.g_self = g_self;
+  p2.g_cross = g_cross;
+  p2.N = s.N;
+  p2.S = r.S;
+  p2.P = r.P;
+  p2.sb = s.sb;
+  p2.sh = s.sh;
+  p2.Hkv = s.Hkv;
+  p2.Hq = s.Hq;
+  p2.G = s.G;
+  p2.W = r.W;
+  p2.GW = p1.GW;
+  p2.scale = r.scale;
+  CosArgs ca;
+  ca.K = K;
+  ca.cos = cos;
+  ca.S = r.S;
+  ca.P = r.P;
+  ca.sb = s.sb;
+  ca.sh = s.sh;
+  ca.Hkv = s.Hkv;
+  if (s.bf16)
+    return s.D == 64 ? launch_score_valu<bf16, 64>(s, r, p1, p2, ca, lse, O, st)
+                     : launch_score_valu<bf16, 128>(s, r, p1, p2, ca, lse, O, st);
+  return s.D == 64 ? launch_score_valu<float, 64>(s, r, p1, p2, ca, lse, O, st)
+                   : launch_score_valu<float, 128>(s, r, p1, p2, ca, lse, O, st);
+}
+
+}  // namespace kvs

@@ -1,0 +1,58 @@
+// Argument blocks and dispatch hooks shared by the VALU and MFMA scorer kernels.
+#pragma once
+
+#include "kvs_internal.h"
+
+namespace kvs {
+
+struct P1Args {
+  const void* K;
+  const void* V;
+  const int32_t* n;
+  const void* Qw;
+  float* part;       // partial records [B*Hkv][GW][nsplit][D + 4]
+  int64_t N, sb, sh, GW, chunk;
+  int Hkv, Hq, G, W, nsplit;
+  float scale;
+};
+
+struct P2Args {
+  const void* K;
+  const void* V;
+  const int32_t* n;
+  const void* Qw;
+  const float* lse;
+  const float* O;
+  float* g_self;
+  float* g_cross;
+  int64_t N, S, P, sb, sh, GW;
+  int Hkv, Hq, G, W;
+  float scale;
+};
+
+struct CosArgs {
+  const void* K;
+  float* cos;
+  int64_t S, P, sb, sh;
+  int Hkv;
+};
+
+// Slot splits of the VALU pass 1: about 512 slots per workgroup, at most 256 splits,
+// every split non-empty.
+inline void valu_pass1_plan(int64_t N, int64_t& chunk, int& nsplit) {
+  int64_t k = (N + 511) / 512;
+  if (k < 1) k = 1;
+  if (k > 256) k = 256;
+  chunk = (N + k - 1) / k;
+  if (chunk < 1) chunk = 1;
+  nsplit = (int)((N + chunk - 1) / chunk);
+  if (nsplit < 1) nsplit = 1;
+}
+
+bool use_mfma_scorer(const Shape& s);
+size_t mfma_score_workspace_bytes(const Shape& s, const RoundP& r);
+hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                             const void* Qw, float* lse, float* O, float* g_self, float* g_cross, float* cos,
+                             void* ws, hipStream_t st);
+
+}  // namespace kvs

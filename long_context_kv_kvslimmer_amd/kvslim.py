@@ -1,0 +1,161 @@
+"""ctypes binding of libkvslim.so (C ABI in include/kvslim.h).
+
+Argument marshalling only: tensors are passed as device pointers, shapes as the
+kvs_cache / kvs_round structs, and the current torch stream as the HIP stream.
+Every step of the path runs in the library's HIP kernels; if the library is
+missing this module raises at import time, so nothing falls back to another path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvslim.so")
+
+KVS_OK, KVS_ERR_NULL, KVS_ERR_SHAPE, KVS_ERR_DTYPE, KVS_ERR_STRIDE, KVS_ERR_ALIGN, \
+    KVS_ERR_INFEASIBLE, KVS_ERR_WORKSPACE, KVS_ERR_HIP = range(9)
+KVS_BF16, KVS_F32 = 0, 1
+KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE = range(4)
+
+EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_merge_weights", "kvs_merge_compact",
+           "kvs_decode_attn", "kvs_status_str", "kvs_last_error", "kvs_version")
+
+
+class KvsCache(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("n_slots", ctypes.c_int64), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64)]
+
+
+class KvsRound(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("n_sink", ctypes.c_int64), ("n_recent", ctypes.c_int64),
+                ("n_merge", ctypes.c_int64), ("sm_scale", ctypes.c_float)]
+
+
+class KvsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_str(status)}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m long_context_kv_kvslimmer_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    C, R = ctypes.POINTER(KvsCache), ctypes.POINTER(KvsRound)
+    sig = {
+        "kvs_num_pairs": (I64, [I64, I64, I64]),
+        "kvs_workspace_bytes": (SZ, [ctypes.c_int, C, R]),
+        "kvs_score": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, R, P, P, P, P, P, P, SZ, P]),
+        "kvs_merge_weights": (ctypes.c_int, [C, R, P, P, P, P, P, P, SZ, P, SZ, P]),
+        "kvs_merge_compact": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, P, R, P, C, ctypes.c_int, P, P, P, P, P]),
+        "kvs_decode_attn": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, F, P, P, SZ, P]),
+        "kvs_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "kvs_last_error": (ctypes.c_char_p, []),
+        "kvs_version": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def status_str(s: int) -> str:
+    return _lib.kvs_status_str(s).decode()
+
+
+def last_error() -> str:
+    return _lib.kvs_last_error().decode()
+
+
+def version() -> int:
+    return _lib.kvs_version()
+
+
+def _check(s: int):
+    if s != KVS_OK:
+        raise KvsError(s, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream) if torch.cuda.is_available() else None
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KVS_BF16
+    if t.dtype == torch.float32:
+        return KVS_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def cache_desc(K: torch.Tensor, n_q_heads: int, n_slots: int | None = None) -> KvsCache:
+    """Describe K (or V) of shape [B, H_kv, capacity, D] (rows contiguous) holding n_slots slots."""
+    if K.dim() != 4 or K.stride(3) != 1 or K.stride(2) != K.shape[3]:
+        raise ValueError("cache tensors must be [B, H_kv, capacity, D] with contiguous rows")
+    B, H, cap, D = K.shape
+    n = cap if n_slots is None else n_slots
+    if n > cap:
+        raise ValueError("n_slots exceeds capacity")
+    return KvsCache(B, H, n_q_heads, D, n, K.stride(0), K.stride(1))
+
+
+def round_desc(window: int, n_sink: int, n_recent: int, n_merge: int, sm_scale: float) -> KvsRound:
+    return KvsRound(window, n_sink, n_recent, n_merge, sm_scale)
+
+
+def num_pairs(n_slots: int, n_sink: int, n_recent: int) -> int:
+    return _lib.kvs_num_pairs(n_slots, n_sink, n_recent)
+
+
+def workspace_bytes(op: int, cache: KvsCache, rnd: KvsRound | None) -> int:
+    return _lib.kvs_workspace_bytes(op, ctypes.byref(cache), ctypes.byref(rnd) if rnd is not None else None)
+
+
+def _same_layout(K, V):
+    if K.shape != V.shape or K.stride() != V.stride() or K.dtype != V.dtype:
+        raise ValueError("K and V must share shape, strides and dtype")
+
+
+def kvs_score(cache: KvsCache, K, V, n, Qw, rnd: KvsRound, lse, O, g_self, g_cross, cos, workspace):
+    _same_layout(K, V)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.kvs_score(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(Qw),
+                          ctypes.byref(rnd), _ptr(lse), _ptr(O), _ptr(g_self), _ptr(g_cross), _ptr(cos),
+                          _ptr(workspace), ws_bytes, _stream()))
+
+
+def kvs_merge_weights(cache: KvsCache, rnd: KvsRound, g_self, g_cross, cos, w, selected, sel_state):
+    sb = 0 if sel_state is None else sel_state.numel() * sel_state.element_size()
+    _check(_lib.kvs_merge_weights(ctypes.byref(cache), ctypes.byref(rnd), _ptr(g_self), _ptr(g_cross), _ptr(cos),
+                                  _ptr(w), _ptr(selected), _ptr(sel_state), sb, None, 0, _stream()))
+
+
+def kvs_merge_compact(cache: KvsCache, K, V, n, g_self, g_cross, rnd: KvsRound, sel_state,
+                      out: KvsCache, K_out, V_out, n_out, src_out):
+    _same_layout(K, V)
+    if K_out.dtype != V_out.dtype:
+        raise ValueError("K_out and V_out must share a dtype")
+    _check(_lib.kvs_merge_compact(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(g_self),
+                                  _ptr(g_cross), ctypes.byref(rnd), _ptr(sel_state), ctypes.byref(out),
+                                  dtype_code(K_out), _ptr(K_out), _ptr(V_out), _ptr(n_out), _ptr(src_out),
+                                  _stream()))
+
+
+def kvs_decode_attn(cache: KvsCache, K, V, n, q, sm_scale: float, out, workspace):
+    _same_layout(K, V)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.kvs_decode_attn(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(q),
+                                ctypes.c_float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream()))

@@ -328,7 +328,23 @@ def merge_round(K, V, n, Qw, scale, n_sink, n_recent, n_merge) -> RoundResult:
         w0, w1, f = forward_only_weights(g_self[m], g_cross[p], g_self[m + 1])
         w[p] = (w0, w1)
         fb[p] = f
-    # 6 + 7. merge and compaction, walking the slots in order
+    # 6 + 7. merge and compaction
+    Ko, Vo, no, so = compact(K, V, nn, w, selected, n_sink)
+    return RoundResult(lse=lse, O=O, g_self=g_self, g_cross=g_cross, cos=cos,
+                       selected=selected, w=w, fallback=fb, K=Ko, V=Vo, n=no, src=so,
+                       extras={"alpha": alpha})
+
+
+def compact(K, V, n, w, selected, n_sink):
+    """Steps 6 and 7: walk the slots in order; the first slot i of a selected pair
+    p emits the merged slot (k* = w_m k_m + w_{m+1} k_{m+1}, [DD] 数学主线四; the
+    lossless value slot of ``merge_values``) with src = i and skips i + 1; every
+    other slot is copied with src = i.  Output length N − (number selected)."""
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    N, D = K.shape
+    nn = np.asarray(n, dtype=np.int64)
+    P = len(selected)
     out_k, out_v, out_n, out_src = [], [], [], []
     i = 0
     while i < N:
@@ -348,11 +364,8 @@ def merge_round(K, V, n, Qw, scale, n_sink, n_recent, n_merge) -> RoundResult:
             out_n.append(int(nn[i]))
             out_src.append(i)
             i += 1
-    return RoundResult(lse=lse, O=O, g_self=g_self, g_cross=g_cross, cos=cos,
-                       selected=selected, w=w, fallback=fb,
-                       K=np.array(out_k).reshape(-1, D), V=np.array(out_v).reshape(-1, D),
-                       n=np.array(out_n, dtype=np.int64), src=np.array(out_src, dtype=np.int64),
-                       extras={"alpha": alpha})
+    return (np.array(out_k).reshape(-1, D), np.array(out_v).reshape(-1, D),
+            np.array(out_n, dtype=np.int64), np.array(out_src, dtype=np.int64))
 
 
 def decode(K, V, n, q, scale) -> np.ndarray:

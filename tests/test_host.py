@@ -1,0 +1,146 @@
+"""Host-side checks of the C-ABI library: it loads, exports every declared
+symbol, sizes workspaces, and rejects bad arguments before launching anything.
+No call here reaches a kernel, so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvslim.h")
+LIB = os.path.join(ROOT, "long_context_kv_kvslimmer_amd", "libkvslim.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkvslim.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvs_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    names = _declared()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    from long_context_kv_kvslimmer_amd import kvslim as L
+    assert set(L.EXPORTS) == set(names)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from long_context_kv_kvslimmer_amd import kvslim
+    return kvslim
+
+
+def test_num_pairs(L):
+    assert L.num_pairs(512, 0, 0) == 256
+    assert L.num_pairs(32768, 0, 32) == 16368
+    assert L.num_pairs(131072, 0, 0) == 65536
+    assert L.num_pairs(33, 32, 0) == 0
+    assert L.num_pairs(10, 3, 2) == 2
+    assert L.num_pairs(-1, 0, 0) == 0
+    assert L.version() == 100
+
+
+def _cache(B=1, H=8, Hq=32, D=128, N=32768, sb=None, sh=None):
+    from long_context_kv_kvslimmer_amd import kvslim as L
+    sh = N * D if sh is None else sh
+    sb = H * sh if sb is None else sb
+    return L.KvsCache(B, H, Hq, D, N, sb, sh)
+
+
+def test_workspace_sizes(L):
+    c = _cache()
+    r = L.round_desc(32, 0, 32, 16368, 128 ** -0.5)
+    assert L.workspace_bytes(L.KVS_OP_SCORE, c, r) > 0
+    assert L.workspace_bytes(L.KVS_OP_SELECT, c, r) == 0
+    # selection state: header + one offset per 64-pair chunk + total, per (b, h)
+    P = 16368
+    chunks = (P + 63) // 64
+    per = ((4 + chunks + 1) + 3) // 4 * 4
+    assert L.workspace_bytes(L.KVS_OP_SEL_STATE, c, r) == 8 * per * 4
+    assert L.workspace_bytes(L.KVS_OP_DECODE, c, None) > 0
+    bad = _cache(D=96)
+    assert L.workspace_bytes(L.KVS_OP_SCORE, bad, r) == 0
+
+
+FAKE = ctypes.c_void_p(4096)   # aligned, never dereferenced: every call below fails validation
+
+
+def _score(L, c, r, dtype=0, K=FAKE, V=FAKE, Qw=FAKE, lse=FAKE, O=FAKE, gs=FAKE, gc=FAKE, ws=FAKE, wsb=1 << 30):
+    return L._lib.kvs_score(ctypes.byref(c) if c is not None else None, dtype, K, V, None, Qw,
+                            ctypes.byref(r) if r is not None else None, lse, O, gs, gc, None, ws, wsb, None)
+
+
+def test_score_validation(L):
+    r = L.round_desc(32, 0, 32, 16368, 0.1)
+    assert _score(L, None, r) == L.KVS_ERR_NULL
+    assert _score(L, _cache(), None) == L.KVS_ERR_NULL
+    assert _score(L, _cache(D=96), r) == L.KVS_ERR_SHAPE
+    assert _score(L, _cache(Hq=30), r) == L.KVS_ERR_SHAPE
+    assert _score(L, _cache(sh=32768 * 128 + 1), r) == L.KVS_ERR_STRIDE
+    assert _score(L, _cache(), r, dtype=7) == L.KVS_ERR_DTYPE
+    assert _score(L, _cache(), r, K=None) == L.KVS_ERR_NULL
+    assert _score(L, _cache(), r, gc=None) == L.KVS_ERR_NULL
+    assert _score(L, _cache(), r, K=ctypes.c_void_p(4100)) == L.KVS_ERR_ALIGN
+    assert _score(L, _cache(), r, wsb=16) == L.KVS_ERR_WORKSPACE
+    assert _score(L, _cache(), L.round_desc(32, 0, 32, 16369, 0.1)) == L.KVS_ERR_INFEASIBLE
+    assert _score(L, _cache(), L.round_desc(32, 0, 32, -1, 0.1)) == L.KVS_ERR_INFEASIBLE
+    assert _score(L, _cache(), L.round_desc(0, 0, 32, 10, 0.1)) == L.KVS_ERR_SHAPE
+    assert _score(L, _cache(N=0), L.round_desc(32, 0, 0, 0, 0.1)) == L.KVS_ERR_SHAPE
+    assert _score(L, _cache(), L.round_desc(32, 0, 32, 10, float("nan"))) == L.KVS_ERR_SHAPE
+    assert "n_merge" in L.last_error() or "sm_scale" in L.last_error()
+
+
+def test_merge_weights_validation(L):
+    c = _cache()
+    r = L.round_desc(32, 0, 32, 100, 0.1)
+    f = L._lib.kvs_merge_weights
+    assert f(ctypes.byref(c), ctypes.byref(r), FAKE, FAKE, FAKE, None, None, None, 0, None, 0, None) == L.KVS_ERR_NULL
+    # a partial round needs the cosine
+    assert f(ctypes.byref(c), ctypes.byref(r), FAKE, FAKE, None, None, None, FAKE, 1 << 30, None, 0,
+             None) == L.KVS_ERR_NULL
+    assert f(ctypes.byref(c), ctypes.byref(r), FAKE, FAKE, FAKE, None, None, FAKE, 16, None, 0,
+             None) == L.KVS_ERR_WORKSPACE
+
+
+def test_merge_compact_validation(L):
+    c = _cache()
+    r = L.round_desc(32, 0, 32, 16368, 0.1)
+    f = L._lib.kvs_merge_compact
+    good_out = _cache(N=32768 - 16368, sh=(32768 - 16368) * 128)
+    wrong_len = _cache(N=32768 - 16367, sh=(32768 - 16368) * 128)
+    wrong_dim = L.KvsCache(1, 8, 32, 64, 32768 - 16368, 8 * 16400 * 64, 16400 * 64)
+
+    def call(out, sel=None, K=FAKE, rr=r, dt=0):
+        return f(ctypes.byref(c), 0, K, FAKE, None, FAKE, FAKE, ctypes.byref(rr), sel,
+                 ctypes.byref(out) if out is not None else None, dt, FAKE, FAKE, FAKE, FAKE, None)
+    assert call(None) == L.KVS_ERR_NULL
+    assert call(wrong_len) == L.KVS_ERR_SHAPE
+    assert call(wrong_dim) == L.KVS_ERR_SHAPE
+    assert call(good_out, K=None) == L.KVS_ERR_NULL
+    assert call(good_out, K=ctypes.c_void_p(4104)) == L.KVS_ERR_ALIGN
+    assert call(good_out, dt=5) == L.KVS_ERR_DTYPE
+    partial = L.round_desc(32, 0, 32, 100, 0.1)
+    part_out = _cache(N=32768 - 100, sh=(32768 - 100) * 128)
+    assert call(part_out, sel=None, rr=partial) == L.KVS_ERR_NULL     # partial round needs sel_state
+
+
+def test_decode_validation(L):
+    f = L._lib.kvs_decode_attn
+    c = _cache()
+    assert f(ctypes.byref(c), 0, FAKE, FAKE, None, FAKE, 0.1, FAKE, FAKE, 16, None) == L.KVS_ERR_WORKSPACE
+    assert f(ctypes.byref(_cache(Hq=24)), 0, FAKE, FAKE, None, FAKE, 0.1, FAKE, FAKE, 1 << 30,
+             None) == L.KVS_ERR_SHAPE   # group 3
+    assert f(ctypes.byref(_cache(N=0)), 0, FAKE, FAKE, None, FAKE, 0.1, FAKE, FAKE, 1 << 30,
+             None) == L.KVS_ERR_SHAPE
+    assert f(ctypes.byref(c), 0, FAKE, FAKE, None, None, 0.1, FAKE, FAKE, 1 << 30, None) == L.KVS_ERR_NULL
+
+
+def test_status_strings(L):
+    for s in range(9):
+        assert L.status_str(s).startswith("KVS_")
