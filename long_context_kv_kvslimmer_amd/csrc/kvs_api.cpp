@@ -89,9 +89,14 @@ size_t kvs_workspace_bytes(kvs_op op, const kvs_cache* cache, const kvs_round* r
   if (check_cache(cache, KVS_BF16, s) != KVS_OK) return 0;
   kvs::RoundP r{};
   switch (op) {
-    case KVS_OP_SCORE:
+    case KVS_OP_SCORE: {
+      // the size depends on the element type; report the larger of the two
       if (!round || check_round(round, s, r, true) != KVS_OK) return 0;
-      return kvs::score_workspace_bytes(s, r);
+      const size_t bf = kvs::score_workspace_bytes(s, r);
+      s.bf16 = false;
+      const size_t f32 = kvs::score_workspace_bytes(s, r);
+      return bf > f32 ? bf : f32;
+    }
     case KVS_OP_SELECT:
       return 0;
     case KVS_OP_SEL_STATE:

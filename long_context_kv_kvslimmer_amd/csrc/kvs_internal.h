@@ -52,6 +52,8 @@ hipError_t launch_merge(const Shape& s, const RoundP& r, const void* K, const vo
 hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, float* lse, float* out,
                           hipStream_t st);
 
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
 // ---- decode ----
 size_t decode_workspace_bytes(const Shape& s);
 hipError_t launch_decode(const Shape& s, const void* K, const void* V, const int32_t* n, const void* q,

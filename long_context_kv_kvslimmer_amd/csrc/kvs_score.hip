@@ -120,29 +120,71 @@ __global__ __launch_bounds__(256) void pass1_valu_kernel(P1Args a) {
 
 // --------------------------------------------------------- log-sum-exp combine --
 // One block of D threads per unit; partial records {m (log2 units), l, -, -, o[D]}.
-// Writes lse (natural log, nullable) and the normalised output row.
-__global__ void combine_kernel(const float* __restrict__ part, int nsplit, int D, float* __restrict__ lse,
-                               float* __restrict__ out) {
+// The split weights 2^(m_s - M) are staged in LDS, so each thread's pass over the
+// splits issues independent loads.  Writes lse (natural log, nullable) and the row.
+constexpr int kMaxSplit = 1024;
+
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part, int nsplit, int D,
+                                                      float* __restrict__ lse, float* __restrict__ out) {
+  __shared__ float wsh[kMaxSplit];
+  __shared__ float red[128];
   const int64_t u = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* r = part + u * nsplit * (int64_t)(D + 4);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, r[s * (int64_t)(D + 4)]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* q = r + s * (int64_t)(D + 4);
-    const float f = exp2f(q[0] - M);
-    L = __builtin_fmaf(q[1], f, L);
-    acc = __builtin_fmaf(q[4 + d], f, acc);
+  const int tid = threadIdx.x;
+  const int64_t rs = D + 4;
+  const float* r = part + u * nsplit * rs;
+  float mx = -INFINITY;
+  for (int s = tid; s < nsplit; s += blockDim.x) {
+    const float v = r[s * rs];
+    wsh[s] = v;
+    mx = fmaxf(mx, v);
   }
-  out[u * D + d] = acc / L;
-  if (lse && d == 0) lse[u] = (M + __log2f(L)) * kLn2;
+  red[tid] = mx;
+  __syncthreads();
+  for (int k = blockDim.x / 2; k > 0; k >>= 1) {
+    if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float L = 0.f;
+  for (int s = tid; s < nsplit; s += blockDim.x) {
+    const float f = wsh[s] == -INFINITY ? 0.f : exp2f(wsh[s] - M);
+    wsh[s] = f;
+    L = __builtin_fmaf(r[s * rs + 1], f, L);
+  }
+  red[tid] = L;
+  __syncthreads();
+  for (int k = blockDim.x / 2; k > 0; k >>= 1) {
+    if (tid < k) red[tid] += red[tid + k];
+    __syncthreads();
+  }
+  L = red[0];
+  for (int d = tid; d < D; d += blockDim.x) {
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) acc = __builtin_fmaf(r[s * rs + 4 + d], wsh[s], acc);
+    out[u * D + d] = acc / L;
+  }
+  if (lse && tid == 0) lse[u] = (M + __log2f(L)) * kLn2;
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, float* lse, float* out,
                           hipStream_t st) {
   if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(units), dim3(D), 0, st, part, nsplit, D, lse, out);
+  if (nsplit > kMaxSplit) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3(units), dim3(128), 0, st, part, nsplit, D, lse, out);
   return hipGetLastError();
 }
 
@@ -269,7 +311,7 @@ static hipError_t launch_score_valu(const Shape& s, const RoundP& r, const P1Arg
   const int64_t BH = (int64_t)s.B * s.Hkv;
   const int nqb = (int)((p1.GW + 127) / 128);
   hipLaunchKernelGGL((pass1_valu_kernel<T, D>), dim3(p1.nsplit, nqb, BH), dim3(256), 0, st, p1);
-  hipLaunchKernelGGL(combine_kernel, dim3(BH * p1.GW), dim3(D), 0, st, p1.part, p1.nsplit, D, lse, O);
+  launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st);
   if (ca.cos && r.P > 0) {
     constexpr int GPB = 256 / (D / Elt<T>::kPerChunk);
     hipLaunchKernelGGL((pair_cos_kernel<T, D>), dim3((r.P + GPB - 1) / GPB, BH), dim3(256), 0, st, ca);
