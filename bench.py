@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0
 def algorithmic_bytes(N, H, D, P, M, T, has_n=False, elt=2):
     """Bytes each call must move (the method's reads and writes, once each)."""
     row = 2 * D * elt                               # one K row + one V row
-    score = 2 * N * H * row + N * H * 4 + 2 * P * H * 4 + 0   # K,V twice; g_self, g_cross, cos out
+    score = 2 * N * H * row + N * H * 4 + P * H * 4   # K,V twice; g_self, g_cross out
     merge = N * H * (row + 4 + (4 if has_n else 0)) + P * H * 4 + T * H * (row + 4 + 4)
     decode = T * H * (row + 4)
     select = 0
@@ -98,15 +98,18 @@ def main():
     rnd = L.round_desc(W, S, R, M, 1.0 / math.sqrt(D))
     out_desc = L.cache_desc(bufs.K, Hq, T)
     names = ("kvs_score", "kvs_merge_weights", "kvs_merge_compact", "kvs_decode_attn")
+    # the adjacent-key cosine only feeds the selection; a round that merges every
+    # candidate pair (or none) has nothing to select, so it is not requested then
+    cos_out = bufs.cos if 0 < M < P else None
 
     def step(i, ev=None):
         K, V, Qw, q = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        L.kvs_score(cache, K, V, None, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, bufs.cos, bufs.score_ws)
+        L.kvs_score(cache, K, V, None, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, cos_out, bufs.score_ws)
         if ev is not None:
             ev[1].record()
-        L.kvs_merge_weights(cache, rnd, bufs.g_self, bufs.g_cross, bufs.cos, None, None, bufs.sel_state)
+        L.kvs_merge_weights(cache, rnd, bufs.g_self, bufs.g_cross, cos_out, None, None, bufs.sel_state)
         if ev is not None:
             ev[2].record()
         L.kvs_merge_compact(cache, K, V, None, bufs.g_self, bufs.g_cross, rnd, bufs.sel_state, out_desc,

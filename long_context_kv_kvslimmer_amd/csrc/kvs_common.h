@@ -97,20 +97,41 @@ __device__ __forceinline__ void store_elems<bf16, 8>(bf16* p, const float* f) {
                                             f32_to_bf16_bits(f[6]) | (f32_to_bf16_bits(f[7]) << 16));
 }
 
-// Butterfly sum over aligned groups of L lanes (L a power of two <= 64).  Every lane of a
-// group ends with the same bits (floating-point addition is commutative), so the result
-// does not depend on which lane reads it.
+// Cross-lane moves inside a 16-lane row (DPP): lane i reads lane i^1, i^2, the mirror
+// within its 8-lane half (7 - i) or within its row (15 - i).  On data that is already
+// uniform over 4 (resp. 8) lanes the two mirrors pair exactly as i^4 (resp. i^8).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// Butterfly sum over aligned groups of L lanes (L a power of two <= 64): DPP inside a
+// 16-lane row, shuffles across rows.  Every lane of a group ends with the same bits
+// (floating-point addition is commutative), so the result does not depend on which lane
+// reads it.
 template <int L>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int off = L / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  if constexpr (L >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (L >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (L >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (L >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (L >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (L >= 64) x += __shfl_xor(x, 32, 64);
   return x;
 }
 
 template <int L>
 __device__ __forceinline__ float group_max(float x) {
-#pragma unroll
-  for (int off = L / 2; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  if constexpr (L >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
+  if constexpr (L >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
+  if constexpr (L >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if constexpr (L >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
+  if constexpr (L >= 32) x = fmaxf(x, __shfl_xor(x, 16, 64));
+  if constexpr (L >= 64) x = fmaxf(x, __shfl_xor(x, 32, 64));
   return x;
 }
 
@@ -137,7 +158,7 @@ __device__ __forceinline__ float pair_cos(const float* a, const float* b) {
   const int lane = threadIdx.x & 63;
   const uint64_t gmask = (LPR == 64 ? ~0ull : ((1ull << LPR) - 1ull)) << (lane & ~(LPR - 1));
   if (na == 0.f || nb == 0.f) return (neq & gmask) ? 0.f : 1.f;
-  float c = d / (sqrtf(na) * sqrtf(nb));
+  const float c = d * __builtin_amdgcn_rsqf(na) * __builtin_amdgcn_rsqf(nb);
   return c + 0.0f;
 }
 

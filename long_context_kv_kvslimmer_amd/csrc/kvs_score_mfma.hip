@@ -33,7 +33,9 @@ template <int D>
 struct TileCfg {
   static constexpr int KB = D / 32;          // 32-wide k blocks of the head dim
   static constexpr int DB = D / 16;          // 16-wide blocks of the head dim
-  static constexpr int PITCH = D + 8;        // bf16 elements per LDS row (16-byte pad)
+  // bf16 elements per LDS row: a 32-byte pad moves consecutive rows 8 banks apart, so the
+  // 16-byte row reads (8 lanes per cycle) and the 4-row transpose reads are conflict-free
+  static constexpr int PITCH = D + 16;
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
 };
 
@@ -41,6 +43,10 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
   u32x4_t v = {u.x, u.y, u.z, u.w};
   return __builtin_bit_cast(bf16x8_t, v);
 }
+
+// Finite stand-in for "no maximum yet": exp2(x - kNoMax) underflows to 0 for any finite x,
+// and exp2(-inf - kNoMax) is 0 as well, so masked slots need no special case.
+constexpr float kNoMax = -1e30f;
 
 __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -56,29 +62,53 @@ __device__ __forceinline__ void split_hi_lo(const float* x, bf16x8_t& hi, bf16x8
   }
 }
 
-// Cooperative load of a 64-slot tile of K and V rows [t0, t0+64) into LDS (zeros outside
-// [lo, hi)).  NT threads, 16-byte chunks.
+// Register-staged tile of K and V rows [t0, t0 + 64): each of NT threads fetches its
+// 16-byte chunks (zeros outside [lo, hi)) so the loads stay in flight while the previous
+// tile is computed, then commits them to LDS.
 template <int D, int NT>
-__device__ __forceinline__ void load_tile(const bf16* Kp, const bf16* Vp, int64_t t0, int64_t lo, int64_t hi,
-                                          bf16* Kt, bf16* Vt) {
+struct TileStage {
   using C = TileCfg<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < kTile * C::CPR / NT; ++it) {
-    const int idx = it * NT + tid;
-    const int row = idx / C::CPR, ch = idx % C::CPR;
-    const int64_t s = t0 + row;
-    uint4 k = make_uint4(0, 0, 0, 0), v = make_uint4(0, 0, 0, 0);
-    if (s >= lo && s < hi) {
-      k = load16(Kp + s * D + ch * 8);
-      v = load16(Vp + s * D + ch * 8);
-    }
-    *reinterpret_cast<uint4*>(Kt + row * C::PITCH + ch * 8) = k;
-    *reinterpret_cast<uint4*>(Vt + row * C::PITCH + ch * 8) = v;
-  }
-}
+  static constexpr int NPT = kTile * C::CPR / NT;
+  uint4 k[NPT], v[NPT];
+  float lg;
 
-// Q rows as the B operand: lane l holds Q[q = qbase + l%16][d = 32 kb + 8 (l/16) .. +7].
+  template <bool HAS_N>
+  __device__ __forceinline__ void fetch(const bf16* Kp, const bf16* Vp, const int32_t* np, int64_t t0, int64_t lo,
+                                        int64_t hi) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < NPT; ++it) {
+      const int idx = it * NT + tid;
+      const int row = idx / C::CPR, ch = idx % C::CPR;
+      const int64_t s = t0 + row;
+      if (s >= lo && s < hi) {
+        k[it] = load16(Kp + s * D + ch * 8);
+        v[it] = load16(Vp + s * D + ch * 8);
+      } else {
+        k[it] = v[it] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < kTile) {
+      const int64_t s = t0 + tid;
+      lg = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)np[s]) : 0.f) : -INFINITY;
+    }
+  }
+
+  __device__ __forceinline__ void commit(bf16* Kt, bf16* Vt, float* lgs) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < NPT; ++it) {
+      const int idx = it * NT + tid;
+      const int row = idx / C::CPR, ch = idx % C::CPR;
+      *reinterpret_cast<uint4*>(Kt + row * C::PITCH + ch * 8) = k[it];
+      *reinterpret_cast<uint4*>(Vt + row * C::PITCH + ch * 8) = v[it];
+    }
+    if (tid < kTile) lgs[tid] = lg;
+  }
+};
+
+// Q (or any fp32-free bf16 row block) as an MFMA operand: lane l holds
+// Q[q = l%16][d = 32 kb + 8 (l/16) .. +7] of the 16 rows starting at query q.
 template <int D>
 __device__ __forceinline__ void load_q(const bf16* Qp, int64_t GW, int64_t q, bf16x8_t (&qop)[TileCfg<D>::KB]) {
   const int g = (threadIdx.x & 63) >> 4;
@@ -90,16 +120,18 @@ __device__ __forceinline__ void load_q(const bf16* Qp, int64_t GW, int64_t q, bf
   }
 }
 
+constexpr int kThreads = 512;   // 8 waves x 16 window queries
+
 // ------------------------------------------------------------------------- pass 1 --
 // grid: x = slot chunk, y = query block (128), z = (b, kv-head); eight waves of 16 queries
 // share each LDS tile.  Partial records as the VALU pass 1: {m (log2 units), l, -, -, o[D]}
 // per (bh, query, chunk).
 template <int D, bool HAS_N>
-__global__ __launch_bounds__(512, 1) void p1_mfma_kernel(P1Args a, int64_t base, CosArgs ca) {
+__global__ __launch_bounds__(kThreads, 1) void p1_mfma_kernel(P1Args a, int64_t base, CosArgs ca) {
   using C = TileCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 Kt[kTile * C::PITCH];
   __shared__ __attribute__((aligned(16))) bf16 Vt[kTile * C::PITCH];
-  __shared__ float lg[kTile];
+  __shared__ __attribute__((aligned(16))) float lgs[kTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -111,38 +143,33 @@ __global__ __launch_bounds__(512, 1) void p1_mfma_kernel(P1Args a, int64_t base,
   const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + h * a.G) * (int64_t)a.W) * D;
 
   const int64_t q0 = (int64_t)blockIdx.y * kQB + wv * 16;
-  bf16x8_t qop[1][C::KB];
-  load_q<D>(Qp, a.GW, q0 + c16, qop[0]);
+  bf16x8_t qop[C::KB];
+  load_q<D>(Qp, a.GW, q0 + c16, qop);
 
   const float cs = a.scale * kLog2e;
-  float m[1] = {-INFINITY}, lsum[1] = {0.f};
-  f32x4_t acc[1][C::DB];
+  float m = kNoMax, lsum = 0.f;
+  f32x4_t acc[C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) acc[0][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int64_t c0 = base + (int64_t)blockIdx.x * a.chunk;
   const int64_t c1 = c0 + a.chunk;
   const int64_t lo = c0 > 0 ? c0 : 0;
   const int64_t hi = c1 < a.N ? c1 : a.N;
+  const int64_t tend = c1 < a.N ? c1 : a.N;
   const bool do_cos = ca.cos != nullptr && blockIdx.y == 0;
 
-  for (int64_t t0 = c0; t0 < c1 && t0 < a.N; t0 += kTile) {
-    __syncthreads();
-    load_tile<D, 512>(Kp, Vp, t0, lo, hi, Kt, Vt);
-    if (tid < kTile) {
-      const int64_t s = t0 + tid;
-      lg[tid] = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)np[s]) : 0.f) : -INFINITY;
-    }
-    __syncthreads();
+  // two register stages keep two tiles (64 KB) of loads in flight per workgroup
+  auto compute = [&](int64_t t0) {
 
-    // adjacent-key cosine of the tile's candidate pairs (row layout: 16 lanes x 8 elements)
+    // adjacent-key cosine of the tile's candidate pairs (row layout: LPR lanes x 8 elements)
     if (do_cos) {
       constexpr int LPR = D / 8;
-      constexpr int GPB = 512 / LPR;
+      constexpr int GPB = kThreads / LPR;
       const int grp = tid / LPR, j = tid % LPR;
 #pragma unroll
       for (int pp0 = 0; pp0 < kTile / 2; pp0 += GPB) {
-        const int pp = (pp0 + grp) & (kTile / 2 - 1);   // groups beyond the tile's pairs repeat a pair, unwritten
+        const int pp = (pp0 + grp) & (kTile / 2 - 1);   // surplus groups repeat a pair and write nothing
         const int64_t m0 = t0 + 2 * pp;
         float k0[8], k1[8];
         unpack<bf16>(*reinterpret_cast<const uint4*>(Kt + (2 * pp) * C::PITCH + j * 8), k0);
@@ -154,109 +181,127 @@ __global__ __launch_bounds__(512, 1) void p1_mfma_kernel(P1Args a, int64_t base,
       }
     }
 
-    // per query block: S^T = K . Q^T over the tile (4 slot blocks), then the online
-    // softmax for the lane's query (lane % 16) over slots 16 sb + 4 g + r
-    {
-      constexpr int qb = 0;
-      f32x4_t st[4];
+    // S^T = K . Q^T over the tile (4 slot blocks); online softmax for the lane's query
+    f32x4_t st[4];
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        st[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < 4; ++sb) {
+      st[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-          const bf16x8_t ak =
-              as_bf16x8(*reinterpret_cast<const uint4*>(Kt + (sb * 16 + c16) * C::PITCH + kb * 32 + g * 8));
-          st[sb] = mfma(ak, qop[qb][kb], st[sb]);
-        }
-      }
-      float e[4][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[sb][r] = __builtin_fmaf(st[sb][r], cs, lg[sb * 16 + g * 4 + r]);
-          mx = fmaxf(mx, e[sb][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m[qb], mx);
-      const float corr = (m[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[qb] - mn);
-      m[qb] = mn;
-      lsum[qb] *= corr;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[qb][db] *= corr;
-      float p[4][4];
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[sb][r] = (mn == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(e[sb][r] - mn);
-          lsum[qb] += p[sb][r];
-        }
-      // O^T += V^T . P^T, two 32-slot halves; k index j <-> slot 32 h + 16 (j / 4) + 4 g + j % 4
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float pv[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pv[r] = p[2 * hf][r];
-          pv[4 + r] = p[2 * hf + 1][r];
-        }
-        bf16x8_t phi, plo;
-        split_hi_lo(pv, phi, plo);
-        // source lane i = lane % 16 points at row 32 hf + 16 half2 + 4 g + i / 4, cols 16 db + 4 (i % 4)
-        const int srow = 32 * hf + 4 * g + (c16 >> 2);
-        const int scol = 4 * (c16 & 3);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-          const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(Vt + srow * C::PITCH + db * 16 + scol));
-          const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(Vt + (srow + 16) * C::PITCH + db * 16 + scol));
-          const bf16x8_t vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          acc[qb][db] = mfma(vop, phi, acc[qb][db]);
-          acc[qb][db] = mfma(vop, plo, acc[qb][db]);
-        }
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const bf16x8_t ak =
+            as_bf16x8(*reinterpret_cast<const uint4*>(Kt + (sb * 16 + c16) * C::PITCH + kb * 32 + g * 8));
+        st[sb] = mfma(ak, qop[kb], st[sb]);
       }
     }
+    float e[4][4];
+    float mx = kNoMax;
+    const bool plain = !HAS_N && t0 >= lo && t0 + kTile <= hi;   // every slot valid, count 1
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const float4 lg4 = plain ? make_float4(0.f, 0.f, 0.f, 0.f)
+                               : *reinterpret_cast<const float4*>(lgs + sb * 16 + g * 4);
+      const float lgv[4] = {lg4.x, lg4.y, lg4.z, lg4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e[sb][r] = __builtin_fmaf(st[sb][r], cs, lgv[r]);
+        mx = fmaxf(mx, e[sb][r]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx > m) {   // rescale only when the running max grows (finite sentinel: no NaN paths)
+      const float corr = __builtin_amdgcn_exp2f(m - mx);
+      lsum *= corr;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) acc[db] *= corr;
+      m = mx;
+    }
+    float p[4][4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[sb][r] = __builtin_amdgcn_exp2f(e[sb][r] - m);
+        lsum += p[sb][r];
+      }
+    // O^T += V^T . P^T, two 32-slot halves; k index j <-> slot 32 hf + 16 (j / 4) + 4 g + j % 4
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float pv[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = p[2 * hf][r];
+        pv[4 + r] = p[2 * hf + 1][r];
+      }
+      bf16x8_t phi, plo;
+      split_hi_lo(pv, phi, plo);
+      // transposed read: source lane i = lane % 16 points at row 32 hf + 4 g + i / 4 (+16),
+      // columns 16 db + 4 (i % 4); lane t receives column 16 db + t of four consecutive rows
+      const int srow = 32 * hf + 4 * g + (c16 >> 2);
+      const int scol = 4 * (c16 & 3);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+        const bf16x4_t v0 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vt + srow * C::PITCH + db * 16 + scol));
+        const bf16x4_t v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vt + (srow + 16) * C::PITCH + db * 16 + scol));
+        const bf16x8_t vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[db] = mfma(vop, phi, acc[db]);
+        acc[db] = mfma(vop, plo, acc[db]);
+      }
+    }
+  };
+  TileStage<D, kThreads> sa, sb2;
+  sa.template fetch<HAS_N>(Kp, Vp, np, c0, lo, hi);
+  if (c0 + kTile < tend) sb2.template fetch<HAS_N>(Kp, Vp, np, c0 + kTile, lo, hi);
+  for (int64_t t0 = c0; t0 < tend; t0 += 2 * kTile) {
+    __syncthreads();
+    sa.commit(Kt, Vt, lgs);
+    __syncthreads();
+    if (t0 + 2 * kTile < tend) sa.template fetch<HAS_N>(Kp, Vp, np, t0 + 2 * kTile, lo, hi);
+    compute(t0);
+    if (t0 + kTile >= tend) break;
+    __syncthreads();
+    sb2.commit(Kt, Vt, lgs);
+    __syncthreads();
+    if (t0 + 3 * kTile < tend) sb2.template fetch<HAS_N>(Kp, Vp, np, t0 + 3 * kTile, lo, hi);
+    compute(t0 + kTile);
   }
 
   // per-query partial record: the four lane groups hold disjoint slots of the same query
-  {
-    constexpr int qb = 0;
-    float l = lsum[qb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const int64_t q = q0 + c16;
-    if (q < a.GW) {
-      float* rec = a.part + ((bh * a.GW + q) * a.nsplit + blockIdx.x) * (int64_t)(D + 4);
-      if (g == 0) {
-        rec[0] = m[qb];
-        rec[1] = l;
-      }
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rec[4 + db * 16 + g * 4 + r] = acc[qb][db][r];
+  float l = lsum;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  const int64_t q = q0 + c16;
+  if (q < a.GW) {
+    float* rec = a.part + ((bh * a.GW + q) * a.nsplit + blockIdx.x) * (int64_t)(D + 4);
+    if (g == 0) {
+      rec[0] = m;
+      rec[1] = l;
     }
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rec[4 + db * 16 + g * 4 + r] = acc[db][r];
   }
 }
 
 // ------------------------------------------------------------------------- pass 2 --
-// grid: x = slot chunk, y = query block (128), z = (b, kv-head).  With more than one query
-// block the per-slot sums are accumulated with atomics (not the case for <= 128 queries).
+// grid: x = slot chunk, y = query block (128), z = (b, kv-head); eight waves of 16 queries.
+// With more than one query block the per-slot sums are accumulated with atomics (not the
+// case for <= 128 window queries per kv head).
 template <int D, bool HAS_N>
-__global__ __launch_bounds__(256, 2) void p2_mfma_kernel(P2Args a, int64_t base, int64_t chunk) {
+__global__ __launch_bounds__(kThreads, 1) void p2_mfma_kernel(P2Args a, int64_t base, int64_t chunk) {
   using C = TileCfg<D>;
+  constexpr int NW = kThreads / 64;
   __shared__ __attribute__((aligned(16))) bf16 Kt[kTile * C::PITCH];
   __shared__ __attribute__((aligned(16))) bf16 Vt[kTile * C::PITCH];
-  __shared__ float lg[kTile];
+  __shared__ __attribute__((aligned(16))) float lgs[kTile];
   __shared__ float vn[kTile];
   __shared__ float dv[kTile / 2];
-  __shared__ float red_s[4][kTile];
-  __shared__ float red_x[4][kTile / 2];
+  __shared__ float red_s[NW][kTile];
+  __shared__ float red_x[NW][kTile / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -269,46 +314,34 @@ __global__ __launch_bounds__(256, 2) void p2_mfma_kernel(P2Args a, int64_t base,
   const float* Op = a.O + bh * a.GW * (int64_t)D;
   const float* Lp = a.lse + bh * a.GW;
 
-  const int64_t q0 = (int64_t)blockIdx.y * kQB + wv * 32;
-  bf16x8_t qop[2][C::KB], ohi[2][C::KB], olo[2][C::KB];
-  float nb[2], on[2];
+  // the wave's 16 queries: Q and -2 O (hi + lo) as MFMA operands, ||o||^2, -lse in log2 units
+  const int64_t q = (int64_t)blockIdx.y * kQB + wv * 16 + c16;
+  bf16x8_t qop[C::KB], ohi[C::KB], olo[C::KB];
+  load_q<D>(Qp, a.GW, q, qop);
+  float on = 0.f;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int64_t q = q0 + qb * 16 + c16;
-    load_q<D>(Qp, a.GW, q, qop[qb]);
-    float s2 = 0.f;
+  for (int kb = 0; kb < C::KB; ++kb) {
+    float o8[8];
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      float o8[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float ov = q < a.GW ? Op[q * D + kb * 32 + g * 8 + j] : 0.f;
-        s2 = __builtin_fmaf(ov, ov, s2);
-        o8[j] = -2.f * ov;
-      }
-      split_hi_lo(o8, ohi[qb][kb], olo[qb][kb]);
+    for (int j = 0; j < 8; ++j) {
+      const float ov = q < a.GW ? Op[q * D + kb * 32 + g * 8 + j] : 0.f;
+      on = __builtin_fmaf(ov, ov, on);
+      o8[j] = -2.f * ov;
     }
-    s2 += __shfl_xor(s2, 16, 64);
-    s2 += __shfl_xor(s2, 32, 64);
-    on[qb] = s2;
-    // alpha = exp2(cs * s + log2 n - lse * log2e); padded queries get alpha = 0
-    nb[qb] = q < a.GW ? -Lp[q] * kLog2e : -INFINITY;
+    split_hi_lo(o8, ohi[kb], olo[kb]);
   }
+  on += __shfl_xor(on, 16, 64);
+  on += __shfl_xor(on, 32, 64);
+  const float nb = q < a.GW ? -Lp[q] * kLog2e : -INFINITY;   // padded queries get alpha = 0
   const float cs = a.scale * kLog2e;
 
   const int64_t c0 = base + (int64_t)blockIdx.x * chunk;
   const int64_t c1 = c0 + chunk;
   const int64_t lo = c0 > 0 ? c0 : 0;
   const int64_t hi = c1 < a.N ? c1 : a.N;
+  const int64_t tend = c1 < a.N ? c1 : a.N;
 
-  for (int64_t t0 = c0; t0 < c1 && t0 < a.N; t0 += kTile) {
-    __syncthreads();
-    load_tile<D, 256>(Kp, Vp, t0, lo, hi, Kt, Vt);
-    if (tid < kTile) {
-      const int64_t s = t0 + tid;
-      lg[tid] = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)np[s]) : 0.f) : -INFINITY;
-    }
-    __syncthreads();
+  auto compute = [&](int64_t t0) {
     // per-slot ||v||^2 and per-pair ||v_m - v_{m+1}||^2: 4 threads per pair, D/4 elements each
     if (tid < 128) {
       const int pp = tid >> 2, qd = tid & 3;
@@ -338,47 +371,40 @@ __global__ __launch_bounds__(256, 2) void p2_mfma_kernel(P2Args a, int64_t base,
     __syncthreads();
 
     float gs[4][4], gx[4][2];
+    const bool plain = !HAS_N && t0 >= lo && t0 + kTile <= hi;   // every slot valid, count 1
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
-      f32x4_t st[2], rt[2];
-      st[0] = st[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f}, rt;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rt[qb][r] = vn[sb * 16 + g * 4 + r] + on[qb];
+      for (int r = 0; r < 4; ++r) rt[r] = vn[sb * 16 + g * 4 + r] + on;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        const bf16x8_t ak = as_bf16x8(*reinterpret_cast<const uint4*>(Kt + (sb * 16 + c16) * C::PITCH + kb * 32 + g * 8));
-        const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(Vt + (sb * 16 + c16) * C::PITCH + kb * 32 + g * 8));
+        const bf16x8_t ak =
+            as_bf16x8(*reinterpret_cast<const uint4*>(Kt + (sb * 16 + c16) * C::PITCH + kb * 32 + g * 8));
+        const bf16x8_t av =
+            as_bf16x8(*reinterpret_cast<const uint4*>(Vt + (sb * 16 + c16) * C::PITCH + kb * 32 + g * 8));
+        st = mfma(ak, qop[kb], st);
+        rt = mfma(av, ohi[kb], rt);
+        rt = mfma(av, olo[kb], rt);
+      }
+      float al[4], r2[4];
+      const float4 lg4 = plain ? make_float4(0.f, 0.f, 0.f, 0.f)
+                               : *reinterpret_cast<const float4*>(lgs + sb * 16 + g * 4);
+      const float lgv[4] = {lg4.x, lg4.y, lg4.z, lg4.w};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          st[qb] = mfma(ak, qop[qb][kb], st[qb]);
-          rt[qb] = mfma(av, ohi[qb][kb], rt[qb]);
-          rt[qb] = mfma(av, olo[qb][kb], rt[qb]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_fmaf(st[r], cs, lgv[r] + nb);
+        al[r] = __builtin_amdgcn_exp2f(e);
+        r2[r] = fmaxf(rt[r], 0.f);
+        gs[sb][r] = al[r] * fabsf(__builtin_fmaf(-2.f, al[r], 1.f)) * __builtin_amdgcn_sqrtf(r2[r]);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) gs[sb][r] = 0.f;
-      gx[sb][0] = gx[sb][1] = 0.f;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float al[4], r2[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_fmaf(st[qb][r], cs, lg[sb * 16 + g * 4 + r] + nb[qb]);
-          al[r] = __builtin_amdgcn_exp2f(e);
-          r2[r] = fmaxf(rt[qb][r], 0.f);
-          const float t = al[r] * fabsf(__builtin_fmaf(-2.f, al[r], 1.f));
-          gs[sb][r] = __builtin_fmaf(t, __builtin_amdgcn_sqrtf(r2[r]), gs[sb][r]);
-        }
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const float rc = fmaxf(__builtin_fmaf(2.f, r2[2 * pr] + r2[2 * pr + 1], -dv[sb * 8 + g * 2 + pr]), 0.f);
-          gx[sb][pr] = __builtin_fmaf(al[2 * pr] * al[2 * pr + 1], __builtin_amdgcn_sqrtf(rc), gx[sb][pr]);
-        }
+      for (int pr = 0; pr < 2; ++pr) {
+        const float rc = fmaxf(__builtin_fmaf(2.f, r2[2 * pr] + r2[2 * pr + 1], -dv[sb * 8 + g * 2 + pr]), 0.f);
+        gx[sb][pr] = al[2 * pr] * al[2 * pr + 1] * __builtin_amdgcn_sqrtf(rc);
       }
     }
-    // sum over the 16 queries of each lane row, then over the four waves
+    // sum over the 16 queries of each lane row (DPP), then over the waves (LDS)
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
 #pragma unroll
@@ -399,7 +425,9 @@ __global__ __launch_bounds__(256, 2) void p2_mfma_kernel(P2Args a, int64_t base,
     if (tid < kTile) {
       const int64_t s = t0 + tid;
       if (s >= lo && s < hi) {
-        const float v = red_s[0][tid] + red_s[1][tid] + red_s[2][tid] + red_s[3][tid];
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += red_s[w][tid];
         if (gridDim.y == 1) a.g_self[bh * a.N + s] = v;
         else atomicAdd(&a.g_self[bh * a.N + s], v);
       }
@@ -408,11 +436,29 @@ __global__ __launch_bounds__(256, 2) void p2_mfma_kernel(P2Args a, int64_t base,
       const int64_t m0 = t0 + 2 * pp;
       const int64_t p = (m0 - a.S) / 2;
       if (m0 >= a.S && m0 >= lo && m0 + 1 < hi && p < a.P) {
-        const float v = red_x[0][pp] + red_x[1][pp] + red_x[2][pp] + red_x[3][pp];
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += red_x[w][pp];
         if (gridDim.y == 1) a.g_cross[bh * a.P + p] = v;
         else atomicAdd(&a.g_cross[bh * a.P + p], v);
       }
     }
+  };
+  TileStage<D, kThreads> sa, sb2;
+  sa.template fetch<HAS_N>(Kp, Vp, np, c0, lo, hi);
+  if (c0 + kTile < tend) sb2.template fetch<HAS_N>(Kp, Vp, np, c0 + kTile, lo, hi);
+  for (int64_t t0 = c0; t0 < tend; t0 += 2 * kTile) {
+    __syncthreads();
+    sa.commit(Kt, Vt, lgs);
+    __syncthreads();
+    if (t0 + 2 * kTile < tend) sa.template fetch<HAS_N>(Kp, Vp, np, t0 + 2 * kTile, lo, hi);
+    compute(t0);
+    if (t0 + kTile >= tend) break;
+    __syncthreads();
+    sb2.commit(Kt, Vt, lgs);
+    __syncthreads();
+    if (t0 + 3 * kTile < tend) sb2.template fetch<HAS_N>(Kp, Vp, np, t0 + 3 * kTile, lo, hi);
+    compute(t0 + kTile);
   }
 }
 
@@ -451,9 +497,9 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
   const int nqb = (int)((p1.GW + kQB - 1) / kQB);
   const dim3 grid(p1.nsplit, nqb, (unsigned)BH);
   if (p1.n)
-    hipLaunchKernelGGL((p1_mfma_kernel<D, true>), grid, dim3(512), 0, st, p1, base, ca);
+    hipLaunchKernelGGL((p1_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p1, base, ca);
   else
-    hipLaunchKernelGGL((p1_mfma_kernel<D, false>), grid, dim3(512), 0, st, p1, base, ca);
+    hipLaunchKernelGGL((p1_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p1, base, ca);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st);
@@ -465,9 +511,9 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
     if (e != hipSuccess) return e;
   }
   if (p2.n)
-    hipLaunchKernelGGL((p2_mfma_kernel<D, true>), grid, dim3(256), 0, st, p2, base, p1.chunk);
+    hipLaunchKernelGGL((p2_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p2, base, p1.chunk);
   else
-    hipLaunchKernelGGL((p2_mfma_kernel<D, false>), grid, dim3(256), 0, st, p2, base, p1.chunk);
+    hipLaunchKernelGGL((p2_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p2, base, p1.chunk);
   return hipGetLastError();
 }
 

@@ -66,8 +66,11 @@ def run_round(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: i
     N = cap if n_slots is None else n_slots
     cache = L.cache_desc(K, n_q_heads, N)
     rnd = L.round_desc(window, n_sink, n_recent, n_merge, 1.0 / math.sqrt(D))
-    L.kvs_score(cache, K, V, n, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, bufs.cos, bufs.score_ws)
-    L.kvs_merge_weights(cache, rnd, bufs.g_self, bufs.g_cross, bufs.cos, bufs.w, bufs.selected, bufs.sel_state)
+    P = L.num_pairs(N, n_sink, n_recent)
+    # the cosine feeds only the selection: computed for partial rounds, or when flags are wanted
+    cos = bufs.cos if (0 < n_merge < P or bufs.selected is not None) else None
+    L.kvs_score(cache, K, V, n, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, cos, bufs.score_ws)
+    L.kvs_merge_weights(cache, rnd, bufs.g_self, bufs.g_cross, cos, bufs.w, bufs.selected, bufs.sel_state)
     out = L.cache_desc(bufs.K, n_q_heads, N - n_merge)
     L.kvs_merge_compact(cache, K, V, n, bufs.g_self, bufs.g_cross, rnd, bufs.sel_state, out,
                         bufs.K, bufs.V, bufs.n, bufs.src)
