@@ -27,7 +27,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;      // slots per LDS tile
-constexpr int kQB = 128;       // window queries per workgroup (4 waves x 32)
+constexpr int kQB = 128;       // window queries per workgroup
 
 template <int D>
 struct TileCfg {
@@ -62,404 +62,487 @@ __device__ __forceinline__ void split_hi_lo(const float* x, bf16x8_t& hi, bf16x8
   }
 }
 
-// Register-staged tile of K and V rows [t0, t0 + 64): each of NT threads fetches its
-// 16-byte chunks (zeros outside [lo, hi)) so the loads stay in flight while the previous
-// tile is computed, then commits them to LDS.
-template <int D, int NT>
-struct TileStage {
-  using C = TileCfg<D>;
-  static constexpr int NPT = kTile * C::CPR / NT;
-  uint4 k[NPT], v[NPT];
-  float lg;
+// ------------------------------------------------------------------ tiling ----
+// A workgroup is two tile groups of four waves (512 threads).  Group g takes the tiles
+// c0 + (2 i + g) * 64 of the workgroup's slot chunk, so each SIMD runs two waves while the
+// workgroup still produces one partial record per query.  A wave owns 32 window queries
+// (32x32x16 MFMA), so the four waves of a group cover 128 queries.  Each group
+// double-buffers its tiles in LDS: tile i + 1 is committed from registers and tile i + 2
+// is fetched while tile i is computed, with one barrier per step.
+constexpr int kGroupWaves = 4;
+constexpr int kGroups = 2;
+constexpr int kGT = 64 * kGroupWaves;              // threads per group
+constexpr int kThreads = kGT * kGroups;            // 512
 
-  template <bool HAS_N>
-  __device__ __forceinline__ void fetch(const bf16* Kp, const bf16* Vp, const int32_t* np, int64_t t0, int64_t lo,
-                                        int64_t hi) {
-    const int tid = threadIdx.x;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+__device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct Cfg32 {
+  static constexpr int KS = D / 16;     // 16-wide k steps over the head dim
+  static constexpr int DB = D / 32;     // 32-wide blocks of the head dim
+  static constexpr int PITCH = D + 16;  // bf16 per LDS row: rows 8 banks apart
+  static constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static constexpr int PPP = kGT / CPR; // pairs per commit pass
+  static constexpr int NPASS = (kTile / 2) / PPP;
+  static constexpr int TILE = kTile * PITCH;   // bf16 per K (or V) tile
+};
+
+// Per-thread staging of one tile for its group: thread gt holds 16-byte chunk gt % CPR of
+// the K and V rows of pair p = pass * PPP + gt / CPR (rows 2p and 2p + 1).
+template <int D>
+struct Stage {
+  using C = Cfg32<D>;
+  uint4 k[C::NPASS][2], v[C::NPASS][2];
+  float lg[2];   // log2 n of rows 2 * (gt % 32) and + 1 ... (only lanes gt < 32)
+
+  __device__ __forceinline__ void fetch(const bf16* Kp, const bf16* Vp, int64_t t0, int64_t lo, int64_t hi,
+                                        int gt) {
+    const int ch = gt % C::CPR;
 #pragma unroll
-    for (int it = 0; it < NPT; ++it) {
-      const int idx = it * NT + tid;
-      const int row = idx / C::CPR, ch = idx % C::CPR;
-      const int64_t s = t0 + row;
-      if (s >= lo && s < hi) {
-        k[it] = load16(Kp + s * D + ch * 8);
-        v[it] = load16(Vp + s * D + ch * 8);
-      } else {
-        k[it] = v[it] = make_uint4(0, 0, 0, 0);
+    for (int ps = 0; ps < C::NPASS; ++ps)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = 2 * (ps * C::PPP + gt / C::CPR) + r;
+        const int64_t s = t0 + row;
+        if (s >= lo && s < hi) {
+          k[ps][r] = load16(Kp + s * D + ch * 8);
+          v[ps][r] = load16(Vp + s * D + ch * 8);
+        } else {
+          k[ps][r] = v[ps][r] = make_uint4(0, 0, 0, 0);
+        }
       }
-    }
-    if (tid < kTile) {
-      const int64_t s = t0 + tid;
-      lg = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)np[s]) : 0.f) : -INFINITY;
-    }
-  }
-
-  __device__ __forceinline__ void commit(bf16* Kt, bf16* Vt, float* lgs) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int it = 0; it < NPT; ++it) {
-      const int idx = it * NT + tid;
-      const int row = idx / C::CPR, ch = idx % C::CPR;
-      *reinterpret_cast<uint4*>(Kt + row * C::PITCH + ch * 8) = k[it];
-      *reinterpret_cast<uint4*>(Vt + row * C::PITCH + ch * 8) = v[it];
-    }
-    if (tid < kTile) lgs[tid] = lg;
   }
 };
 
-// Q (or any fp32-free bf16 row block) as an MFMA operand: lane l holds
-// Q[q = l%16][d = 32 kb + 8 (l/16) .. +7] of the 16 rows starting at query q.
 template <int D>
-__device__ __forceinline__ void load_q(const bf16* Qp, int64_t GW, int64_t q, bf16x8_t (&qop)[TileCfg<D>::KB]) {
-  const int g = (threadIdx.x & 63) >> 4;
+__device__ __forceinline__ void commit_rows(const Stage<D>& st, bf16* Kt, bf16* Vt, int gt) {
+  using C = Cfg32<D>;
+  const int ch = gt % C::CPR;
 #pragma unroll
-  for (int kb = 0; kb < TileCfg<D>::KB; ++kb) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (q < GW) u = load16(Qp + q * D + kb * 32 + g * 8);
-    qop[kb] = as_bf16x8(u);
+  for (int ps = 0; ps < C::NPASS; ++ps)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 2 * (ps * C::PPP + gt / C::CPR) + r;
+      *reinterpret_cast<uint4*>(Kt + row * C::PITCH + ch * 8) = st.k[ps][r];
+      *reinterpret_cast<uint4*>(Vt + row * C::PITCH + ch * 8) = st.v[ps][r];
+    }
+}
+
+// log2 n (0 when there are no counts) of every slot of the tile, -inf outside [lo, hi).
+template <bool HAS_N>
+__device__ __forceinline__ void tile_bias(const int32_t* np, int64_t t0, int64_t lo, int64_t hi, int gt, float* lgs) {
+  if (gt < kTile) {
+    const int64_t s = t0 + gt;
+    lgs[gt] = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)np[s]) : 0.f) : -INFINITY;
   }
 }
 
-constexpr int kThreads = 512;   // 8 waves x 16 window queries
+// Q rows as a 32x32x16 operand: lane l holds row[q][16 ks + 8 (l / 32) .. +7] of query q.
+template <int D>
+__device__ __forceinline__ void load_rows32(const bf16* Qp, int64_t GW, int64_t q, bf16x8_t (&op)[Cfg32<D>::KS]) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < Cfg32<D>::KS; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (q < GW) u = load16(Qp + q * D + ks * 16 + h * 8);
+    op[ks] = as_bf16x8(u);
+  }
+}
 
 // ------------------------------------------------------------------------- pass 1 --
-// grid: x = slot chunk, y = query block (128), z = (b, kv-head); eight waves of 16 queries
-// share each LDS tile.  Partial records as the VALU pass 1: {m (log2 units), l, -, -, o[D]}
-// per (bh, query, chunk).
+// grid: x = slot chunk, y = query block (128), z = (b, kv-head).  Partial records as the
+// VALU pass 1: {m (log2 units), l, -, -, o[D]} per (bh, query, chunk).
 template <int D, bool HAS_N>
 __global__ __launch_bounds__(kThreads, 1) void p1_mfma_kernel(P1Args a, int64_t base, CosArgs ca) {
-  using C = TileCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Kt[kTile * C::PITCH];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[kTile * C::PITCH];
-  __shared__ __attribute__((aligned(16))) float lgs[kTile];
+  using C = Cfg32<D>;
+  __shared__ __attribute__((aligned(16))) bf16 smem[kGroups * 2 * 2 * C::TILE];
+  __shared__ __attribute__((aligned(16))) float lgs[kGroups * 2 * kTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int grp = wv / kGroupWaves, gw = wv % kGroupWaves, gt = tid % kGT;
+  const int c32 = lane & 31, h = lane >> 5, G16 = lane >> 4, t16 = lane & 15;
   const int64_t bh = blockIdx.z;
-  const int64_t b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const bf16* Kp = static_cast<const bf16*>(a.K) + b * a.sb + h * a.sh;
-  const bf16* Vp = static_cast<const bf16*>(a.V) + b * a.sb + h * a.sh;
-  const int32_t* np = HAS_N ? a.n + (b * a.sb + h * a.sh) / D : nullptr;
-  const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + h * a.G) * (int64_t)a.W) * D;
+  const int64_t b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const bf16* Kp = static_cast<const bf16*>(a.K) + b * a.sb + hk * a.sh;
+  const bf16* Vp = static_cast<const bf16*>(a.V) + b * a.sb + hk * a.sh;
+  const int32_t* np = HAS_N ? a.n + (b * a.sb + hk * a.sh) / D : nullptr;
+  const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + hk * a.G) * (int64_t)a.W) * D;
 
-  const int64_t q0 = (int64_t)blockIdx.y * kQB + wv * 16;
-  bf16x8_t qop[C::KB];
-  load_q<D>(Qp, a.GW, q0 + c16, qop);
+  const int64_t q = (int64_t)blockIdx.y * kQB + gw * 32 + c32;
+  bf16x8_t qop[C::KS];
+  load_rows32<D>(Qp, a.GW, q, qop);
 
   const float cs = a.scale * kLog2e;
   float m = kNoMax, lsum = 0.f;
-  f32x4_t acc[C::DB];
+  f32x16_t acc[C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
   const int64_t c0 = base + (int64_t)blockIdx.x * a.chunk;
   const int64_t c1 = c0 + a.chunk;
   const int64_t lo = c0 > 0 ? c0 : 0;
   const int64_t hi = c1 < a.N ? c1 : a.N;
-  const int64_t tend = c1 < a.N ? c1 : a.N;
+  const int64_t tend = hi;
+  const int ntiles = (int)((tend - c0 + kTile - 1) / kTile);
+  const int iters = (ntiles + 1) / 2;
   const bool do_cos = ca.cos != nullptr && blockIdx.y == 0;
+  auto tile_of = [&](int i) { return c0 + (int64_t)(2 * i + grp) * kTile; };
+  auto Kt = [&](int s) { return smem + ((grp * 2 + s) * 2) * C::TILE; };
+  auto Vt = [&](int s) { return smem + ((grp * 2 + s) * 2 + 1) * C::TILE; };
+  auto Lg = [&](int s) { return lgs + (grp * 2 + s) * kTile; };
 
-  // two register stages keep two tiles (64 KB) of loads in flight per workgroup
-  auto compute = [&](int64_t t0) {
-
-    // adjacent-key cosine of the tile's candidate pairs (row layout: LPR lanes x 8 elements)
+  // commit one staged tile; the cosine of its candidate pairs comes from the staged rows
+  auto commit = [&](const Stage<D>& st, int s, int64_t t0) {
+    commit_rows<D>(st, Kt(s), Vt(s), gt);
+    tile_bias<HAS_N>(np, t0, lo, hi, gt, Lg(s));
     if (do_cos) {
-      constexpr int LPR = D / 8;
-      constexpr int GPB = kThreads / LPR;
-      const int grp = tid / LPR, j = tid % LPR;
 #pragma unroll
-      for (int pp0 = 0; pp0 < kTile / 2; pp0 += GPB) {
-        const int pp = (pp0 + grp) & (kTile / 2 - 1);   // surplus groups repeat a pair and write nothing
-        const int64_t m0 = t0 + 2 * pp;
+      for (int ps = 0; ps < C::NPASS; ++ps) {
         float k0[8], k1[8];
-        unpack<bf16>(*reinterpret_cast<const uint4*>(Kt + (2 * pp) * C::PITCH + j * 8), k0);
-        unpack<bf16>(*reinterpret_cast<const uint4*>(Kt + (2 * pp + 1) * C::PITCH + j * 8), k1);
-        const float cv = pair_cos<8, LPR>(k0, k1);
+        unpack<bf16>(st.k[ps][0], k0);
+        unpack<bf16>(st.k[ps][1], k1);
+        const float cv = pair_cos<8, C::CPR>(k0, k1);
+        const int64_t m0 = t0 + 2 * (ps * C::PPP + gt / C::CPR);
         const int64_t p = (m0 - ca.S) / 2;
-        if (j == 0 && pp0 + grp < kTile / 2 && m0 >= ca.S && p < ca.P && m0 >= lo && m0 + 1 < hi)
-          ca.cos[bh * ca.P + p] = cv;
-      }
-    }
-
-    // S^T = K . Q^T over the tile (4 slot blocks); online softmax for the lane's query
-    f32x4_t st[4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      st[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const bf16x8_t ak =
-            as_bf16x8(*reinterpret_cast<const uint4*>(Kt + (sb * 16 + c16) * C::PITCH + kb * 32 + g * 8));
-        st[sb] = mfma(ak, qop[kb], st[sb]);
-      }
-    }
-    float e[4][4];
-    float mx = kNoMax;
-    const bool plain = !HAS_N && t0 >= lo && t0 + kTile <= hi;   // every slot valid, count 1
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      const float4 lg4 = plain ? make_float4(0.f, 0.f, 0.f, 0.f)
-                               : *reinterpret_cast<const float4*>(lgs + sb * 16 + g * 4);
-      const float lgv[4] = {lg4.x, lg4.y, lg4.z, lg4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        e[sb][r] = __builtin_fmaf(st[sb][r], cs, lgv[r]);
-        mx = fmaxf(mx, e[sb][r]);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (mx > m) {   // rescale only when the running max grows (finite sentinel: no NaN paths)
-      const float corr = __builtin_amdgcn_exp2f(m - mx);
-      lsum *= corr;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db] *= corr;
-      m = mx;
-    }
-    float p[4][4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[sb][r] = __builtin_amdgcn_exp2f(e[sb][r] - m);
-        lsum += p[sb][r];
-      }
-    // O^T += V^T . P^T, two 32-slot halves; k index j <-> slot 32 hf + 16 (j / 4) + 4 g + j % 4
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      float pv[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[r] = p[2 * hf][r];
-        pv[4 + r] = p[2 * hf + 1][r];
-      }
-      bf16x8_t phi, plo;
-      split_hi_lo(pv, phi, plo);
-      // transposed read: source lane i = lane % 16 points at row 32 hf + 4 g + i / 4 (+16),
-      // columns 16 db + 4 (i % 4); lane t receives column 16 db + t of four consecutive rows
-      const int srow = 32 * hf + 4 * g + (c16 >> 2);
-      const int scol = 4 * (c16 & 3);
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-        const bf16x4_t v0 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vt + srow * C::PITCH + db * 16 + scol));
-        const bf16x4_t v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vt + (srow + 16) * C::PITCH + db * 16 + scol));
-        const bf16x8_t vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[db] = mfma(vop, phi, acc[db]);
-        acc[db] = mfma(vop, plo, acc[db]);
+        if (gt % C::CPR == 0 && m0 >= ca.S && p < ca.P && m0 >= lo && m0 + 1 < hi) ca.cos[bh * ca.P + p] = cv;
       }
     }
   };
-  TileStage<D, kThreads> sa, sb2;
-  sa.template fetch<HAS_N>(Kp, Vp, np, c0, lo, hi);
-  if (c0 + kTile < tend) sb2.template fetch<HAS_N>(Kp, Vp, np, c0 + kTile, lo, hi);
-  for (int64_t t0 = c0; t0 < tend; t0 += 2 * kTile) {
+
+  auto compute = [&](int s, int64_t t0) {
+    const bf16* K_ = Kt(s);
+    const bf16* V_ = Vt(s);
+    const float* L_ = Lg(s);
+    const bool plain = !HAS_N && t0 >= lo && t0 + kTile <= hi;   // every slot valid, count 1
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      // S^T = K . Q^T for 32 slots: lane holds slots 32 sb + 8 (i / 4) + 4 h + i % 4 of query c32
+      f32x16_t st;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8_t ak = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + (sb * 32 + c32) * C::PITCH + ks * 16 + h * 8));
+        st = mfma32(ak, qop[ks], st);
+      }
+      float e[16];
+      float mx = kNoMax;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const float4 l4 = plain ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                : *reinterpret_cast<const float4*>(L_ + sb * 32 + k4 * 8 + h * 4);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[k4 * 4 + r] = __builtin_fmaf(st[k4 * 4 + r], cs, lv[r]);
+          mx = fmaxf(mx, e[k4 * 4 + r]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (mx > m) {   // rescale only when the running max grows (finite sentinel: no NaN paths)
+        const float corr = __builtin_amdgcn_exp2f(m - mx);
+        lsum *= corr;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] *= corr;
+        m = mx;
+      }
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(e[i] - m);
+        lsum += p[i];
+      }
+      // O^T += V^T . P^T in two 16-slot k steps; k index (h, j) <-> slot
+      // 32 sb + 16 ks + 8 (j / 4) + 4 h + j % 4, i.e. the lane's own p[8 ks + j]
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8_t phi, plo;
+        split_hi_lo(p + 8 * ks, phi, plo);
+        // transposed read: source lane i = lane % 16 points at row r0 + i / 4 (and + 8),
+        // columns 32 db + 16 (G16 % 2) + 4 (i % 4); lane t receives column + t of 4 rows
+        const int r0 = sb * 32 + ks * 16 + 4 * h + (t16 >> 2);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+          const int col = db * 32 + 16 * (G16 & 1) + 4 * (t16 & 3);
+          const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(V_ + r0 * C::PITCH + col));
+          const bf16x4_t v1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(V_ + (r0 + 8) * C::PITCH + col));
+          const bf16x8_t vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[db] = mfma32(vop, phi, acc[db]);
+          acc[db] = mfma32(vop, plo, acc[db]);
+        }
+      }
+    }
+  };
+
+  Stage<D> stg;
+  if (tile_of(0) < tend) {
+    stg.fetch(Kp, Vp, tile_of(0), lo, hi, gt);
+    commit(stg, 0, tile_of(0));
+  }
+  if (tile_of(1) < tend) stg.fetch(Kp, Vp, tile_of(1), lo, hi, gt);
+  for (int i = 0; i < iters; ++i) {
     __syncthreads();
-    sa.commit(Kt, Vt, lgs);
-    __syncthreads();
-    if (t0 + 2 * kTile < tend) sa.template fetch<HAS_N>(Kp, Vp, np, t0 + 2 * kTile, lo, hi);
-    compute(t0);
-    if (t0 + kTile >= tend) break;
-    __syncthreads();
-    sb2.commit(Kt, Vt, lgs);
-    __syncthreads();
-    if (t0 + 3 * kTile < tend) sb2.template fetch<HAS_N>(Kp, Vp, np, t0 + 3 * kTile, lo, hi);
-    compute(t0 + kTile);
+    if (tile_of(i + 1) < tend) commit(stg, (i + 1) & 1, tile_of(i + 1));
+    if (tile_of(i + 2) < tend) stg.fetch(Kp, Vp, tile_of(i + 2), lo, hi, gt);
+    if (tile_of(i) < tend) compute(i & 1, tile_of(i));
   }
 
-  // per-query partial record: the four lane groups hold disjoint slots of the same query
-  float l = lsum;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  const int64_t q = q0 + c16;
-  if (q < a.GW) {
+  // merge the two groups' running states through LDS, then write the partial record
+  float l = lsum + __shfl_xor(lsum, 32, 64);
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(smem);            // [128 queries][D]
+  float* xm = xo + kQB * D;                              // [128] max, [128] sum
+  const int qi = gw * 32 + c32;
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xo[qi * D + db * 32 + (i >> 2) * 8 + h * 4 + (i & 3)] = acc[db][i];
+    if (h == 0) {
+      xm[qi] = m;
+      xm[kQB + qi] = l;
+    }
+  }
+  __syncthreads();
+  if (grp == 0 && q < a.GW) {
+    const float m1 = xm[qi], l1 = xm[kQB + qi];
+    const float M = fmaxf(m, m1);
+    const float f0 = __builtin_amdgcn_exp2f(m - M), f1 = __builtin_amdgcn_exp2f(m1 - M);
     float* rec = a.part + ((bh * a.GW + q) * a.nsplit + blockIdx.x) * (int64_t)(D + 4);
-    if (g == 0) {
-      rec[0] = m;
-      rec[1] = l;
+    if (h == 0) {
+      rec[0] = M;
+      rec[1] = l * f0 + l1 * f1;
     }
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rec[4 + db * 16 + g * 4 + r] = acc[db][r];
+      for (int i = 0; i < 16; ++i) {
+        const int d = db * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+        rec[4 + d] = acc[db][i] * f0 + xo[qi * D + d] * f1;
+      }
   }
 }
 
 // ------------------------------------------------------------------------- pass 2 --
-// grid: x = slot chunk, y = query block (128), z = (b, kv-head); eight waves of 16 queries.
-// With more than one query block the per-slot sums are accumulated with atomics (not the
-// case for <= 128 window queries per kv head).
+// grid: x = slot chunk, y = query block (128), z = (b, kv-head).  Slot-per-lane layout:
+// S[q, slot] = Q . K^T and R[q, slot] = (-2 O) . V^T + ||v||^2 + ||o||^2 on 32x32x16 MFMA,
+// lane l holding slot 32 sb + l % 32 for 16 of the wave's 32 queries, so the sum over
+// queries stays in registers; the pair partner slot is one DPP xor-1 away.  With more
+// than one query block the per-slot sums are accumulated with atomics (not the case for
+// <= 128 window queries per kv head).
 template <int D, bool HAS_N>
 __global__ __launch_bounds__(kThreads, 1) void p2_mfma_kernel(P2Args a, int64_t base, int64_t chunk) {
-  using C = TileCfg<D>;
-  constexpr int NW = kThreads / 64;
-  __shared__ __attribute__((aligned(16))) bf16 Kt[kTile * C::PITCH];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[kTile * C::PITCH];
-  __shared__ __attribute__((aligned(16))) float lgs[kTile];
-  __shared__ float vn[kTile];
-  __shared__ float dv[kTile / 2];
-  __shared__ float red_s[NW][kTile];
-  __shared__ float red_x[NW][kTile / 2];
+  using C = Cfg32<D>;
+  __shared__ __attribute__((aligned(16))) bf16 smem[kGroups * 2 * 2 * C::TILE];
+  __shared__ __attribute__((aligned(16))) float lgs[kGroups * 2 * kTile];
+  __shared__ float vns[kGroups * 2 * kTile];
+  __shared__ float dvs[kGroups * 2 * (kTile / 2)];
+  __shared__ float red_s[kGroups * 2 * kGroupWaves * kTile];
+  __shared__ float red_x[kGroups * 2 * kGroupWaves * (kTile / 2)];
+  __shared__ __attribute__((aligned(16))) float qon[kQB];   // ||o_q||^2 of the block's queries
+  __shared__ __attribute__((aligned(16))) float qnb[kQB];   // -lse_q in log2 units (-inf: padding)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int grp = wv / kGroupWaves, gw = wv % kGroupWaves, gt = tid % kGT;
+  const int c32 = lane & 31, h = lane >> 5;
+  const bool odd = (c32 & 1) != 0;
   const int64_t bh = blockIdx.z;
-  const int64_t b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const bf16* Kp = static_cast<const bf16*>(a.K) + b * a.sb + h * a.sh;
-  const bf16* Vp = static_cast<const bf16*>(a.V) + b * a.sb + h * a.sh;
-  const int32_t* np = HAS_N ? a.n + (b * a.sb + h * a.sh) / D : nullptr;
-  const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + h * a.G) * (int64_t)a.W) * D;
+  const int64_t b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const bf16* Kp = static_cast<const bf16*>(a.K) + b * a.sb + hk * a.sh;
+  const bf16* Vp = static_cast<const bf16*>(a.V) + b * a.sb + hk * a.sh;
+  const int32_t* np = HAS_N ? a.n + (b * a.sb + hk * a.sh) / D : nullptr;
+  const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + hk * a.G) * (int64_t)a.W) * D;
   const float* Op = a.O + bh * a.GW * (int64_t)D;
   const float* Lp = a.lse + bh * a.GW;
 
-  // the wave's 16 queries: Q and -2 O (hi + lo) as MFMA operands, ||o||^2, -lse in log2 units
-  const int64_t q = (int64_t)blockIdx.y * kQB + wv * 16 + c16;
-  bf16x8_t qop[C::KB], ohi[C::KB], olo[C::KB];
-  load_q<D>(Qp, a.GW, q, qop);
-  float on = 0.f;
+  // the wave's 32 queries as the A operand: Q and -2 O (hi + lo), row q0 + l % 32
+  const int64_t q0 = (int64_t)blockIdx.y * kQB + gw * 32;
+  const int64_t qa = q0 + c32;
+  bf16x8_t qop[C::KS], ohi[C::KS], olo[C::KS];
+  load_rows32<D>(Qp, a.GW, qa, qop);
+  float on_a = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) {
+  for (int ks = 0; ks < C::KS; ++ks) {
     float o8[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float ov = q < a.GW ? Op[q * D + kb * 32 + g * 8 + j] : 0.f;
-      on = __builtin_fmaf(ov, ov, on);
+      const float ov = qa < a.GW ? Op[qa * D + ks * 16 + h * 8 + j] : 0.f;
+      on_a = __builtin_fmaf(ov, ov, on_a);
       o8[j] = -2.f * ov;
     }
-    split_hi_lo(o8, ohi[kb], olo[kb]);
+    split_hi_lo(o8, ohi[ks], olo[ks]);
   }
-  on += __shfl_xor(on, 16, 64);
-  on += __shfl_xor(on, 32, 64);
-  const float nb = q < a.GW ? -Lp[q] * kLog2e : -INFINITY;   // padded queries get alpha = 0
+  on_a += __shfl_xor(on_a, 32, 64);
+  if (grp == 0 && h == 0) {
+    qon[gw * 32 + c32] = on_a;
+    qnb[gw * 32 + c32] = qa < a.GW ? -Lp[qa] * kLog2e : -INFINITY;   // padded queries: alpha = 0
+  }
+  // result rows of this lane are queries q0 + 8 (i / 4) + 4 h + i % 4; their constants are
+  // read from LDS as broadcast float4s (published before the first tile barrier)
+  const float* on_row = qon + gw * 32 + 4 * h;
+  const float* nb_row = qnb + gw * 32 + 4 * h;
   const float cs = a.scale * kLog2e;
 
   const int64_t c0 = base + (int64_t)blockIdx.x * chunk;
   const int64_t c1 = c0 + chunk;
   const int64_t lo = c0 > 0 ? c0 : 0;
   const int64_t hi = c1 < a.N ? c1 : a.N;
-  const int64_t tend = c1 < a.N ? c1 : a.N;
+  const int64_t tend = hi;
+  const int ntiles = (int)((tend - c0 + kTile - 1) / kTile);
+  const int iters = (ntiles + 1) / 2;
+  auto tile_of = [&](int i) { return c0 + (int64_t)(2 * i + grp) * kTile; };
+  auto Kt = [&](int s) { return smem + ((grp * 2 + s) * 2) * C::TILE; };
+  auto Vt = [&](int s) { return smem + ((grp * 2 + s) * 2 + 1) * C::TILE; };
+  auto Lg = [&](int s) { return lgs + (grp * 2 + s) * kTile; };
+  auto Vn = [&](int s) { return vns + (grp * 2 + s) * kTile; };
+  auto Dv = [&](int s) { return dvs + (grp * 2 + s) * (kTile / 2); };
+  auto Rs = [&](int par, int w) { return red_s + ((grp * 2 + par) * kGroupWaves + w) * kTile; };
+  auto Rx = [&](int par, int w) { return red_x + ((grp * 2 + par) * kGroupWaves + w) * (kTile / 2); };
 
-  auto compute = [&](int64_t t0) {
-    // per-slot ||v||^2 and per-pair ||v_m - v_{m+1}||^2: 4 threads per pair, D/4 elements each
-    if (tid < 128) {
-      const int pp = tid >> 2, qd = tid & 3;
+  // commit a staged tile with ||v||^2 per slot and ||v_m - v_{m+1}||^2 per pair
+  auto commit = [&](const Stage<D>& st, int s, int64_t t0) {
+    commit_rows<D>(st, Kt(s), Vt(s), gt);
+    tile_bias<HAS_N>(np, t0, lo, hi, gt, Lg(s));
+#pragma unroll
+    for (int ps = 0; ps < C::NPASS; ++ps) {
+      float x0[8], x1[8];
+      unpack<bf16>(st.v[ps][0], x0);
+      unpack<bf16>(st.v[ps][1], x1);
       float s0 = 0.f, s1 = 0.f, sd = 0.f;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        float x0[8], x1[8];
-        unpack<bf16>(*reinterpret_cast<const uint4*>(Vt + (2 * pp) * C::PITCH + qd * (D / 4) + c * 8), x0);
-        unpack<bf16>(*reinterpret_cast<const uint4*>(Vt + (2 * pp + 1) * C::PITCH + qd * (D / 4) + c * 8), x1);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          s0 = __builtin_fmaf(x0[j], x0[j], s0);
-          s1 = __builtin_fmaf(x1[j], x1[j], s1);
-          const float d = x0[j] - x1[j];
-          sd = __builtin_fmaf(d, d, sd);
-        }
+      for (int j = 0; j < 8; ++j) {
+        s0 = __builtin_fmaf(x0[j], x0[j], s0);
+        s1 = __builtin_fmaf(x1[j], x1[j], s1);
+        const float d = x0[j] - x1[j];
+        sd = __builtin_fmaf(d, d, sd);
       }
-      s0 = group_sum<4>(s0);
-      s1 = group_sum<4>(s1);
-      sd = group_sum<4>(sd);
-      if (qd == 0) {
-        vn[2 * pp] = s0;
-        vn[2 * pp + 1] = s1;
-        dv[pp] = sd;
+      s0 = group_sum<C::CPR>(s0);
+      s1 = group_sum<C::CPR>(s1);
+      sd = group_sum<C::CPR>(sd);
+      if (gt % C::CPR == 0) {
+        const int pp = ps * C::PPP + gt / C::CPR;
+        Vn(s)[2 * pp] = s0;
+        Vn(s)[2 * pp + 1] = s1;
+        Dv(s)[pp] = sd;
       }
     }
-    __syncthreads();
+  };
 
-    float gs[4][4], gx[4][2];
-    const bool plain = !HAS_N && t0 >= lo && t0 + kTile <= hi;   // every slot valid, count 1
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f}, rt;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rt[r] = vn[sb * 16 + g * 4 + r] + on;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const bf16x8_t ak =
-            as_bf16x8(*reinterpret_cast<const uint4*>(Kt + (sb * 16 + c16) * C::PITCH + kb * 32 + g * 8));
-        const bf16x8_t av =
-            as_bf16x8(*reinterpret_cast<const uint4*>(Vt + (sb * 16 + c16) * C::PITCH + kb * 32 + g * 8));
-        st = mfma(ak, qop[kb], st);
-        rt = mfma(av, ohi[kb], rt);
-        rt = mfma(av, olo[kb], rt);
-      }
-      float al[4], r2[4];
-      const float4 lg4 = plain ? make_float4(0.f, 0.f, 0.f, 0.f)
-                               : *reinterpret_cast<const float4*>(lgs + sb * 16 + g * 4);
-      const float lgv[4] = {lg4.x, lg4.y, lg4.z, lg4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = __builtin_fmaf(st[r], cs, lgv[r] + nb);
-        al[r] = __builtin_amdgcn_exp2f(e);
-        r2[r] = fmaxf(rt[r], 0.f);
-        gs[sb][r] = al[r] * fabsf(__builtin_fmaf(-2.f, al[r], 1.f)) * __builtin_amdgcn_sqrtf(r2[r]);
-      }
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const float rc = fmaxf(__builtin_fmaf(2.f, r2[2 * pr] + r2[2 * pr + 1], -dv[sb * 8 + g * 2 + pr]), 0.f);
-        gx[sb][pr] = al[2 * pr] * al[2 * pr + 1] * __builtin_amdgcn_sqrtf(rc);
-      }
-    }
-    // sum over the 16 queries of each lane row (DPP), then over the waves (LDS)
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) gs[sb][r] = group_sum<16>(gs[sb][r]);
-      gx[sb][0] = group_sum<16>(gx[sb][0]);
-      gx[sb][1] = group_sum<16>(gx[sb][1]);
-    }
-    if (c16 == 0) {
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red_s[wv][sb * 16 + g * 4 + r] = gs[sb][r];
-        red_x[wv][sb * 8 + g * 2] = gx[sb][0];
-        red_x[wv][sb * 8 + g * 2 + 1] = gx[sb][1];
-      }
-    }
-    __syncthreads();
-    if (tid < kTile) {
-      const int64_t s = t0 + tid;
+  // write the wave-summed g_self / g_cross of a finished tile (parity par)
+  auto flush = [&](int par, int64_t t0) {
+    if (gt < kTile) {
+      const int64_t s = t0 + gt;
       if (s >= lo && s < hi) {
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) v += red_s[w][tid];
+        for (int w = 0; w < kGroupWaves; ++w) v += Rs(par, w)[gt];
         if (gridDim.y == 1) a.g_self[bh * a.N + s] = v;
         else atomicAdd(&a.g_self[bh * a.N + s], v);
       }
-    } else if (tid < kTile + kTile / 2) {
-      const int pp = tid - kTile;
+    } else if (gt < kTile + kTile / 2) {
+      const int pp = gt - kTile;
       const int64_t m0 = t0 + 2 * pp;
       const int64_t p = (m0 - a.S) / 2;
       if (m0 >= a.S && m0 >= lo && m0 + 1 < hi && p < a.P) {
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) v += red_x[w][pp];
+        for (int w = 0; w < kGroupWaves; ++w) v += Rx(par, w)[pp];
         if (gridDim.y == 1) a.g_cross[bh * a.P + p] = v;
         else atomicAdd(&a.g_cross[bh * a.P + p], v);
       }
     }
   };
-  TileStage<D, kThreads> sa, sb2;
-  sa.template fetch<HAS_N>(Kp, Vp, np, c0, lo, hi);
-  if (c0 + kTile < tend) sb2.template fetch<HAS_N>(Kp, Vp, np, c0 + kTile, lo, hi);
-  for (int64_t t0 = c0; t0 < tend; t0 += 2 * kTile) {
-    __syncthreads();
-    sa.commit(Kt, Vt, lgs);
-    __syncthreads();
-    if (t0 + 2 * kTile < tend) sa.template fetch<HAS_N>(Kp, Vp, np, t0 + 2 * kTile, lo, hi);
-    compute(t0);
-    if (t0 + kTile >= tend) break;
-    __syncthreads();
-    sb2.commit(Kt, Vt, lgs);
-    __syncthreads();
-    if (t0 + 3 * kTile < tend) sb2.template fetch<HAS_N>(Kp, Vp, np, t0 + 3 * kTile, lo, hi);
-    compute(t0 + kTile);
+
+  auto compute = [&](int s, int par, int64_t t0) {
+    const bf16* K_ = Kt(s);
+    const bf16* V_ = Vt(s);
+    const bool plain = !HAS_N && t0 >= lo && t0 + kTile <= hi;
+#pragma unroll 1
+    for (int sb = 0; sb < 2; ++sb) {
+      const int slot = sb * 32 + c32;
+      const float vn = Vn(s)[slot];
+      const float dvp = Dv(s)[slot >> 1];
+      const float lgv = plain ? 0.f : Lg(s)[slot];
+      f32x16_t st, rt;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const float4 o4 = *reinterpret_cast<const float4*>(on_row + 8 * k4);
+        rt[4 * k4] = vn + o4.x;
+        rt[4 * k4 + 1] = vn + o4.y;
+        rt[4 * k4 + 2] = vn + o4.z;
+        rt[4 * k4 + 3] = vn + o4.w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[4 * k4 + r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8_t bk = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + slot * C::PITCH + ks * 16 + h * 8));
+        const bf16x8_t bv = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + slot * C::PITCH + ks * 16 + h * 8));
+        st = mfma32(qop[ks], bk, st);
+        rt = mfma32(ohi[ks], bv, rt);
+        rt = mfma32(olo[ks], bv, rt);
+      }
+      float al[16];
+      float gs = 0.f;
+      float nb[16];
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const float4 n4 = *reinterpret_cast<const float4*>(nb_row + 8 * k4);
+        nb[4 * k4] = n4.x;
+        nb[4 * k4 + 1] = n4.y;
+        nb[4 * k4 + 2] = n4.z;
+        nb[4 * k4 + 3] = n4.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        al[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], cs, lgv + nb[i]));
+        const float t = al[i] * fabsf(__builtin_fmaf(-2.f, al[i], 1.f));
+        gs = __builtin_fmaf(t, __builtin_amdgcn_sqrtf(fabsf(rt[i])), gs);
+      }
+      // pairs (even slot, odd slot) of the same query: the even lane takes queries i < 8,
+      // the odd lane queries i >= 8, each receiving the partner's alpha and r^2 by DPP
+      float gx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float sa = odd ? al[i] : al[i + 8], sr = odd ? rt[i] : rt[i + 8];
+        const float oa = odd ? al[i + 8] : al[i], orr = odd ? rt[i + 8] : rt[i];
+        const float pa = dpp<kDppXor1>(sa), pr = dpp<kDppXor1>(sr);
+        const float rc = __builtin_fmaf(2.f, orr + pr, -dvp);
+        gx = __builtin_fmaf(oa * pa, __builtin_amdgcn_sqrtf(fabsf(rc)), gx);
+      }
+      gx += dpp<kDppXor1>(gx);
+      gs += __shfl_xor(gs, 32, 64);
+      gx += __shfl_xor(gx, 32, 64);
+      if (h == 0) {
+        Rs(par, gw)[slot] = gs;
+        if (!odd) Rx(par, gw)[slot >> 1] = gx;
+      }
+    }
+  };
+
+  Stage<D> stg;
+  if (tile_of(0) < tend) {
+    stg.fetch(Kp, Vp, tile_of(0), lo, hi, gt);
+    commit(stg, 0, tile_of(0));
   }
+  if (tile_of(1) < tend) stg.fetch(Kp, Vp, tile_of(1), lo, hi, gt);
+  for (int i = 0; i < iters; ++i) {
+    __syncthreads();
+    if (i > 0 && tile_of(i - 1) < tend) flush((i - 1) & 1, tile_of(i - 1));
+    if (tile_of(i + 1) < tend) commit(stg, (i + 1) & 1, tile_of(i + 1));
+    if (tile_of(i + 2) < tend) stg.fetch(Kp, Vp, tile_of(i + 2), lo, hi, gt);
+    if (tile_of(i) < tend) compute(i & 1, i & 1, tile_of(i));
+  }
+  __syncthreads();
+  if (iters > 0 && tile_of(iters - 1) < tend) flush((iters - 1) & 1, tile_of(iters - 1));
 }
 
 // -------------------------------------------------------------------- dispatch --
