@@ -98,3 +98,40 @@ def decode(K, V, n, q, n_slots: int | None = None, sm_scale: float | None = None
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=K.device)
     L.kvs_decode_attn(cache, K, V, n, q, 1.0 / math.sqrt(D) if sm_scale is None else sm_scale, out, workspace)
     return out
+
+
+# ---------------------------------------------------------------- workloads --
+def config_cache(cfg, layer: int, device, batches=None):
+    """Seeded raw cache of one layer: K, V [B, H_kv, N, D] and the last raw keys [B, H_kv, D]."""
+    from . import synth
+    bs = range(cfg.batch) if batches is None else batches
+    ks, vs, lasts = [], [], []
+    for b in bs:
+        k, v, last = synth.make_cache(cfg, layer, b, device)
+        ks.append(k)
+        vs.append(v)
+        lasts.append(last)
+    return torch.stack(ks), torch.stack(vs), torch.stack(lasts)
+
+
+def config_rounds(cfg, layer: int, device, K=None, V=None, batches=None, out_dtype=None, want_flags=True,
+                  last_capacity: int = 0):
+    """Run every merge round of a workload config on one layer.  Returns a list of
+    (K_in, V_in, n_in, Qw, M, bufs) per round; round r + 1 consumes round r's output.
+    `last_capacity` extra slots are reserved after the last round's output (decode appends)."""
+    from . import synth
+    if K is None:
+        K, V, _ = config_cache(cfg, layer, device, batches)
+    bs = list(range(cfg.batch)) if batches is None else list(batches)
+    n = None
+    out = []
+    N = K.shape[2]
+    for r, M in enumerate(cfg.rounds):
+        Qw = torch.stack([synth.window_queries(cfg, layer, b, r, device) for b in bs])
+        T = N - M
+        cap = T + (last_capacity if r == len(cfg.rounds) - 1 else 0)
+        bufs = merge_round(K, V, n, Qw, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, n_slots=N,
+                           out_dtype=out_dtype, out_capacity=cap, want_flags=want_flags)
+        out.append((K, V, n, Qw, M, bufs))
+        K, V, n, N = bufs.K, bufs.V, bufs.n, T
+    return out

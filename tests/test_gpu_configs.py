@@ -1,0 +1,134 @@
+"""GPU parity on the five workload configs at their real per-layer shapes.
+
+C1 and C2 are covered in test_gpu_parity.py.  Here: C3 (one 32-layer-model layer
+at 128K, partial round to a 29% reduction), C4 (batch 8 x 32K, three 2x rounds
+with fresh window queries), C5 (128K merged 4x, then 128 decode steps with
+appended tokens).  Every (batch, layer, kv-head) slice is an independent call
+of the same kernels, so one layer is run in full on the GPU, every slice is
+checked for the compaction invariants, and sampled slices are checked against
+the oracle on the very inputs the GPU consumed in that round.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvs_oracle as O
+from tests.parity import REL_TOL, check_round_slice, host, maxrel
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _invariants(bufs, n_in, N, M, S, R):
+    T = N - M
+    n_out = bufs.n[:, :, :T].long()
+    total_in = N if n_in is None else None
+    sums = n_out.sum(dim=2)
+    if n_in is None:
+        assert torch.all(sums == N)
+    else:
+        assert torch.equal(sums, n_in[:, :, :N].long().sum(dim=2))
+    src = bufs.src[:, :, :T].long()
+    assert torch.all(src[:, :, 1:] > src[:, :, :-1])
+    if bufs.selected is not None:
+        P = O.num_pairs(N, S, R)
+        assert torch.all(bufs.selected[:, :, :P].long().sum(dim=2) == M)
+
+
+def test_c3_partial_round_128k():
+    from long_context_kv_kvslimmer_amd import configs, pipeline
+    cfg = configs.C3
+    layer = 7
+    print("\n[C3] layer 7, N=131072, M=38011", flush=True)
+    rounds = pipeline.config_rounds(cfg, layer, DEV, out_dtype=torch.float32)
+    K, V, n, Qw, M, bufs = rounds[0]
+    torch.cuda.synchronize()
+    N = cfg.n_slots
+    assert M == round(0.29 * N) and bufs.K.shape[2] == N - M == 93061
+    _invariants(bufs, n, N, M, cfg.n_sink, cfg.n_recent)
+    print("[C3] oracle head 3", flush=True)
+    check_round_slice(bufs, K, V, n, Qw, 0, 3, N, cfg.n_sink, cfg.n_recent, M, 1 / math.sqrt(cfg.head_dim),
+                      label="C3 h3")
+
+
+def _parity_rerun(cfg, K, V, n, Qw, M, bufs, N):
+    """Re-run one round with fp32 output on the same inputs: the bf16 output of the real
+    path must be its round-to-nearest-even image, and the fp32 output is what the oracle
+    is compared with."""
+    from long_context_kv_kvslimmer_amd import pipeline
+    b32 = pipeline.merge_round(K, V, n, Qw, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, n_slots=N,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    T = N - M
+    assert torch.equal(b32.K[:, :, :T].to(torch.bfloat16), bufs.K[:, :, :T])
+    assert torch.equal(b32.V[:, :, :T].to(torch.bfloat16), bufs.V[:, :, :T])
+    assert torch.equal(b32.src[:, :, :T], bufs.src[:, :, :T]) and torch.equal(b32.n[:, :, :T], bufs.n[:, :, :T])
+    return b32
+
+
+def test_c4_three_rounds_batch8():
+    from long_context_kv_kvslimmer_amd import configs, pipeline
+    cfg = configs.C4
+    layer = 11
+    print("\n[C4] layer 11, batch 8, three 2x rounds", flush=True)
+    rounds = pipeline.config_rounds(cfg, layer, DEV)
+    torch.cuda.synchronize()
+    N = cfg.n_slots
+    src = None
+    for r, (K, V, n, Qw, M, bufs) in enumerate(rounds):
+        _invariants(bufs, n, N, M, cfg.n_sink, cfg.n_recent)
+        b, h = (5, 2) if r != 1 else (0, 7)
+        print(f"[C4] round {r} oracle b{b} h{h}", flush=True)
+        b32 = _parity_rerun(cfg, K, V, n, Qw, M, bufs, N)
+        check_round_slice(b32, K, V, n, Qw, b, h, N, cfg.n_sink, cfg.n_recent, M, 1 / math.sqrt(cfg.head_dim),
+                          label=f"C4 r{r} b{b} h{h}")
+        s = bufs.src[:, :, :N - M].long()
+        src = s if src is None else torch.gather(src, 2, s)
+        N = N - M
+    # three full 2x rounds: 8x, every output slot holds 8 consecutive tokens
+    assert N == cfg.n_slots // 8
+    assert torch.all(src == torch.arange(0, cfg.n_slots, 8, device=DEV))
+    assert torch.all(rounds[-1][5].n[:, :, :N] == 8)
+
+
+def test_c5_merge_then_decode_128_steps():
+    from long_context_kv_kvslimmer_amd import configs, pipeline, synth
+    cfg = configs.C5
+    layer = 3
+    steps = cfg.decode_steps
+    print("\n[C5] layer 3, 128K merged 4x", flush=True)
+    K0, V0, last = pipeline.config_cache(cfg, layer, DEV)
+    rounds = pipeline.config_rounds(cfg, layer, DEV, K=K0, V=V0, want_flags=False, last_capacity=steps)
+    torch.cuda.synchronize()
+    N = cfg.n_slots
+    for r, (K, V, n, Qw, M, bufs) in enumerate(rounds):
+        _invariants(bufs, n, N, M, cfg.n_sink, cfg.n_recent)
+        N = N - M
+    assert N == cfg.n_slots // 4
+    # round 2 against the oracle on its actual (bf16, counts 2) inputs, one head
+    K, V, n, Qw, M, bufs = rounds[1]
+    print("[C5] oracle round 2, head 6", flush=True)
+    b32 = _parity_rerun(cfg, K, V, n, Qw, M, bufs, 2 * N)
+    check_round_slice(b32, K, V, n, Qw, 0, 6, 2 * N, cfg.n_sink, cfg.n_recent, M, 1 / math.sqrt(cfg.head_dim),
+                      label="C5 r2 h6")
+    # 128 decode steps: append (k, v, n=1) at slot N + t, then attend over N + t + 1 slots
+    Kc, Vc, nc = bufs.K, bufs.V, bufs.n
+    k_new, v_new = synth.decode_tokens(cfg, layer, 0, last[0], steps, DEV)
+    ws = None
+    check_steps = {0, 1, 63, 127}
+    for t in range(steps):
+        Kc[0, :, N + t] = k_new[:, t]
+        Vc[0, :, N + t] = v_new[:, t]
+        nc[0, :, N + t] = 1
+        q = synth.decode_query(cfg, layer, 0, t, DEV)[None]
+        out = pipeline.decode(Kc, Vc, nc, q, n_slots=N + t + 1, workspace=ws)
+        if t in check_steps:
+            torch.cuda.synchronize()
+            print(f"[C5] decode step {t}", flush=True)
+            for hq in (0, 13, 31):
+                h = hq // cfg.group
+                ref = O.decode(host(Kc[0, h, :N + t + 1]), host(Vc[0, h, :N + t + 1]),
+                               host(nc[0, h, :N + t + 1]), host(q[0, hq]), 1 / math.sqrt(cfg.head_dim))
+                assert maxrel(host(out[0, hq]), ref) <= REL_TOL, f"step {t} hq {hq}"
