@@ -26,14 +26,148 @@ METRIC = "KV tokens merged/sec + achieved HBM GB/s (Llama-3.1-8B layer, 32K ctx)
 HBM_PEAK_GBS = 8000.0
 
 
-def algorithmic_bytes(N, H, D, P, M, T, has_n=False, elt=2):
-    """Bytes each call must move (the method's reads and writes, once each)."""
-    row = 2 * D * elt                               # one K row + one V row
-    score = 2 * N * H * row + N * H * 4 + P * H * 4   # K,V twice; g_self, g_cross out
-    merge = N * H * (row + 4 + (4 if has_n else 0)) + P * H * 4 + T * H * (row + 4 + 4)
-    decode = T * H * (row + 4)
-    select = 0
-    return {"kvs_score": score, "kvs_merge_weights": select, "kvs_merge_compact": merge, "kvs_decode_attn": decode}
+def kernel_bytes(N, H, D, P, T, GW, has_n=False, elt=2):
+    """Algorithmic HBM bytes per launch of each kernel: what the method must move, once.
+    row = one K row + one V row of one (batch, kv-head) slot."""
+    row = 2 * D * elt
+    nb = 4 if has_n else 0
+    return {
+        "score_pass1": N * H * (row + nb),                        # K, V once (lse/O partials are not counted)
+        "combine": 0,
+        "score_pass2": N * H * (row + nb) + (N + P) * H * 4,       # K, V once; g_self, g_cross out
+        "select": 0,                                              # a full round selects by rule
+        "merge_compact": N * H * (row + 4 + nb) + P * H * 4 + T * H * (row + 4 + 4),
+        "decode": T * H * (row + 4),
+    }
+
+
+# rocprofv3 kernel names -> the labels the library gives its launches
+KERNEL_LABELS = (("p1_mfma_kernel", "score_pass1"), ("pass1_valu_kernel", "score_pass1"),
+                 ("p2_mfma_kernel", "score_pass2"), ("pass2_valu_kernel", "score_pass2"),
+                 ("combine_kernel", "combine"), ("fill_zero_kernel", "fill_zero"), ("pair_cos_kernel", "pair_cos"),
+                 ("select_kernel", "select"), ("select_fixed_kernel", "select"),
+                 ("merge_compact_kernel", "merge_compact"), ("decode_mfma_kernel", "decode"),
+                 ("decode_kernel", "decode"))
+COPY_BYTES = 1 << 30            # calibration copy: reads and writes this many bytes
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_c2_layer32k.md")
+
+
+def kernel_label(rocprof_name):
+    if "kvs::" not in rocprof_name:
+        return None
+    for key, label in KERNEL_LABELS:
+        if "kvs::" + key in rocprof_name:
+            return label
+    return None
+
+
+def sources_digest():
+    """Digest of every source the kernels are built from; counter figures taken on other
+    sources no longer describe the kernels and are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "long_context_kv_kvslimmer_amd", "csrc"), os.path.join(ROOT, "include")):
+        for f in sorted(os.listdir(d)):
+            if f.endswith((".hip", ".h", ".cpp")):
+                h.update(f.encode())
+                with open(os.path.join(d, f), "rb") as fh:
+                    h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(label):
+    """HBM bytes per launch of `label` from the committed counter summary, if it was
+    taken on the current sources; else None."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    vals = dict(l.strip("` ").split(" = ", 1) for l in lines if l.startswith("`") and " = " in l)
+    if vals.get("sources") != sources_digest():
+        return None
+    v = vals.get(f"traffic_bytes[{label}]")
+    return None if v is None else int(v)
+
+
+def summarize_counters(fetch_csv, write_csv, cmd):
+    """Markdown summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of
+    `bench.py --copy-calibration`: per-dispatch KiB of each library kernel, scaled by
+    what the same counter reads for the calibration copy of COPY_BYTES."""
+    import csv
+    import statistics
+
+    def load(path, counter):
+        per = {}
+        copy = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "neg_kernel" in r["Kernel_Name"] and int(r["Grid_Size"]) >= (1 << 20):
+                copy.append(v)
+            lab = kernel_label(r["Kernel_Name"])
+            if lab:
+                per.setdefault(lab, []).append(v)
+        return {k: statistics.mean(v) for k, v in per.items()}, statistics.mean(copy)
+
+    fetch, fcopy = load(fetch_csv, "FETCH_SIZE")
+    write, wcopy = load(write_csv, "WRITE_SIZE")
+    ff = COPY_BYTES / (fcopy * 1024)
+    fw = COPY_BYTES / (wcopy * 1024)
+    out = ["# HBM traffic per launch, C2 layer (32K ctx, 8x128 KV heads, bf16)", "",
+           "Made by:", "", "```", cmd, "```", "",
+           f"Calibration: a plain elementwise copy (torch.neg) reads and writes {COPY_BYTES} B; FETCH_SIZE "
+           f"reads {fcopy:.1f} KiB for it, WRITE_SIZE {wcopy:.1f} KiB.  Scale factors: fetch {ff:.4f}, "
+           f"write {fw:.4f}.", "",
+           "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB | traffic MB |",
+           "|---|---:|---:|---:|---:|---:|"]
+    lines = []
+    for lab in sorted(set(fetch) | set(write)):
+        r = fetch.get(lab, 0.0) * 1024 * ff
+        w = write.get(lab, 0.0) * 1024 * fw
+        out.append(f"| {lab} | {fetch.get(lab, 0):.1f} | {write.get(lab, 0):.1f} | {r / 1e6:.2f} | {w / 1e6:.2f} | "
+                   f"{(r + w) / 1e6:.2f} |")
+        lines.append(f"`traffic_bytes[{lab}] = {int(round(r + w))}`")
+    out += ["", "Machine-read values (bytes per launch; valid for these sources only):", "",
+            f"`sources = {sources_digest()}`", ""] + lines
+    return "\n".join(out) + "\n"
+
+
+def summarize_trace(stats_csv, bench_json, cmd):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of bench.py next to the
+    per-kernel HIP-event times the same run printed."""
+    import csv
+    rows = {}
+    for r in csv.DictReader(open(stats_csv)):
+        lab = kernel_label(r["Name"])
+        if lab:
+            c, t = rows.get(lab, (0, 0.0))
+            rows[lab] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
+    line = json.loads([l for l in open(bench_json).read().splitlines() if l.startswith("{")][-1])
+    ev = line.get("kernels_warmup_marked", {})
+    out = ["# Kernel durations, C2 layer (32K ctx, 8x128 KV heads, bf16)", "", "Made by:", "", "```", cmd, "```",
+           "", "rocprofv3 averages over every launch in the run; HIP-event averages over the marked warm-up "
+           "steps (every kernel marked).", "",
+           "| kernel | launches | rocprofv3 avg us | HIP-event avg us | algorithmic MB | GB/s (events) |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for lab, (c, t) in sorted(rows.items(), key=lambda kv: -kv[1][1]):
+        e = ev.get(lab, {})
+        out.append(f"| {lab} | {c} | {t / c / 1e3:.2f} | {e.get('avg_ms', float('nan')) * 1e3:.2f} | "
+                   f"{e.get('algorithmic_MB', 0)} | {e.get('GBps')} |")
+    out += ["", f"ms_per_step {line['ms_per_step']}, value {line['value']} {line['unit']}, roofline "
+            f"{json.dumps(line['roofline'])}"]
+    return "\n".join(out) + "\n"
+
+
+def copy_calibration(dev):
+    """A plain copy of known size for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(cfg, K, V, Qw, heads=2):
@@ -66,7 +200,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4, help="rotating input layers (>= 3 to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB copy first (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "CMD"))
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "BENCH_JSON", "CMD"))
     args = ap.parse_args()
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(*args.summarize_counters))
+        return
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(*args.summarize_trace))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported (each (batch, layer, "
               f"kv-head) slice is independent, see DESIGN.md for how the path shards)", file=sys.stderr)
@@ -79,6 +223,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     cfg = configs.C2
+    if args.copy_calibration:
+        copy_calibration(dev)
     B, H, Hq, D, N, W = cfg.batch, cfg.kv_heads, cfg.q_heads, cfg.head_dim, cfg.n_slots, cfg.window
     S, R, M = cfg.n_sink, cfg.n_recent, cfg.rounds[0]
     P = L.num_pairs(N, S, R)
@@ -97,56 +243,62 @@ def main():
     cache = L.cache_desc(sets[0][0], Hq, N)
     rnd = L.round_desc(W, S, R, M, 1.0 / math.sqrt(D))
     out_desc = L.cache_desc(bufs.K, Hq, T)
-    names = ("kvs_score", "kvs_merge_weights", "kvs_merge_compact", "kvs_decode_attn")
     # the adjacent-key cosine only feeds the selection; a round that merges every
     # candidate pair (or none) has nothing to select, so it is not requested then
     cos_out = bufs.cos if 0 < M < P else None
 
-    def step(i, ev=None):
+    def step(i):
         K, V, Qw, q = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record()
         L.kvs_score(cache, K, V, None, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, cos_out, bufs.score_ws)
-        if ev is not None:
-            ev[1].record()
         L.kvs_merge_weights(cache, rnd, bufs.g_self, bufs.g_cross, cos_out, None, None, bufs.sel_state)
-        if ev is not None:
-            ev[2].record()
         L.kvs_merge_compact(cache, K, V, None, bufs.g_self, bufs.g_cross, rnd, bufs.sel_state, out_desc,
                             bufs.K, bufs.V, bufs.n, bufs.src)
-        if ev is not None:
-            ev[3].record()
         L.kvs_decode_attn(dec_cache, bufs.K, bufs.V, bufs.n, q, 1.0 / math.sqrt(D), dec_out, dec_ws)
-        if ev is not None:
-            ev[4].record()
 
-    for i in range(args.warmup):
+    # warm-up; its last steps mark every kernel launch with HIP events to rank the kernels
+    n_marked = min(args.warmup, 5)
+    for i in range(args.warmup - n_marked):
         step(i)
+    every = L.KernelMarks(max_launches=16 * max(n_marked, 1))
+    with every:
+        for i in range(args.warmup - n_marked, args.warmup):
+            step(i)
     torch.cuda.synchronize()
+    per_kernel = {}
+    for name, ms in every.times():
+        tot, cnt = per_kernel.get(name, (0.0, 0))
+        per_kernel[name] = (tot + ms, cnt + 1)
+    dominant = max(per_kernel, key=lambda n: per_kernel[n][0]) if per_kernel else None
 
-    # timed region: K whole steps, per-call HIP events on the stream the kernels run on
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed region: K whole steps; the library records HIP events right before and after
+    # each launch of the dominant kernel (on its stream), timing that kernel live
+    marks = L.KernelMarks(max_launches=4 * args.steps, label=dominant)
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, events[i])
+    t_start.record()
+    with marks:
+        for i in range(args.steps):
+            step(args.warmup + i)
+    t_stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_call = {n: 0.0 for n in names}
-    for ev in events:
-        for k, n in enumerate(names):
-            per_call[n] += ev[k].elapsed_time(ev[k + 1])
-    gpu_ms = sum(events[i][0].elapsed_time(events[i][4]) for i in range(args.steps))
     ms_step = wall * 1e3 / args.steps
-    per_call = {n: v / args.steps for n, v in per_call.items()}
-    abytes = algorithmic_bytes(N, H, D, P, M, T)
-    kernels = {n: {"ms": round(per_call[n], 4),
-                   "algorithmic_MB": round(abytes[n] / 1e6, 2),
-                   "GBps": round(abytes[n] / (per_call[n] * 1e-3) / 1e9, 1) if per_call[n] > 0 else None}
-               for n in names}
-    dominant = max(names, key=lambda n: per_call[n])
-    ach = abytes[dominant] / (per_call[dominant] * 1e-3) / 1e9
-    step_bytes = sum(abytes.values())
+    gpu_ms = t_start.elapsed_time(t_stop) / args.steps
+    timed = [ms for _, ms in marks.times()]
+    if dominant is None and timed:
+        dominant = marks.times()[0][0]
+    kb = kernel_bytes(N, H, D, P, T, cfg.group * W)
+    kernels = {}
+    for name, (tot, cnt) in per_kernel.items():
+        avg = tot / cnt
+        by = kb.get(name, 0)
+        kernels[name] = {"launches_per_step": cnt // max(n_marked, 1), "avg_ms": round(avg, 4),
+                         "algorithmic_MB": round(by / 1e6, 2),
+                         "GBps": round(by / (avg * 1e-3) / 1e9, 1) if by else None}
+    dom_ms = sum(timed) / len(timed)
+    dom_gbps = kb[dominant] / (dom_ms * 1e-3) / 1e9
+    step_bytes = sum(kb[n] * kernels[n]["launches_per_step"] for n in kernels if n in kb)
     line = {
         "metric": METRIC,
         "value": round(B * N / (ms_step * 1e-3), 1),
@@ -165,10 +317,12 @@ def main():
                    "n_slots": N, "window": W, "n_merge": M, "out_slots": T, "input_sets": len(sets),
                    "accumulate": "f32"},
         "hbm_GBps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-        "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
-        "kernels": kernels,
-        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "kernels_warmup_marked": kernels,
+        "roofline": {"kernel": dominant, "avg_ms": round(dom_ms, 4), "launches": len(timed),
+                     "algorithmic_bytes": kb[dominant], "bound": "hbm", "achieved": round(dom_gbps, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(dominant)},
     }
     if not args.no_cpu_baseline:
         K, V, Qw, _ = sets[0]

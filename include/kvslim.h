@@ -190,6 +190,26 @@ kvs_status kvs_decode_attn(const kvs_cache* cache, kvs_dtype dtype,
                            const void* q, float sm_scale, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Kernel timing marks (instrumentation, off by default).
+ *
+ * kvs_marks_begin(max_launches, label): from now on, on the calling thread, the library
+ * records a HIP event on a launch's stream just before and just after each of its kernel
+ * launches whose label equals `label` (every launch if `label` is NULL or ""), for the
+ * first `max_launches` such launches.  Labels: "score_pass1", "score_pass2", "combine",
+ * "fill_zero", "pair_cos", "select", "merge_compact", "decode".  The events are owned by
+ * the library (a per-thread pool created with hipEventDisableSystemFence, grown on demand
+ * and kept until the process ends).  Errors: KVS_ERR_SHAPE if max_launches is outside
+ * [1, 65536] or the label is longer than 63 bytes; KVS_ERR_HIP if an event cannot be made.
+ * kvs_marks_end() stops recording and returns the number of launches marked.
+ * After kvs_marks_end: kvs_mark_name(k) is the k-th marked launch's label (static string,
+ * "" if k is out of range) and kvs_mark_ms(k) its duration in milliseconds (waits for
+ * that launch to finish; -1 if k is out of range or the events fail).
+ * A new kvs_marks_begin discards earlier marks. */
+kvs_status kvs_marks_begin(int32_t max_launches, const char* label);
+int32_t kvs_marks_end(void);
+const char* kvs_mark_name(int32_t k);
+float kvs_mark_ms(int32_t k);
+
 /* Human-readable name of a status code (static string). */
 const char* kvs_status_str(kvs_status s);
 

@@ -1,11 +1,14 @@
 // C ABI of libkvslim (declared in include/kvslim.h): argument validation, workspace
-// sizing and launches on the caller's stream.  No device memory is allocated here and no
-// state is kept besides a per-thread message for the last error.
+// sizing and launches on the caller's stream.  No device memory is allocated here; the
+// only state is a per-thread message for the last error and the per-thread timing-mark
+// event pool (created on first use of kvs_marks_begin).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
+#include <vector>
 
 #include "../../include/kvslim.h"
 #include "kvs_internal.h"
@@ -75,9 +78,81 @@ kvs_status check_round(const kvs_round* r, const kvs::Shape& s, kvs::RoundP& rp,
   return KVS_OK;
 }
 
+// timing marks (kvs_marks_begin): library-owned HIP events, thread-local, off by default
+constexpr int kMaxMarks = 1 << 16;
+struct Marks {
+  std::vector<hipEvent_t> ev;           // 2 per marked launch: before, after
+  std::vector<const char*> names;
+  int cap = 0;                          // launches that fit the event pool
+  int k = 0;                            // launches marked so far
+  bool on = false;
+  char filter[64] = {0};                // mark only launches with this label ("" = all)
+};
+thread_local Marks g_marks;
+
 }  // namespace
 
+namespace kvs {
+
+void mark_before(hipStream_t st, const char* name) {
+  Marks& m = g_marks;
+  if (!m.on || m.k >= m.cap) return;
+  if (m.filter[0] && std::strcmp(m.filter, name) != 0) return;
+  if (hipEventRecord(m.ev[2 * m.k], st) != hipSuccess) return;
+  m.names[m.k] = name;
+  m.k = -m.k - 1;                       // pending: the matching mark_after completes it
+}
+
+void mark_after(hipStream_t st) {
+  Marks& m = g_marks;
+  if (!m.on || m.k >= 0) return;
+  const int k = -m.k - 1;
+  m.k = (hipEventRecord(m.ev[2 * k + 1], st) == hipSuccess) ? k + 1 : k;
+}
+
+}  // namespace kvs
+
 extern "C" {
+
+kvs_status kvs_marks_begin(int32_t max_launches, const char* label) {
+  Marks& m = g_marks;
+  if (max_launches < 1 || max_launches > kMaxMarks)
+    return fail(KVS_ERR_SHAPE, "max_launches %d outside [1, %d]", (int)max_launches, kMaxMarks);
+  if (label && std::strlen(label) >= sizeof(m.filter)) return fail(KVS_ERR_SHAPE, "label too long");
+  while ((int)m.ev.size() < 2 * max_launches) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
+    if (err != hipSuccess) return fail(KVS_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(err));
+    m.ev.push_back(e);
+  }
+  m.names.assign(max_launches, "");
+  m.cap = max_launches;
+  m.k = 0;
+  std::snprintf(m.filter, sizeof(m.filter), "%s", label ? label : "");
+  m.on = true;
+  return KVS_OK;
+}
+
+int32_t kvs_marks_end(void) {
+  Marks& m = g_marks;
+  m.on = false;
+  if (m.k < 0) m.k = -m.k - 1;
+  return m.k;
+}
+
+const char* kvs_mark_name(int32_t k) {
+  const Marks& m = g_marks;
+  return (!m.on && k >= 0 && k < m.k) ? m.names[k] : "";
+}
+
+float kvs_mark_ms(int32_t k) {
+  const Marks& m = g_marks;
+  if (m.on || k < 0 || k >= m.k) return -1.0f;
+  if (hipEventSynchronize(m.ev[2 * k + 1]) != hipSuccess) return -1.0f;
+  float ms = -1.0f;
+  if (hipEventElapsedTime(&ms, m.ev[2 * k], m.ev[2 * k + 1]) != hipSuccess) return -1.0f;
+  return ms;
+}
 
 int64_t kvs_num_pairs(int64_t n_slots, int64_t n_sink, int64_t n_recent) {
   if (n_slots < 0 || n_sink < 0 || n_recent < 0) return 0;

@@ -385,9 +385,9 @@ template <typename T, int D, int G>
 static hipError_t launch_dec_g(const DecArgs& a, const Shape& s, hipStream_t st) {
   const dim3 grid(a.nsplit, (unsigned)(s.B * s.Hkv));
   if (a.n)
-    hipLaunchKernelGGL((decode_kernel<T, D, G, true>), grid, dim3(256), 0, st, a);
+    KVS_LAUNCH("decode", (decode_kernel<T, D, G, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_kernel<T, D, G, false>), grid, dim3(256), 0, st, a);
+    KVS_LAUNCH("decode", (decode_kernel<T, D, G, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -395,9 +395,9 @@ template <int D, int G>
 static hipError_t launch_dec_mfma_g(const DecArgs& a, const Shape& s, hipStream_t st) {
   const dim3 grid(a.nsplit, (unsigned)(s.B * s.Hkv));
   if (a.n)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G, true>), grid, dim3(64 * kDecWaves), 0, st, a);
+    KVS_LAUNCH("decode", (decode_mfma_kernel<D, G, true>), grid, dim3(64 * kDecWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G, false>), grid, dim3(64 * kDecWaves), 0, st, a);
+    KVS_LAUNCH("decode", (decode_mfma_kernel<D, G, false>), grid, dim3(64 * kDecWaves), 0, st, a);
   return hipGetLastError();
 }
 

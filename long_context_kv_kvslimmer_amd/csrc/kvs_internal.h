@@ -7,6 +7,18 @@
 
 namespace kvs {
 
+// Timing marks (see kvs_set_marks): before / after every kernel launch.
+void mark_before(hipStream_t st, const char* name);
+void mark_after(hipStream_t st);
+
+// Launch with timing marks around it.
+#define KVS_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                 \
+  do {                                                                           \
+    ::kvs::mark_before((stream), (name));                                        \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);         \
+    ::kvs::mark_after((stream));                                                 \
+  } while (0)
+
 constexpr int kChunkPairs = 64;      // pairs per compaction chunk (one wavefront)
 constexpr int kSelHeaderInts = 4;    // SelHeader size in int32
 

@@ -198,14 +198,14 @@ static hipError_t launch_merge_t(const MergeArgs& a, bool partial, bool has_n, h
   const int blocks = (int)((a.total_waves + 3) / 4);
   if (partial) {
     if (has_n)
-      hipLaunchKernelGGL((merge_compact_kernel<TI, TO, D, true, true>), dim3(blocks), dim3(256), 0, st, a);
+      KVS_LAUNCH("merge_compact", (merge_compact_kernel<TI, TO, D, true, true>), dim3(blocks), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((merge_compact_kernel<TI, TO, D, true, false>), dim3(blocks), dim3(256), 0, st, a);
+      KVS_LAUNCH("merge_compact", (merge_compact_kernel<TI, TO, D, true, false>), dim3(blocks), dim3(256), 0, st, a);
   } else {
     if (has_n)
-      hipLaunchKernelGGL((merge_compact_kernel<TI, TO, D, false, true>), dim3(blocks), dim3(256), 0, st, a);
+      KVS_LAUNCH("merge_compact", (merge_compact_kernel<TI, TO, D, false, true>), dim3(blocks), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((merge_compact_kernel<TI, TO, D, false, false>), dim3(blocks), dim3(256), 0, st, a);
+      KVS_LAUNCH("merge_compact", (merge_compact_kernel<TI, TO, D, false, false>), dim3(blocks), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -176,7 +176,7 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  KVS_LAUNCH("fill_zero", fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 
@@ -184,7 +184,7 @@ hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, f
                           hipStream_t st) {
   if (units == 0) return hipSuccess;
   if (nsplit > kMaxSplit) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3(units), dim3(128), 0, st, part, nsplit, D, lse, out);
+  KVS_LAUNCH("combine", combine_kernel, dim3(units), dim3(128), 0, st, part, nsplit, D, lse, out);
   return hipGetLastError();
 }
 
@@ -310,17 +310,17 @@ static hipError_t launch_score_valu(const Shape& s, const RoundP& r, const P1Arg
                                     const CosArgs& ca, float* lse, float* O, hipStream_t st) {
   const int64_t BH = (int64_t)s.B * s.Hkv;
   const int nqb = (int)((p1.GW + 127) / 128);
-  hipLaunchKernelGGL((pass1_valu_kernel<T, D>), dim3(p1.nsplit, nqb, BH), dim3(256), 0, st, p1);
+  KVS_LAUNCH("score_pass1", (pass1_valu_kernel<T, D>), dim3(p1.nsplit, nqb, BH), dim3(256), 0, st, p1);
   launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st);
   if (ca.cos && r.P > 0) {
     constexpr int GPB = 256 / (D / Elt<T>::kPerChunk);
-    hipLaunchKernelGGL((pair_cos_kernel<T, D>), dim3((r.P + GPB - 1) / GPB, BH), dim3(256), 0, st, ca);
+    KVS_LAUNCH("pair_cos", (pair_cos_kernel<T, D>), dim3((r.P + GPB - 1) / GPB, BH), dim3(256), 0, st, ca);
   }
   const int64_t units = r.S + r.P + (s.N - r.S - 2 * r.P);
   if (p2.n)
-    hipLaunchKernelGGL((pass2_valu_kernel<T, D, true>), dim3((units + 63) / 64, BH), dim3(256), 0, st, p2);
+    KVS_LAUNCH("score_pass2", (pass2_valu_kernel<T, D, true>), dim3((units + 63) / 64, BH), dim3(256), 0, st, p2);
   else
-    hipLaunchKernelGGL((pass2_valu_kernel<T, D, false>), dim3((units + 63) / 64, BH), dim3(256), 0, st, p2);
+    KVS_LAUNCH("score_pass2", (pass2_valu_kernel<T, D, false>), dim3((units + 63) / 64, BH), dim3(256), 0, st, p2);
   return hipGetLastError();
 }
 

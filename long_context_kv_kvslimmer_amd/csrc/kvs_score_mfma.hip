@@ -580,9 +580,9 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
   const int nqb = (int)((p1.GW + kQB - 1) / kQB);
   const dim3 grid(p1.nsplit, nqb, (unsigned)BH);
   if (p1.n)
-    hipLaunchKernelGGL((p1_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p1, base, ca);
+    KVS_LAUNCH("score_pass1", (p1_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p1, base, ca);
   else
-    hipLaunchKernelGGL((p1_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p1, base, ca);
+    KVS_LAUNCH("score_pass1", (p1_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p1, base, ca);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st);
@@ -594,9 +594,9 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
     if (e != hipSuccess) return e;
   }
   if (p2.n)
-    hipLaunchKernelGGL((p2_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p2, base, p1.chunk);
+    KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p2, base, p1.chunk);
   else
-    hipLaunchKernelGGL((p2_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p2, base, p1.chunk);
+    KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p2, base, p1.chunk);
   return hipGetLastError();
 }
 

@@ -201,9 +201,9 @@ hipError_t launch_select(const Shape& s, const RoundP& r, const float* g_self, c
   const int blocks = s.B * s.Hkv;
   if (blocks == 0) return hipSuccess;
   if (cos == nullptr)
-    hipLaunchKernelGGL(select_fixed_kernel, dim3(blocks), dim3(kSelThreads), 0, st, a);
+    KVS_LAUNCH("select", select_fixed_kernel, dim3(blocks), dim3(kSelThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(select_kernel, dim3(blocks), dim3(kSelThreads), 0, st, a);
+    KVS_LAUNCH("select", select_kernel, dim3(blocks), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
 

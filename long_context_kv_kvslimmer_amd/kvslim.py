@@ -21,7 +21,8 @@ KVS_BF16, KVS_F32 = 0, 1
 KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE = range(4)
 
 EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_merge_weights", "kvs_merge_compact",
-           "kvs_decode_attn", "kvs_status_str", "kvs_last_error", "kvs_version")
+           "kvs_decode_attn", "kvs_marks_begin", "kvs_marks_end", "kvs_mark_name", "kvs_mark_ms", "kvs_status_str",
+           "kvs_last_error", "kvs_version")
 
 
 class KvsCache(ctypes.Structure):
@@ -54,6 +55,10 @@ def _load():
         "kvs_merge_weights": (ctypes.c_int, [C, R, P, P, P, P, P, P, SZ, P, SZ, P]),
         "kvs_merge_compact": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, P, R, P, C, ctypes.c_int, P, P, P, P, P]),
         "kvs_decode_attn": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, F, P, P, SZ, P]),
+        "kvs_marks_begin": (ctypes.c_int, [I32, ctypes.c_char_p]),
+        "kvs_marks_end": (I32, []),
+        "kvs_mark_name": (ctypes.c_char_p, [I32]),
+        "kvs_mark_ms": (F, [I32]),
         "kvs_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "kvs_last_error": (ctypes.c_char_p, []),
         "kvs_version": (I32, []),
@@ -78,6 +83,34 @@ def last_error() -> str:
 
 def version() -> int:
     return _lib.kvs_version()
+
+
+class KernelMarks:
+    """Time the library's kernel launches inside a `with` block: HIP events recorded by the
+    library right before and after each launch (only those labelled `label`, if given),
+    on that launch's stream.  After the block `.times()` gives [(label, ms), ...]."""
+
+    def __init__(self, max_launches: int = 64, label: str | None = None):
+        self.max_launches = max_launches
+        self.label = label
+        self.n = 0
+
+    def __enter__(self):
+        _check(_lib.kvs_marks_begin(self.max_launches, None if self.label is None else self.label.encode()))
+        return self
+
+    def __exit__(self, *exc):
+        self.n = _lib.kvs_marks_end()
+        return False
+
+    def times(self):
+        out = []
+        for k in range(self.n):
+            ms = _lib.kvs_mark_ms(k)
+            if ms < 0:
+                raise KvsError(KVS_ERR_HIP, f"timing mark {k} failed")
+            out.append((_lib.kvs_mark_name(k).decode(), ms))
+        return out
 
 
 def _check(s: int):

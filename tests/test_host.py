@@ -144,3 +144,14 @@ def test_decode_validation(L):
 def test_status_strings(L):
     for s in range(9):
         assert L.status_str(s).startswith("KVS_")
+
+
+def test_timing_marks_validation(L):
+    lib = L._lib
+    assert lib.kvs_marks_begin(0, None) == L.KVS_ERR_SHAPE
+    assert lib.kvs_marks_begin(1 << 17, None) == L.KVS_ERR_SHAPE
+    assert lib.kvs_marks_begin(4, b"x" * 64) == L.KVS_ERR_SHAPE
+    # nothing was marked: no names, no durations
+    assert lib.kvs_marks_end() == 0
+    assert lib.kvs_mark_name(0) == b""
+    assert lib.kvs_mark_ms(0) == -1.0
