@@ -332,40 +332,164 @@ __global__ __launch_bounds__(kThreads, 1) void p1_mfma_kernel(P1Args a, int64_t 
 }
 
 // ------------------------------------------------------------------------- pass 2 --
-// grid: x = slot chunk, y = query block (128), z = (b, kv-head).  Slot-per-lane layout:
-// S[q, slot] = Q . K^T and R[q, slot] = (-2 O) . V^T + ||v||^2 + ||o||^2 on 32x32x16 MFMA,
-// lane l holding slot 32 sb + l % 32 for 16 of the wave's 32 queries, so the sum over
-// queries stays in registers; the pair partner slot is one DPP xor-1 away.  With more
-// than one query block the per-slot sums are accumulated with atomics (not the case for
-// <= 128 window queries per kv head).
+// Slot-per-lane layout: S[q, slot] = Q . K^T and R[q, slot] = (-2 O) . V^T + ||v||^2 + ||o||^2
+// on 32x32x16 MFMA, lane l holding slot l % 32 of the tile for 16 of the wave's 32 queries,
+// so the sum over queries stays in registers; the pair partner slot is one DPP xor-1 away.
+//
+// A workgroup is four waves (128 queries) over one slot chunk; two workgroups share a CU.
+// K and V arrive by 16-byte buffer loads written straight into LDS (no register staging)
+// as 32-slot tiles in a four-deep ring: tile t is computed while t + 1 has landed and
+// t + 2, t + 3 are in flight.  Rows are unpadded; the 16-byte chunks of row r sit at
+// position c ^ swz(r), which keeps both the row reads of the MFMA operands and the tile
+// setup reads free of bank conflicts.  Per-slot sums over the four waves are folded into
+// LDS once per tile and written out at the end, so the loop issues no global stores.
+constexpr int kT2 = 32;              // slots per tile
+constexpr int kRing2 = 4;            // tile buffers
+constexpr int kW2 = 4;               // waves per workgroup
+constexpr int kChunk2Max = 1024;     // slots per workgroup at most
+
+template <int D>
+struct Dma {
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int ROWB = 2 * D;               // bytes per row
+  static constexpr int TILEB = kT2 * ROWB;         // bytes per K (or V) tile
+  static constexpr int RPI = 1024 / ROWB;          // rows filled by one wave-wide 16-byte load
+  static constexpr int IPW = TILEB / 1024 / kW2;   // such loads per wave per K (or V) tile
+};
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// byte offset of 16-byte chunk c of row r inside a tile
+template <int D>
+__device__ __forceinline__ int chunk_off(int r, int c) {
+  return r * (2 * D) + ((c ^ swz<D>(r)) << 4);
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes from `base` (stride 0): loads beyond the range
+// return zeros.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4_t r;
+  r.x = (uint32_t)a;
+  r.y = (uint32_t)(a >> 32) & 0xffffu;
+  r.z = bytes;
+  r.w = 0x00020000u;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uint64_t>((const lds_u8*)p);
+}
+
+// Buffer loads written straight to LDS: lane i's 16 (or 4) bytes land at lds + 16 i (4 i).
+// They are issued as inline assembly with no register results, so the compiler does not
+// order them against unrelated LDS reads; the caller tracks completion with wait_vm.
+__device__ __forceinline__ void dma16(const u32x4_t& rs, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(off), "s"(rs)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const u32x4_t& rs, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(off), "s"(rs)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (loads
+// return in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// grid: one workgroup per (bh, slot chunk, query block), bh fastest so that the blocks of
+// one head land on one XCD.
 template <int D, bool HAS_N>
-__global__ __launch_bounds__(kThreads, 1) void p2_mfma_kernel(P2Args a, int64_t base, int64_t chunk) {
+__global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t base, int64_t chunk, int nsplit,
+                                                             int BH) {
   using C = Cfg32<D>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[kGroups * 2 * 2 * C::TILE];
-  __shared__ __attribute__((aligned(16))) float lgs[kGroups * 2 * kTile];
-  __shared__ float vns[kGroups * 2 * kTile];
-  __shared__ float dvs[kGroups * 2 * (kTile / 2)];
-  __shared__ float red_s[kGroups * 2 * kGroupWaves * kTile];
-  __shared__ float red_x[kGroups * 2 * kGroupWaves * (kTile / 2)];
-  __shared__ __attribute__((aligned(16))) float qon[kQB];   // ||o_q||^2 of the block's queries
+  using M = Dma<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t kr[kRing2 * M::TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vr[kRing2 * M::TILEB];
+  __shared__ int32_t nr[kRing2 * kT2];            // slot counts as loaded
+  __shared__ float lgs[kRing2 * kT2];             // log2 n; -inf outside the chunk
+  __shared__ float vns[kRing2 * kT2];             // ||v||^2
+  __shared__ float dvs[kRing2 * (kT2 / 2)];       // ||v_m - v_{m+1}||^2
+  __shared__ float red_s[2 * kW2 * kT2];
+  __shared__ float red_x[2 * kW2 * (kT2 / 2)];
+  __shared__ float gss[kChunk2Max];
+  __shared__ float gxs[kChunk2Max / 2];
+  __shared__ __attribute__((aligned(16))) float qon[kQB];   // ||o_q||^2
   __shared__ __attribute__((aligned(16))) float qnb[kQB];   // -lse_q in log2 units (-inf: padding)
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int grp = wv / kGroupWaves, gw = wv % kGroupWaves, gt = tid % kGT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, h = lane >> 5;
   const bool odd = (c32 & 1) != 0;
-  const int64_t bh = blockIdx.z;
+  const int64_t id = blockIdx.x;
+  const int64_t bh = id % BH;
+  const int64_t rest = id / BH;
+  const int64_t split = rest % nsplit, qb = rest / nsplit;
   const int64_t b = bh / a.Hkv, hk = bh - b * a.Hkv;
-  const bf16* Kp = static_cast<const bf16*>(a.K) + b * a.sb + hk * a.sh;
-  const bf16* Vp = static_cast<const bf16*>(a.V) + b * a.sb + hk * a.sh;
-  const int32_t* np = HAS_N ? a.n + (b * a.sb + hk * a.sh) / D : nullptr;
+  const int64_t hoff = b * a.sb + hk * a.sh;
+
+  const int64_t c0 = base + split * chunk;
+  const int64_t lo = c0 > 0 ? c0 : 0;
+  const int64_t hi = c0 + chunk < a.N ? c0 + chunk : a.N;
+  if (hi <= lo) return;
+  const int ntiles = (int)((hi - c0 + kT2 - 1) / kT2);
+  const uint32_t span = (uint32_t)(hi - lo);
+  const u32x4_t rk = make_rsrc(static_cast<const bf16*>(a.K) + hoff + lo * D, span * M::ROWB);
+  const u32x4_t rv = make_rsrc(static_cast<const bf16*>(a.V) + hoff + lo * D, span * M::ROWB);
+  const int32_t* np = HAS_N ? a.n + hoff / D + lo : nullptr;
+  const u32x4_t rn = make_rsrc(HAS_N ? static_cast<const void*>(np) : a.K, HAS_N ? span * 4u : 0u);
+
+  // tile t -> ring buffer t % kRing2; rows outside [lo, hi) read as zeros
+  auto issue = [&](int t) {
+    const int buf = t % kRing2;
+    const int64_t t0 = c0 + (int64_t)t * kT2;
+#pragma unroll
+    for (int j = 0; j < M::IPW; ++j) {
+      const int u = j * kW2 + wv;
+      const int r = u * M::RPI + lane / M::CPR;
+      const int c = (lane % M::CPR) ^ swz<D>(r);
+      const uint32_t off = (uint32_t)((t0 + r - lo) * M::ROWB) + (uint32_t)(c << 4);
+      dma16(rk, lds_addr(kr + buf * M::TILEB + u * 1024), off);
+      dma16(rv, lds_addr(vr + buf * M::TILEB + u * 1024), off);
+    }
+    if (HAS_N && wv == 0 && lane < kT2) {
+      const uint32_t off = (uint32_t)((t0 + lane - lo) * 4);
+      dma4(rn, lds_addr(nr + buf * kT2), off);
+    }
+  };
+  // wait for every load of tile t + 1 given whether tile t + 2 was issued after it
+  auto wait_tile = [&](bool later) {
+    if (later) {
+      if (HAS_N && wv == 0) wait_vm<2 * M::IPW + 1>();
+      else wait_vm<2 * M::IPW>();
+    } else {
+      wait_vm<0>();
+    }
+  };
+
+  issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+
+  // the wave's 32 queries as the A operand: Q and -2 O (hi + lo), row q0 + l % 32
   const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + hk * a.G) * (int64_t)a.W) * D;
   const float* Op = a.O + bh * a.GW * (int64_t)D;
   const float* Lp = a.lse + bh * a.GW;
-
-  // the wave's 32 queries as the A operand: Q and -2 O (hi + lo), row q0 + l % 32
-  const int64_t q0 = (int64_t)blockIdx.y * kQB + gw * 32;
-  const int64_t qa = q0 + c32;
+  const int64_t qa = qb * kQB + wv * 32 + c32;
   bf16x8_t qop[C::KS], ohi[C::KS], olo[C::KS];
   load_rows32<D>(Qp, a.GW, qa, qop);
   float on_a = 0.f;
@@ -381,41 +505,24 @@ __global__ __launch_bounds__(kThreads, 1) void p2_mfma_kernel(P2Args a, int64_t 
     split_hi_lo(o8, ohi[ks], olo[ks]);
   }
   on_a += __shfl_xor(on_a, 32, 64);
-  if (grp == 0 && h == 0) {
-    qon[gw * 32 + c32] = on_a;
-    qnb[gw * 32 + c32] = qa < a.GW ? -Lp[qa] * kLog2e : -INFINITY;   // padded queries: alpha = 0
+  if (h == 0) {
+    qon[wv * 32 + c32] = on_a;
+    qnb[wv * 32 + c32] = qa < a.GW ? -Lp[qa] * kLog2e : -INFINITY;   // padded queries: alpha = 0
   }
-  // result rows of this lane are queries q0 + 8 (i / 4) + 4 h + i % 4; their constants are
-  // read from LDS as broadcast float4s (published before the first tile barrier)
-  const float* on_row = qon + gw * 32 + 4 * h;
-  const float* nb_row = qnb + gw * 32 + 4 * h;
+  // result rows of this lane are queries 8 (i / 4) + 4 h + i % 4 of the wave's block
+  const float* on_row = qon + wv * 32 + 4 * h;
+  const float* nb_row = qnb + wv * 32 + 4 * h;
   const float cs = a.scale * kLog2e;
 
-  const int64_t c0 = base + (int64_t)blockIdx.x * chunk;
-  const int64_t c1 = c0 + chunk;
-  const int64_t lo = c0 > 0 ? c0 : 0;
-  const int64_t hi = c1 < a.N ? c1 : a.N;
-  const int64_t tend = hi;
-  const int ntiles = (int)((tend - c0 + kTile - 1) / kTile);
-  const int iters = (ntiles + 1) / 2;
-  auto tile_of = [&](int i) { return c0 + (int64_t)(2 * i + grp) * kTile; };
-  auto Kt = [&](int s) { return smem + ((grp * 2 + s) * 2) * C::TILE; };
-  auto Vt = [&](int s) { return smem + ((grp * 2 + s) * 2 + 1) * C::TILE; };
-  auto Lg = [&](int s) { return lgs + (grp * 2 + s) * kTile; };
-  auto Vn = [&](int s) { return vns + (grp * 2 + s) * kTile; };
-  auto Dv = [&](int s) { return dvs + (grp * 2 + s) * (kTile / 2); };
-  auto Rs = [&](int par, int w) { return red_s + ((grp * 2 + par) * kGroupWaves + w) * kTile; };
-  auto Rx = [&](int par, int w) { return red_x + ((grp * 2 + par) * kGroupWaves + w) * (kTile / 2); };
-
-  // commit a staged tile with ||v||^2 per slot and ||v_m - v_{m+1}||^2 per pair
-  auto commit = [&](const Stage<D>& st, int s, int64_t t0) {
-    commit_rows<D>(st, Kt(s), Vt(s), gt);
-    tile_bias<HAS_N>(np, t0, lo, hi, gt, Lg(s));
-#pragma unroll
-    for (int ps = 0; ps < C::NPASS; ++ps) {
+  // per-tile setup of tile t (landed): ||v||^2, ||v_m - v_{m+1}||^2 and log2 n per slot
+  auto setup = [&](int t) {
+    const int buf = t % kRing2;
+    const uint8_t* V_ = vr + buf * M::TILEB;
+    if (tid < (kT2 / 2) * M::CPR) {
+      const int pp = tid / M::CPR, ch = tid % M::CPR;
       float x0[8], x1[8];
-      unpack<bf16>(st.v[ps][0], x0);
-      unpack<bf16>(st.v[ps][1], x1);
+      unpack<bf16>(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(2 * pp, ch)), x0);
+      unpack<bf16>(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(2 * pp + 1, ch)), x1);
       float s0 = 0.f, s1 = 0.f, sd = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -424,125 +531,134 @@ __global__ __launch_bounds__(kThreads, 1) void p2_mfma_kernel(P2Args a, int64_t 
         const float d = x0[j] - x1[j];
         sd = __builtin_fmaf(d, d, sd);
       }
-      s0 = group_sum<C::CPR>(s0);
-      s1 = group_sum<C::CPR>(s1);
-      sd = group_sum<C::CPR>(sd);
-      if (gt % C::CPR == 0) {
-        const int pp = ps * C::PPP + gt / C::CPR;
-        Vn(s)[2 * pp] = s0;
-        Vn(s)[2 * pp + 1] = s1;
-        Dv(s)[pp] = sd;
+      s0 = group_sum<M::CPR>(s0);
+      s1 = group_sum<M::CPR>(s1);
+      sd = group_sum<M::CPR>(sd);
+      if (ch == 0) {
+        vns[buf * kT2 + 2 * pp] = s0;
+        vns[buf * kT2 + 2 * pp + 1] = s1;
+        dvs[buf * (kT2 / 2) + pp] = sd;
       }
+    }
+    if (tid < kT2) {
+      const int64_t s = c0 + (int64_t)t * kT2 + tid;
+      lgs[buf * kT2 + tid] = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)nr[buf * kT2 + tid]) : 0.f) : -INFINITY;
     }
   };
 
-  // write the wave-summed g_self / g_cross of a finished tile (parity par)
-  auto flush = [&](int par, int64_t t0) {
-    if (gt < kTile) {
-      const int64_t s = t0 + gt;
-      if (s >= lo && s < hi) {
-        float v = 0.f;
+  // fold the four waves' sums of tile t into the chunk's per-slot totals
+  auto fold = [&](int t) {
+    const int par = t & 1;
+    const int64_t t0 = c0 + (int64_t)t * kT2;
+    if (tid < kT2) {
+      float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < kGroupWaves; ++w) v += Rs(par, w)[gt];
-        if (gridDim.y == 1) a.g_self[bh * a.N + s] = v;
-        else atomicAdd(&a.g_self[bh * a.N + s], v);
-      }
-    } else if (gt < kTile + kTile / 2) {
-      const int pp = gt - kTile;
-      const int64_t m0 = t0 + 2 * pp;
-      const int64_t p = (m0 - a.S) / 2;
-      if (m0 >= a.S && m0 >= lo && m0 + 1 < hi && p < a.P) {
-        float v = 0.f;
+      for (int w = 0; w < kW2; ++w) v += red_s[(par * kW2 + w) * kT2 + tid];
+      gss[t * kT2 + tid] = v;
+    } else if (tid < kT2 + kT2 / 2) {
+      const int pp = tid - kT2;
+      float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < kGroupWaves; ++w) v += Rx(par, w)[pp];
-        if (gridDim.y == 1) a.g_cross[bh * a.P + p] = v;
-        else atomicAdd(&a.g_cross[bh * a.P + p], v);
+      for (int w = 0; w < kW2; ++w) v += red_x[(par * kW2 + w) * (kT2 / 2) + pp];
+      gxs[t * (kT2 / 2) + pp] = v;
+    }
+    (void)t0;
+  };
+
+  auto compute = [&](int t) {
+    const int buf = t % kRing2;
+    const int64_t t0 = c0 + (int64_t)t * kT2;
+    const uint8_t* K_ = kr + buf * M::TILEB;
+    const uint8_t* V_ = vr + buf * M::TILEB;
+    const bool plain = !HAS_N && t0 >= lo && t0 + kT2 <= hi;
+    const float vn = vns[buf * kT2 + c32];
+    const float dvp = dvs[buf * (kT2 / 2) + (c32 >> 1)];
+    const float lgv = plain ? 0.f : lgs[buf * kT2 + c32];
+    f32x16_t st, rt;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float4 o4 = *reinterpret_cast<const float4*>(on_row + 8 * k4);
+      rt[4 * k4] = vn + o4.x;
+      rt[4 * k4 + 1] = vn + o4.y;
+      rt[4 * k4 + 2] = vn + o4.z;
+      rt[4 * k4 + 3] = vn + o4.w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[4 * k4 + r] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int off = chunk_off<D>(c32, 2 * ks + h);
+      const bf16x8_t bk = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + off));
+      const bf16x8_t bv = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + off));
+      st = mfma32(qop[ks], bk, st);
+      rt = mfma32(ohi[ks], bv, rt);
+      rt = mfma32(olo[ks], bv, rt);
+    }
+    float al[16];
+    float gs = 0.f;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float4 n4 = *reinterpret_cast<const float4*>(nb_row + 8 * k4);
+      const float nb[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * k4 + r;
+        al[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], cs, lgv + nb[r]));
+        const float tt = al[i] * fabsf(__builtin_fmaf(-2.f, al[i], 1.f));
+        gs = __builtin_fmaf(tt, __builtin_amdgcn_sqrtf(fabsf(rt[i])), gs);
       }
+    }
+    // pairs (even slot, odd slot) of the same query: the even lane takes queries i < 8,
+    // the odd lane queries i >= 8, each receiving the partner's alpha and r^2 by DPP
+    float gx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sa = odd ? al[i] : al[i + 8], sr = odd ? rt[i] : rt[i + 8];
+      const float oa = odd ? al[i + 8] : al[i], orr = odd ? rt[i + 8] : rt[i];
+      const float pa = dpp<kDppXor1>(sa), pr = dpp<kDppXor1>(sr);
+      const float rc = __builtin_fmaf(2.f, orr + pr, -dvp);
+      gx = __builtin_fmaf(oa * pa, __builtin_amdgcn_sqrtf(fabsf(rc)), gx);
+    }
+    gx += dpp<kDppXor1>(gx);
+    gs += __shfl_xor(gs, 32, 64);
+    gx += __shfl_xor(gx, 32, 64);
+    if (h == 0) {
+      red_s[((t & 1) * kW2 + wv) * kT2 + c32] = gs;
+      if (!odd) red_x[((t & 1) * kW2 + wv) * (kT2 / 2) + (c32 >> 1)] = gx;
     }
   };
 
-  auto compute = [&](int s, int par, int64_t t0) {
-    const bf16* K_ = Kt(s);
-    const bf16* V_ = Vt(s);
-    const bool plain = !HAS_N && t0 >= lo && t0 + kTile <= hi;
-#pragma unroll 1
-    for (int sb = 0; sb < 2; ++sb) {
-      const int slot = sb * 32 + c32;
-      const float vn = Vn(s)[slot];
-      const float dvp = Dv(s)[slot >> 1];
-      const float lgv = plain ? 0.f : Lg(s)[slot];
-      f32x16_t st, rt;
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const float4 o4 = *reinterpret_cast<const float4*>(on_row + 8 * k4);
-        rt[4 * k4] = vn + o4.x;
-        rt[4 * k4 + 1] = vn + o4.y;
-        rt[4 * k4 + 2] = vn + o4.z;
-        rt[4 * k4 + 3] = vn + o4.w;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[4 * k4 + r] = 0.f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8_t bk = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + slot * C::PITCH + ks * 16 + h * 8));
-        const bf16x8_t bv = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + slot * C::PITCH + ks * 16 + h * 8));
-        st = mfma32(qop[ks], bk, st);
-        rt = mfma32(ohi[ks], bv, rt);
-        rt = mfma32(olo[ks], bv, rt);
-      }
-      float al[16];
-      float gs = 0.f;
-      float nb[16];
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const float4 n4 = *reinterpret_cast<const float4*>(nb_row + 8 * k4);
-        nb[4 * k4] = n4.x;
-        nb[4 * k4 + 1] = n4.y;
-        nb[4 * k4 + 2] = n4.z;
-        nb[4 * k4 + 3] = n4.w;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        al[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], cs, lgv + nb[i]));
-        const float t = al[i] * fabsf(__builtin_fmaf(-2.f, al[i], 1.f));
-        gs = __builtin_fmaf(t, __builtin_amdgcn_sqrtf(fabsf(rt[i])), gs);
-      }
-      // pairs (even slot, odd slot) of the same query: the even lane takes queries i < 8,
-      // the odd lane queries i >= 8, each receiving the partner's alpha and r^2 by DPP
-      float gx = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float sa = odd ? al[i] : al[i + 8], sr = odd ? rt[i] : rt[i + 8];
-        const float oa = odd ? al[i + 8] : al[i], orr = odd ? rt[i + 8] : rt[i];
-        const float pa = dpp<kDppXor1>(sa), pr = dpp<kDppXor1>(sr);
-        const float rc = __builtin_fmaf(2.f, orr + pr, -dvp);
-        gx = __builtin_fmaf(oa * pa, __builtin_amdgcn_sqrtf(fabsf(rc)), gx);
-      }
-      gx += dpp<kDppXor1>(gx);
-      gs += __shfl_xor(gs, 32, 64);
-      gx += __shfl_xor(gx, 32, 64);
-      if (h == 0) {
-        Rs(par, gw)[slot] = gs;
-        if (!odd) Rx(par, gw)[slot >> 1] = gx;
-      }
-    }
-  };
-
-  Stage<D> stg;
-  if (tile_of(0) < tend) {
-    stg.fetch(Kp, Vp, tile_of(0), lo, hi, gt);
-    commit(stg, 0, tile_of(0));
-  }
-  if (tile_of(1) < tend) stg.fetch(Kp, Vp, tile_of(1), lo, hi, gt);
-  for (int i = 0; i < iters; ++i) {
+  wait_tile(ntiles > 1);     // tile 0 landed
+  __syncthreads();
+  setup(0);
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) wait_tile(t + 2 < ntiles);
     __syncthreads();
-    if (i > 0 && tile_of(i - 1) < tend) flush((i - 1) & 1, tile_of(i - 1));
-    if (tile_of(i + 1) < tend) commit(stg, (i + 1) & 1, tile_of(i + 1));
-    if (tile_of(i + 2) < tend) stg.fetch(Kp, Vp, tile_of(i + 2), lo, hi, gt);
-    if (tile_of(i) < tend) compute(i & 1, i & 1, tile_of(i));
+    if (t + 3 < ntiles) issue(t + 3);
+    if (t + 1 < ntiles) setup(t + 1);
+    if (t > 0) fold(t - 1);
+    compute(t);
   }
   __syncthreads();
-  if (iters > 0 && tile_of(iters - 1) < tend) flush((iters - 1) & 1, tile_of(iters - 1));
+  fold(ntiles - 1);
+  __syncthreads();
+
+  // per-slot totals of the chunk -> global (several query blocks accumulate)
+  const bool acc = gridDim.x > (unsigned)(BH * nsplit);
+  for (int64_t s = lo + tid; s < hi; s += kW2 * 64) {
+    const float v = gss[s - c0];
+    if (acc) atomicAdd(&a.g_self[bh * a.N + s], v);
+    else a.g_self[bh * a.N + s] = v;
+  }
+  for (int64_t pp = tid; 2 * pp < hi - c0; pp += kW2 * 64) {
+    const int64_t m0 = c0 + 2 * pp;
+    const int64_t p = (m0 - a.S) / 2;
+    if (m0 >= a.S && m0 >= lo && m0 + 1 < hi && p < a.P) {
+      const float v = gxs[pp];
+      if (acc) atomicAdd(&a.g_cross[bh * a.P + p], v);
+      else a.g_cross[bh * a.P + p] = v;
+    }
+  }
 }
 
 // -------------------------------------------------------------------- dispatch --
@@ -561,6 +677,21 @@ static void mfma_plan(const Shape& s, const RoundP& r, int64_t& base, int64_t& c
   int64_t c = (span + want - 1) / want;
   if (c < 1024) c = 1024;                               // keep partial records small
   c = (c + kTile - 1) / kTile * kTile;
+  chunk = c;
+  nsplit = (int)((span + c - 1) / c);
+}
+
+// Pass-2 chunks: multiples of the tile, at most kChunk2Max slots, about two workgroups
+// per CU over the grid.
+static void p2_plan(const Shape& s, const RoundP& r, int64_t& chunk, int& nsplit) {
+  const int64_t span = s.N + (r.S & 1);
+  const int64_t BH = (int64_t)s.B * s.Hkv;
+  const int64_t nqb = ((int64_t)s.G * r.W + kQB - 1) / kQB;
+  int64_t want = (512 + BH * nqb - 1) / (BH * nqb);
+  if (want < 1) want = 1;
+  int64_t c = (span + want - 1) / want;
+  c = (c + kT2 - 1) / kT2 * kT2;
+  if (c > kChunk2Max) c = kChunk2Max;
   chunk = c;
   nsplit = (int)((span + c - 1) / c);
 }
@@ -593,10 +724,16 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
     if (e == hipSuccess) e = launch_fill_zero(p2.g_cross, BH * r.P, st);
     if (e != hipSuccess) return e;
   }
+  int64_t chunk2;
+  int nsplit2;
+  p2_plan(s, r, chunk2, nsplit2);
+  const dim3 grid2((unsigned)(BH * nsplit2 * nqb));
   if (p2.n)
-    KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p2, base, p1.chunk);
+    KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, true>), grid2, dim3(kW2 * 64), 0, st, p2, base, chunk2, nsplit2,
+               (int)BH);
   else
-    KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p2, base, p1.chunk);
+    KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, false>), grid2, dim3(kW2 * 64), 0, st, p2, base, chunk2, nsplit2,
+               (int)BH);
   return hipGetLastError();
 }
 
