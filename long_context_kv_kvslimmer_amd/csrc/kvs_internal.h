@@ -60,9 +60,25 @@ hipError_t launch_merge(const Shape& s, const RoundP& r, const void* K, const vo
                         void* K_out, void* V_out, int32_t* n_out, int32_t* src_out, hipStream_t st);
 
 // ---- log-sum-exp combine of split partial records {m (log2 units), l, -, -, o[D]} ----
-// units: rows of `out` ([units, D]); lse (natural log) is nullable.
+// Optional operand pack for the bf16 MFMA pass 2 (written by the combine, read by pass 2):
+// per kv head, the window queries in blocks of 32 (one wave each), two 16-query halves;
+// for half q2 and 32-wide k step ks, 64 lanes x 16 bytes hold lane l = n + 16 g ->
+// head-dim chunk 4 ks + g of query 16 q2 + n, as Q (bf16), hi and lo bf16 parts of -2 O.
+// qc holds {||o||^2, -lse * log2(e)} per query.  Queries past GW are not written.
+struct PackP {
+  uint4* ops;          // [BH][nwb][2][3][KS][64]
+  float* qc;           // [BH][nwb * 32][2]
+  const void* Qw;      // bf16 [B, Hq, W, D]
+  int64_t nwb, GW;     // 32-query blocks per kv head, window queries per kv head
+  int Hkv, Hq, G, W;
+};
+__host__ __device__ inline int64_t pack_ops_index(int64_t bh, int64_t nwb, int64_t q, int which, int chunk, int KS) {
+  const int64_t wb = q >> 5, q2 = (q >> 4) & 1, n = q & 15;
+  return (((((bh * nwb + wb) * 2 + q2) * 3 + which) * KS + (chunk >> 2)) * 64) + n + 16 * (chunk & 3);
+}
+// units: rows of `out` ([units, D]); lse (natural log) is nullable; pack nullable.
 hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, float* lse, float* out,
-                          hipStream_t st);
+                          hipStream_t st, const PackP* pack = nullptr);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 

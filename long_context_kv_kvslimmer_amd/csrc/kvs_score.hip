@@ -125,9 +125,10 @@ __global__ __launch_bounds__(256) void pass1_valu_kernel(P1Args a) {
 constexpr int kMaxSplit = 1024;
 
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part, int nsplit, int D,
-                                                      float* __restrict__ lse, float* __restrict__ out) {
+                                                      float* __restrict__ lse, float* __restrict__ out, PackP pk) {
   __shared__ float wsh[kMaxSplit];
   __shared__ float red[128];
+  __shared__ float osh[128];
   const int64_t u = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t rs = D + 4;
@@ -164,8 +165,42 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
 #pragma unroll 8
     for (int s = 0; s < nsplit; ++s) acc = __builtin_fmaf(r[s * rs + 4 + d], wsh[s], acc);
     out[u * D + d] = acc / L;
+    if (pk.ops) osh[d] = acc / L;
   }
-  if (lse && tid == 0) lse[u] = (M + __log2f(L)) * kLn2;
+  const float lse_u = (M + __log2f(L)) * kLn2;
+  if (lse && tid == 0) lse[u] = lse_u;
+  if (pk.ops) {
+    // operands of the MFMA pass 2: Q, and -2 O as bf16 hi + lo, in lane order
+    __syncthreads();
+    const int64_t bh = u / pk.GW, q = u - bh * pk.GW;
+    const int nch = D / 8, KS = D / 32;
+    float on = 0.f;
+    if (tid < nch) {
+      const int64_t b = bh / pk.Hkv, hk = bh - b * pk.Hkv;
+      const bf16* qrow = static_cast<const bf16*>(pk.Qw) + ((b * pk.Hq + hk * pk.G) * (int64_t)pk.W + q) * D;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = osh[tid * 8 + 2 * j], x1 = osh[tid * 8 + 2 * j + 1];
+        on = __builtin_fmaf(x0, x0, __builtin_fmaf(x1, x1, on));
+        const float m0 = -2.f * x0, m1 = -2.f * x1;
+        const uint32_t h0 = f32_to_bf16_bits(m0), h1 = f32_to_bf16_bits(m1);
+        const uint32_t l0 = f32_to_bf16_bits(m0 - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_bits(m1 - __uint_as_float(h1 << 16));
+        hi[j] = h0 | (h1 << 16);
+        lo[j] = l0 | (l1 << 16);
+      }
+      pk.ops[pack_ops_index(bh, pk.nwb, q, 0, tid, KS)] = *reinterpret_cast<const uint4*>(qrow + tid * 8);
+      pk.ops[pack_ops_index(bh, pk.nwb, q, 1, tid, KS)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      pk.ops[pack_ops_index(bh, pk.nwb, q, 2, tid, KS)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    // ||o||^2 over the nch chunk threads (all inside the first wave)
+    on = group_sum<16>(on);
+    if (tid == 0) {   // lanes past nch contributed zeros
+      pk.qc[(bh * pk.nwb * 32 + q) * 2] = on;
+      pk.qc[(bh * pk.nwb * 32 + q) * 2 + 1] = -lse_u * kLog2e;
+    }
+  }
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -181,10 +216,12 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
 }
 
 hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, float* lse, float* out,
-                          hipStream_t st) {
+                          hipStream_t st, const PackP* pack) {
   if (units == 0) return hipSuccess;
   if (nsplit > kMaxSplit) return hipErrorInvalidValue;
-  KVS_LAUNCH("combine", combine_kernel, dim3(units), dim3(128), 0, st, part, nsplit, D, lse, out);
+  PackP pk{};
+  if (pack) pk = *pack;
+  KVS_LAUNCH("combine", combine_kernel, dim3(units), dim3(128), 0, st, part, nsplit, D, lse, out, pk);
   return hipGetLastError();
 }
 

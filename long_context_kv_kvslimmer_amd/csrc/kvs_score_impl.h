@@ -25,6 +25,9 @@ struct P2Args {
   const float* O;
   float* g_self;
   float* g_cross;
+  const uint4* ops;  // operand pack (MFMA pass 2 only)
+  const float* qc;
+  int64_t nwb;
   int64_t N, S, P, sb, sh, GW;
   int Hkv, Hq, G, W;
   float scale;

@@ -332,21 +332,25 @@ __global__ __launch_bounds__(kThreads, 1) void p1_mfma_kernel(P1Args a, int64_t 
 }
 
 // ------------------------------------------------------------------------- pass 2 --
-// Slot-per-lane layout: S[q, slot] = Q . K^T and R[q, slot] = (-2 O) . V^T + ||v||^2 + ||o||^2
-// on 32x32x16 MFMA, lane l holding slot l % 32 of the tile for 16 of the wave's 32 queries,
-// so the sum over queries stays in registers; the pair partner slot is one DPP xor-1 away.
+// S[q, slot] = Q . K^T and R[q, slot] = (-2 O) . V^T + ||o||^2 (+ ||v||^2) on 16x16x32 MFMA,
+// with the even and the odd slots of a 32-slot tile in separate products: lane l then
+// holds both slots of candidate pair l % 16 for 8 of the wave's 32 queries, so the pair
+// term needs no cross-lane exchange and the sums over queries are mostly in registers.
 //
 // A workgroup is four waves (128 queries) over one slot chunk; two workgroups share a CU.
 // K and V arrive by 16-byte buffer loads written straight into LDS (no register staging)
-// as 32-slot tiles in a four-deep ring: tile t is computed while t + 1 has landed and
-// t + 2, t + 3 are in flight.  Rows are unpadded; the 16-byte chunks of row r sit at
-// position c ^ swz(r), which keeps both the row reads of the MFMA operands and the tile
-// setup reads free of bank conflicts.  Per-slot sums over the four waves are folded into
-// LDS once per tile and written out at the end, so the loop issues no global stores.
+// as 32-slot tiles in a four-deep ring: tile t is computed while t + 1 .. t + 3 are in
+// flight.  A tile's LDS row R holds slot 2 (R % 16) + R / 16 (even slots first).  Rows are
+// unpadded; the 16-byte chunks of row r sit at position c ^ swz(r), which keeps the MFMA
+// operand reads free of bank conflicts.  ||v||^2 and v_m . v_{m+1} come from the
+// diagonals of Gram products of the V operand registers, so a tile needs no setup pass
+// and one barrier.  Each wave keeps its per-slot sums in LDS; the four waves' sums are
+// added and written once, at the end, so the loop issues no global stores.  The query
+// operands come pre-packed in lane order from the log-sum-exp combine.
 constexpr int kT2 = 32;              // slots per tile
 constexpr int kRing2 = 4;            // tile buffers
 constexpr int kW2 = 4;               // waves per workgroup
-constexpr int kChunk2Max = 1024;     // slots per workgroup at most
+constexpr int kChunk2Max = 512;      // slots per workgroup at most
 
 template <int D>
 struct Dma {
@@ -412,29 +416,24 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// LDS row R of a tile holds slot 2 (R % 16) + R / 16 of the tile.
+__device__ __forceinline__ int row_slot(int R) { return 2 * (R & 15) + (R >> 4); }
+
 // grid: one workgroup per (bh, slot chunk, query block), bh fastest so that the blocks of
 // one head land on one XCD.
 template <int D, bool HAS_N>
 __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t base, int64_t chunk, int nsplit,
                                                              int BH) {
-  using C = Cfg32<D>;
   using M = Dma<D>;
+  constexpr int KS = D / 32;                      // 32-wide k steps of 16x16x32 MFMA
   __shared__ __attribute__((aligned(1024))) uint8_t kr[kRing2 * M::TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t vr[kRing2 * M::TILEB];
-  __shared__ int32_t nr[kRing2 * kT2];            // slot counts as loaded
-  __shared__ float lgs[kRing2 * kT2];             // log2 n; -inf outside the chunk
-  __shared__ float vns[kRing2 * kT2];             // ||v||^2
-  __shared__ float dvs[kRing2 * (kT2 / 2)];       // ||v_m - v_{m+1}||^2
-  __shared__ float red_s[2 * kW2 * kT2];
-  __shared__ float red_x[2 * kW2 * (kT2 / 2)];
-  __shared__ float gss[kChunk2Max];
-  __shared__ float gxs[kChunk2Max / 2];
-  __shared__ __attribute__((aligned(16))) float qon[kQB];   // ||o_q||^2
-  __shared__ __attribute__((aligned(16))) float qnb[kQB];   // -lse_q in log2 units (-inf: padding)
+  __shared__ int32_t nr[kRing2 * kT2];            // slot counts as loaded (LDS-row order)
+  __shared__ float red_s[kW2 * kChunk2Max];       // per-wave sums over its queries, per slot
+  __shared__ float red_x[kW2 * (kChunk2Max / 2)]; // and per candidate pair
 
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c32 = lane & 31, h = lane >> 5;
-  const bool odd = (c32 & 1) != 0;
+  const int n16 = lane & 15, g4 = lane >> 4;
   const int64_t id = blockIdx.x;
   const int64_t bh = id % BH;
   const int64_t rest = id / BH;
@@ -460,24 +459,27 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
 #pragma unroll
     for (int j = 0; j < M::IPW; ++j) {
       const int u = j * kW2 + wv;
-      const int r = u * M::RPI + lane / M::CPR;
-      const int c = (lane % M::CPR) ^ swz<D>(r);
-      const uint32_t off = (uint32_t)((t0 + r - lo) * M::ROWB) + (uint32_t)(c << 4);
+      const int R = u * M::RPI + lane / M::CPR;
+      const int c = (lane % M::CPR) ^ swz<D>(R);
+      const uint32_t off = (uint32_t)((t0 + row_slot(R) - lo) * M::ROWB) + (uint32_t)(c << 4);
       dma16(rk, lds_addr(kr + buf * M::TILEB + u * 1024), off);
       dma16(rv, lds_addr(vr + buf * M::TILEB + u * 1024), off);
     }
     if (HAS_N && wv == 0 && lane < kT2) {
-      const uint32_t off = (uint32_t)((t0 + lane - lo) * 4);
+      const uint32_t off = (uint32_t)((t0 + row_slot(lane) - lo) * 4);
       dma4(rn, lds_addr(nr + buf * kT2), off);
     }
   };
-  // wait for every load of tile t + 1 given whether tile t + 2 was issued after it
-  auto wait_tile = [&](bool later) {
-    if (later) {
-      if (HAS_N && wv == 0) wait_vm<2 * M::IPW + 1>();
-      else wait_vm<2 * M::IPW>();
+  // wait for every load of a tile after which `later` (0..2) tiles were issued
+  auto wait_tile = [&](int later) {
+    if (HAS_N && wv == 0) {
+      if (later >= 2) wait_vm<2 * (2 * M::IPW + 1)>();
+      else if (later == 1) wait_vm<2 * M::IPW + 1>();
+      else wait_vm<0>();
     } else {
-      wait_vm<0>();
+      if (later >= 2) wait_vm<2 * (2 * M::IPW)>();
+      else if (later == 1) wait_vm<2 * M::IPW>();
+      else wait_vm<0>();
     }
   };
 
@@ -485,168 +487,140 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
   if (ntiles > 1) issue(1);
   if (ntiles > 2) issue(2);
 
-  // the wave's 32 queries as the A operand: Q and -2 O (hi + lo), row q0 + l % 32
-  const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + hk * a.G) * (int64_t)a.W) * D;
-  const float* Op = a.O + bh * a.GW * (int64_t)D;
-  const float* Lp = a.lse + bh * a.GW;
-  const int64_t qa = qb * kQB + wv * 32 + c32;
-  bf16x8_t qop[C::KS], ohi[C::KS], olo[C::KS];
-  load_rows32<D>(Qp, a.GW, qa, qop);
-  float on_a = 0.f;
+  // the wave's 32 queries as A operands (two 16-query blocks): lane l holds query
+  // 16 qb2 + l % 16, head-dim chunk 4 ks + l / 16 of Q and of -2 O (bf16 hi + lo), read
+  // from the operand pack in lane order (every load is 1 KB contiguous per wave); the
+  // result rows of the lane are queries 16 q2 + 4 (l / 16) + r.  Queries past the window
+  // (never written to the pack) are replaced by zeros and alpha = 0.
+  const int64_t wb = qb * (kQB / 32) + wv;
+  const int64_t wbl = wb < a.nwb ? wb : a.nwb - 1;     // blocks past the window: loads clamped, all masked
+  bf16x8_t qop[2][KS], ohi[2][KS], olo[2][KS];
+  float nbq[2][4];
+  f32x4_t onv[2];
+  {
+    const uint4* opb = a.ops + (bh * a.nwb + wbl) * 2 * 3 * KS * 64 + lane;
+    uint4 raw[2][3][KS];
+    float4 qcr[2][2];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    float o8[8];
+    for (int q2 = 0; q2 < 2; ++q2) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float ov = qa < a.GW ? Op[qa * D + ks * 16 + h * 8 + j] : 0.f;
-      on_a = __builtin_fmaf(ov, ov, on_a);
-      o8[j] = -2.f * ov;
+      for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) raw[q2][w][ks] = opb[((q2 * 3 + w) * KS + ks) * 64];
+      const float* qcp = a.qc + ((bh * a.nwb + wbl) * 32 + q2 * 16 + 4 * g4) * 2;
+      qcr[q2][0] = *reinterpret_cast<const float4*>(qcp);
+      qcr[q2][1] = *reinterpret_cast<const float4*>(qcp + 4);
     }
-    split_hi_lo(o8, ohi[ks], olo[ks]);
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const bool va = wb * 32 + q2 * 16 + n16 < a.GW;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 zero = make_uint4(0, 0, 0, 0);
+        qop[q2][ks] = as_bf16x8(va ? raw[q2][0][ks] : zero);
+        ohi[q2][ks] = as_bf16x8(va ? raw[q2][1][ks] : zero);
+        olo[q2][ks] = as_bf16x8(va ? raw[q2][2][ks] : zero);
+      }
+      const float c8[8] = {qcr[q2][0].x, qcr[q2][0].y, qcr[q2][0].z, qcr[q2][0].w,
+                           qcr[q2][1].x, qcr[q2][1].y, qcr[q2][1].z, qcr[q2][1].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool vc = wb * 32 + q2 * 16 + 4 * g4 + r < a.GW;
+        onv[q2][r] = vc ? c8[2 * r] : 0.f;
+        nbq[q2][r] = vc ? c8[2 * r + 1] : -INFINITY;
+      }
+    }
   }
-  on_a += __shfl_xor(on_a, 32, 64);
-  if (h == 0) {
-    qon[wv * 32 + c32] = on_a;
-    qnb[wv * 32 + c32] = qa < a.GW ? -Lp[qa] * kLog2e : -INFINITY;   // padded queries: alpha = 0
-  }
-  // result rows of this lane are queries 8 (i / 4) + 4 h + i % 4 of the wave's block
-  const float* on_row = qon + wv * 32 + 4 * h;
-  const float* nb_row = qnb + wv * 32 + 4 * h;
   const float cs = a.scale * kLog2e;
-
-  // per-tile setup of tile t (landed): ||v||^2, ||v_m - v_{m+1}||^2 and log2 n per slot
-  auto setup = [&](int t) {
-    const int buf = t % kRing2;
-    const uint8_t* V_ = vr + buf * M::TILEB;
-    if (tid < (kT2 / 2) * M::CPR) {
-      const int pp = tid / M::CPR, ch = tid % M::CPR;
-      float x0[8], x1[8];
-      unpack<bf16>(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(2 * pp, ch)), x0);
-      unpack<bf16>(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(2 * pp + 1, ch)), x1);
-      float s0 = 0.f, s1 = 0.f, sd = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        s0 = __builtin_fmaf(x0[j], x0[j], s0);
-        s1 = __builtin_fmaf(x1[j], x1[j], s1);
-        const float d = x0[j] - x1[j];
-        sd = __builtin_fmaf(d, d, sd);
-      }
-      s0 = group_sum<M::CPR>(s0);
-      s1 = group_sum<M::CPR>(s1);
-      sd = group_sum<M::CPR>(sd);
-      if (ch == 0) {
-        vns[buf * kT2 + 2 * pp] = s0;
-        vns[buf * kT2 + 2 * pp + 1] = s1;
-        dvs[buf * (kT2 / 2) + pp] = sd;
-      }
-    }
-    if (tid < kT2) {
-      const int64_t s = c0 + (int64_t)t * kT2 + tid;
-      lgs[buf * kT2 + tid] = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)nr[buf * kT2 + tid]) : 0.f) : -INFINITY;
-    }
-  };
-
-  // fold the four waves' sums of tile t into the chunk's per-slot totals
-  auto fold = [&](int t) {
-    const int par = t & 1;
-    const int64_t t0 = c0 + (int64_t)t * kT2;
-    if (tid < kT2) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kW2; ++w) v += red_s[(par * kW2 + w) * kT2 + tid];
-      gss[t * kT2 + tid] = v;
-    } else if (tid < kT2 + kT2 / 2) {
-      const int pp = tid - kT2;
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kW2; ++w) v += red_x[(par * kW2 + w) * (kT2 / 2) + pp];
-      gxs[t * (kT2 / 2) + pp] = v;
-    }
-    (void)t0;
-  };
 
   auto compute = [&](int t) {
     const int buf = t % kRing2;
     const int64_t t0 = c0 + (int64_t)t * kT2;
     const uint8_t* K_ = kr + buf * M::TILEB;
     const uint8_t* V_ = vr + buf * M::TILEB;
-    const bool plain = !HAS_N && t0 >= lo && t0 + kT2 <= hi;
-    const float vn = vns[buf * kT2 + c32];
-    const float dvp = dvs[buf * (kT2 / 2) + (c32 >> 1)];
-    const float lgv = plain ? 0.f : lgs[buf * kT2 + c32];
-    f32x16_t st, rt;
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const float4 o4 = *reinterpret_cast<const float4*>(on_row + 8 * k4);
-      rt[4 * k4] = vn + o4.x;
-      rt[4 * k4 + 1] = vn + o4.y;
-      rt[4 * k4 + 2] = vn + o4.z;
-      rt[4 * k4 + 3] = vn + o4.w;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st[4 * k4 + r] = 0.f;
+    // log2 n of the lane's even and odd slot (-inf outside the chunk)
+    float lge = 0.f, lgo = 0.f;
+    if (HAS_N || t0 < lo || t0 + kT2 > hi) {
+      const int64_t se_ = t0 + 2 * n16;
+      lge = (se_ >= lo && se_ < hi) ? (HAS_N ? __log2f((float)nr[buf * kT2 + n16]) : 0.f) : -INFINITY;
+      lgo = (se_ + 1 >= lo && se_ + 1 < hi) ? (HAS_N ? __log2f((float)nr[buf * kT2 + 16 + n16]) : 0.f) : -INFINITY;
     }
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t se[2], so[2], re[2], ro[2], gee = z, goo = z, geo = z;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const int off = chunk_off<D>(c32, 2 * ks + h);
-      const bf16x8_t bk = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + off));
-      const bf16x8_t bv = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + off));
-      st = mfma32(qop[ks], bk, st);
-      rt = mfma32(ohi[ks], bv, rt);
-      rt = mfma32(olo[ks], bv, rt);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = 4 * ks + g4;
+      const bf16x8_t ke = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(n16, ch)));
+      const bf16x8_t ko = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(16 + n16, ch)));
+      const bf16x8_t ve = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(n16, ch)));
+      const bf16x8_t vo = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(16 + n16, ch)));
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        se[q2] = mfma(qop[q2][ks], ke, ks == 0 ? z : se[q2]);
+        so[q2] = mfma(qop[q2][ks], ko, ks == 0 ? z : so[q2]);
+        re[q2] = mfma(ohi[q2][ks], ve, ks == 0 ? onv[q2] : re[q2]);
+        ro[q2] = mfma(ohi[q2][ks], vo, ks == 0 ? onv[q2] : ro[q2]);
+        re[q2] = mfma(olo[q2][ks], ve, re[q2]);
+        ro[q2] = mfma(olo[q2][ks], vo, ro[q2]);
+      }
+      // Gram blocks of the tile's values (the V registers serve as both operands):
+      // their diagonals give ||v_m||^2, ||v_{m+1}||^2 and v_m . v_{m+1}
+      gee = mfma(ve, ve, gee);
+      goo = mfma(vo, vo, goo);
+      geo = mfma(ve, vo, geo);
     }
-    float al[16];
-    float gs = 0.f;
+    // diagonal element n of a 16x16 result sits in lane n + 16 (n / 4), register n % 4
+    const int rsel = n16 & 3;
+    auto pick = [&](const f32x4_t& g) {
+      return rsel == 0 ? g[0] : rsel == 1 ? g[1] : rsel == 2 ? g[2] : g[3];
+    };
+    const int src = n16 + 16 * (n16 >> 2);
+    const float vne = __shfl(pick(gee), src, 64);
+    const float vno = __shfl(pick(goo), src, 64);
+    const float veo = __shfl(pick(geo), src, 64);
+    const float dvp = vne + vno - 2.f * veo;          // ||v_m - v_{m+1}||^2
+    float gse = 0.f, gso = 0.f, gx = 0.f;
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const float4 n4 = *reinterpret_cast<const float4*>(nb_row + 8 * k4);
-      const float nb[4] = {n4.x, n4.y, n4.z, n4.w};
+    for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 4 * k4 + r;
-        al[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], cs, lgv + nb[r]));
-        const float tt = al[i] * fabsf(__builtin_fmaf(-2.f, al[i], 1.f));
-        gs = __builtin_fmaf(tt, __builtin_amdgcn_sqrtf(fabsf(rt[i])), gs);
+        const float ae = __builtin_amdgcn_exp2f(__builtin_fmaf(se[q2][r], cs, nbq[q2][r] + lge));
+        const float ao = __builtin_amdgcn_exp2f(__builtin_fmaf(so[q2][r], cs, nbq[q2][r] + lgo));
+        const float rre = re[q2][r] + vne, rro = ro[q2][r] + vno;
+        gse = __builtin_fmaf(ae * fabsf(__builtin_fmaf(-2.f, ae, 1.f)), __builtin_amdgcn_sqrtf(fabsf(rre)), gse);
+        gso = __builtin_fmaf(ao * fabsf(__builtin_fmaf(-2.f, ao, 1.f)), __builtin_amdgcn_sqrtf(fabsf(rro)), gso);
+        // ||v_m + v_{m+1} - 2 o||^2 = 2 r_m^2 + 2 r_{m+1}^2 - ||v_m - v_{m+1}||^2
+        const float rc = __builtin_fmaf(2.f, rre + rro, -dvp);
+        gx = __builtin_fmaf(ae * ao, __builtin_amdgcn_sqrtf(fabsf(rc)), gx);
       }
-    }
-    // pairs (even slot, odd slot) of the same query: the even lane takes queries i < 8,
-    // the odd lane queries i >= 8, each receiving the partner's alpha and r^2 by DPP
-    float gx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float sa = odd ? al[i] : al[i + 8], sr = odd ? rt[i] : rt[i + 8];
-      const float oa = odd ? al[i + 8] : al[i], orr = odd ? rt[i + 8] : rt[i];
-      const float pa = dpp<kDppXor1>(sa), pr = dpp<kDppXor1>(sr);
-      const float rc = __builtin_fmaf(2.f, orr + pr, -dvp);
-      gx = __builtin_fmaf(oa * pa, __builtin_amdgcn_sqrtf(fabsf(rc)), gx);
-    }
-    gx += dpp<kDppXor1>(gx);
-    gs += __shfl_xor(gs, 32, 64);
+    // sum the four lane groups (queries 4 g + r)
+    gse += __shfl_xor(gse, 16, 64);
+    gso += __shfl_xor(gso, 16, 64);
+    gx += __shfl_xor(gx, 16, 64);
+    gse += __shfl_xor(gse, 32, 64);
+    gso += __shfl_xor(gso, 32, 64);
     gx += __shfl_xor(gx, 32, 64);
-    if (h == 0) {
-      red_s[((t & 1) * kW2 + wv) * kT2 + c32] = gs;
-      if (!odd) red_x[((t & 1) * kW2 + wv) * (kT2 / 2) + (c32 >> 1)] = gx;
+    if (g4 == 0) {
+      red_s[wv * kChunk2Max + t * kT2 + 2 * n16] = gse;
+      red_s[wv * kChunk2Max + t * kT2 + 2 * n16 + 1] = gso;
+      red_x[wv * (kChunk2Max / 2) + t * (kT2 / 2) + n16] = gx;
     }
   };
 
-  wait_tile(ntiles > 1);     // tile 0 landed
-  __syncthreads();
-  setup(0);
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) wait_tile(t + 2 < ntiles);
+    wait_tile(ntiles - 1 - t < 2 ? ntiles - 1 - t : 2);   // tile t landed
     __syncthreads();
     if (t + 3 < ntiles) issue(t + 3);
-    if (t + 1 < ntiles) setup(t + 1);
-    if (t > 0) fold(t - 1);
     compute(t);
   }
-  __syncthreads();
-  fold(ntiles - 1);
   __syncthreads();
 
   // per-slot totals of the chunk -> global (several query blocks accumulate)
   const bool acc = gridDim.x > (unsigned)(BH * nsplit);
   for (int64_t s = lo + tid; s < hi; s += kW2 * 64) {
-    const float v = gss[s - c0];
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kW2; ++w) v += red_s[w * kChunk2Max + (s - c0)];
     if (acc) atomicAdd(&a.g_self[bh * a.N + s], v);
     else a.g_self[bh * a.N + s] = v;
   }
@@ -654,7 +628,9 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     const int64_t m0 = c0 + 2 * pp;
     const int64_t p = (m0 - a.S) / 2;
     if (m0 >= a.S && m0 >= lo && m0 + 1 < hi && p < a.P) {
-      const float v = gxs[pp];
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kW2; ++w) v += red_x[w * (kChunk2Max / 2) + pp];
       if (acc) atomicAdd(&a.g_cross[bh * a.P + p], v);
       else a.g_cross[bh * a.P + p] = v;
     }
@@ -696,12 +672,23 @@ static void p2_plan(const Shape& s, const RoundP& r, int64_t& chunk, int& nsplit
   nsplit = (int)((span + c - 1) / c);
 }
 
-size_t mfma_score_workspace_bytes(const Shape& s, const RoundP& r) {
+// Workspace: pass-1 partial records, then (256-byte aligned) the pass-2 operand pack.
+static size_t part_bytes(const Shape& s, const RoundP& r) {
   int64_t base, chunk;
   int nsplit;
   mfma_plan(s, r, base, chunk, nsplit);
   const int64_t GW = (int64_t)s.G * r.W;
-  return (size_t)s.B * s.Hkv * GW * nsplit * (s.D + 4) * sizeof(float);
+  return ((size_t)s.B * s.Hkv * GW * nsplit * (s.D + 4) * sizeof(float) + 255) / 256 * 256;
+}
+
+static int64_t pack_blocks(const Shape& s, const RoundP& r) { return ((int64_t)s.G * r.W + 31) / 32; }
+
+static size_t pack_ops_bytes(const Shape& s, const RoundP& r) {
+  return ((size_t)s.B * s.Hkv * pack_blocks(s, r) * 32 * 3 * s.D * 2 + 255) / 256 * 256;
+}
+
+size_t mfma_score_workspace_bytes(const Shape& s, const RoundP& r) {
+  return part_bytes(s, r) + pack_ops_bytes(s, r) + (size_t)s.B * s.Hkv * pack_blocks(s, r) * 32 * 2 * sizeof(float);
 }
 
 template <int D>
@@ -716,7 +703,17 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
     KVS_LAUNCH("score_pass1", (p1_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p1, base, ca);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st);
+  PackP pk;
+  pk.ops = const_cast<uint4*>(p2.ops);
+  pk.qc = const_cast<float*>(p2.qc);
+  pk.Qw = p1.Qw;
+  pk.nwb = p2.nwb;
+  pk.GW = p1.GW;
+  pk.Hkv = s.Hkv;
+  pk.Hq = s.Hq;
+  pk.G = s.G;
+  pk.W = r.W;
+  e = launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st, &pk);
   if (e != hipSuccess) return e;
   if (nqb > 1) {
     // several query blocks accumulate into the same sums
@@ -758,6 +755,9 @@ hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, con
   p1.scale = r.scale;
   mfma_plan(s, r, base, p1.chunk, p1.nsplit);
   P2Args p2;
+  p2.nwb = pack_blocks(s, r);
+  p2.ops = reinterpret_cast<const uint4*>(static_cast<uint8_t*>(ws) + part_bytes(s, r));
+  p2.qc = reinterpret_cast<const float*>(static_cast<uint8_t*>(ws) + part_bytes(s, r) + pack_ops_bytes(s, r));
   p2.K = K;
   p2.V = V;
   p2.n = n;
