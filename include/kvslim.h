@@ -133,7 +133,9 @@ kvs_status kvs_score(const kvs_cache* cache, kvs_dtype dtype,
  * ties to the smaller p.  The result is written to `sel_state` (an opaque device buffer of
  * kvs_workspace_bytes(KVS_OP_SEL_STATE) bytes) that kvs_merge_compact consumes; optionally
  * also as one flag byte per pair, selected[b, h, p] in {0, 1} ([B, H_kv, P], nullable).
- * `cos` may be NULL only when n_merge is 0 or P (nothing to choose).
+ * `cos` may be NULL only when n_merge is 0 or P (nothing to choose).  In that case, when
+ * neither `w` nor `selected` is requested, nothing is enqueued and `sel_state` is left
+ * untouched (kvs_merge_compact does not read it for such rounds).
  *
  * Weights (deep-dive 数学主线四, closed-form forward-only k*), for every pair p, m = S + 2p:
  *   A = g_self[m] - 2 g_cross[p] + g_self[m+1]
@@ -161,8 +163,9 @@ kvs_status kvs_merge_weights(const kvs_cache* cache, const kvs_round* round,
  * copied unchanged.  Slots keep their order: the output has T = N - M slots and
  * src_out[j] is the input slot of the first token of output slot j.
  *
- * `sel_state` comes from kvs_merge_weights for the same shapes and round; it may be NULL
- * when n_merge == P (every pair merges) or n_merge == 0 (plain copy).  The kernel
+ * `sel_state` comes from kvs_merge_weights for the same shapes and round; it is read only
+ * when 0 < n_merge < P (n_merge == P merges every pair, n_merge == 0 copies), and may be
+ * NULL otherwise.  The kernel
  * recomputes each pair's cosine with the same routine kvs_score uses and tests it
  * against the selection threshold.  `out` describes the K_out/V_out layout: same batch,
  * heads and head_dim as `cache`, n_slots == N - M, its own strides.  n_out and src_out

@@ -222,6 +222,7 @@ kvs_status kvs_merge_weights(const kvs_cache* cache, const kvs_round* round, con
   const size_t need = (size_t)s.B * s.Hkv * kvs::sel_stride_ints(r.P) * sizeof(int32_t);
   if (sel_state_bytes < need)
     return fail(KVS_ERR_WORKSPACE, "sel_state needs %zu bytes, got %zu", need, sel_state_bytes);
+  if (!choose && !w && !selected) return KVS_OK;   // nothing to choose, nothing requested
   return hip_status(kvs::launch_select(s, r, g_self, g_cross, choose ? cos : nullptr, w, selected,
                                        static_cast<int32_t*>(sel_state), static_cast<hipStream_t>(stream)),
                     "kvs_merge_weights");

@@ -242,13 +242,10 @@ hipError_t launch_merge(const Shape& s, const RoundP& r, const void* K, const vo
   a.Hkv = s.Hkv;
   a.total_waves = (int64_t)s.B * s.Hkv * a.nchunks;
   if (s.N == 0 || a.total_waves == 0) return hipSuccess;
-  // M == 0 and M == P need no threshold: M == P merges every pair; M == 0 is a partial
-  // round whose state selects nothing, or (without state) a copy done by a full-round
-  // launch over zero pairs.
-  bool partial = sel_state != nullptr && r.M != r.P;
-  if (sel_state == nullptr && r.M == 0 && r.P > 0) {
-    // plain copy: treat every pair as unselected via a partial launch is impossible without
-    // state, so copy with a zero-pair full round over the whole range instead.
+  // M == 0 and M == P need no threshold and never read the selection state: M == P
+  // merges every pair; M == 0 is a plain copy, done as a full round over zero pairs.
+  bool partial = r.M != 0 && r.M != r.P;
+  if (r.M == 0 && r.P > 0) {
     a.P = 0;
     a.S = 0;
     a.nchunks = 1;

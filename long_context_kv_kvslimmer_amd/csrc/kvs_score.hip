@@ -124,48 +124,69 @@ __global__ __launch_bounds__(256) void pass1_valu_kernel(P1Args a) {
 // splits issues independent loads.  Writes lse (natural log, nullable) and the row.
 constexpr int kMaxSplit = 1024;
 
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part, int nsplit, int D,
-                                                      float* __restrict__ lse, float* __restrict__ out, PackP pk) {
+// One 256-thread workgroup per unit (row of `out`).  All split maxima and sums are loaded
+// in one round, reduced in LDS to M and the weights f_s = exp2(m_s - M); then thread t
+// accumulates head-dim element t % D over its own share of the splits (all of its loads
+// issued together) and the shares are added in LDS in a fixed order, so results do not
+// depend on timing.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineUnroll = 16;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part, int nsplit, int D,
+                                                                 float* __restrict__ lse, float* __restrict__ out,
+                                                                 PackP pk) {
   __shared__ float wsh[kMaxSplit];
-  __shared__ float red[128];
-  __shared__ float osh[128];
+  __shared__ float red[kCombineThreads];
+  __shared__ float osh[kCombineThreads];
   const int64_t u = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t rs = D + 4;
   const float* r = part + u * nsplit * rs;
   float mx = -INFINITY;
-  for (int s = tid; s < nsplit; s += blockDim.x) {
+  for (int s = tid; s < nsplit; s += kCombineThreads) {
     const float v = r[s * rs];
     wsh[s] = v;
     mx = fmaxf(mx, v);
   }
-  red[tid] = mx;
+  mx = group_max<64>(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  for (int k = blockDim.x / 2; k > 0; k >>= 1) {
-    if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float L = 0.f;
-  for (int s = tid; s < nsplit; s += blockDim.x) {
-    const float f = wsh[s] == -INFINITY ? 0.f : exp2f(wsh[s] - M);
-    wsh[s] = f;
-    L = __builtin_fmaf(r[s * rs + 1], f, L);
+  for (int s = tid; s < nsplit; s += kCombineThreads) {
+    const float w = wsh[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wsh[s] - M);
+    wsh[s] = w;
+    L = __builtin_fmaf(r[s * rs + 1], w, L);
   }
-  red[tid] = L;
+  L = group_sum<64>(L);
   __syncthreads();
-  for (int k = blockDim.x / 2; k > 0; k >>= 1) {
-    if (tid < k) red[tid] += red[tid + k];
-    __syncthreads();
+  if ((tid & 63) == 0) red[4 + (tid >> 6)] = L;
+  __syncthreads();
+  L = (red[4] + red[5]) + (red[6] + red[7]);
+  // thread t: element d = t % D over splits s = g, g + ng, ... (g = t / D, ng = 256 / D)
+  const int d = tid % D, g = tid / D, ng = kCombineThreads / D;
+  float acc = 0.f;
+  for (int s0 = g; s0 < nsplit; s0 += ng * kCombineUnroll) {
+    float o[kCombineUnroll];
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k) {
+      const int s = s0 + k * ng;
+      o[k] = s < nsplit ? r[s * rs + 4 + d] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k) {
+      const int s = s0 + k * ng;
+      if (s < nsplit) acc = __builtin_fmaf(o[k], wsh[s], acc);
+    }
   }
-  L = red[0];
-  for (int d = tid; d < D; d += blockDim.x) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) acc = __builtin_fmaf(r[s * rs + 4 + d], wsh[s], acc);
-    out[u * D + d] = acc / L;
-    if (pk.ops) osh[d] = acc / L;
+  osh[tid] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float v = 0.f;
+    for (int k = 0; k < ng; ++k) v += osh[k * D + tid];
+    const float o = v / L;
+    out[u * D + tid] = o;
+    osh[tid] = o;   // each thread overwrites only its own slot after reading the shares
   }
   const float lse_u = (M + __log2f(L)) * kLn2;
   if (lse && tid == 0) lse[u] = lse_u;
@@ -194,9 +215,8 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
       pk.ops[pack_ops_index(bh, pk.nwb, q, 1, tid, KS)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       pk.ops[pack_ops_index(bh, pk.nwb, q, 2, tid, KS)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
-    // ||o||^2 over the nch chunk threads (all inside the first wave)
-    on = group_sum<16>(on);
-    if (tid == 0) {   // lanes past nch contributed zeros
+    on = group_sum<16>(on);   // lanes past nch contributed zeros
+    if (tid == 0) {
       pk.qc[(bh * pk.nwb * 32 + q) * 2] = on;
       pk.qc[(bh * pk.nwb * 32 + q) * 2 + 1] = -lse_u * kLog2e;
     }
@@ -219,9 +239,11 @@ hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, f
                           hipStream_t st, const PackP* pack) {
   if (units == 0) return hipSuccess;
   if (nsplit > kMaxSplit) return hipErrorInvalidValue;
+  if (D > 128) return hipErrorInvalidValue;
   PackP pk{};
   if (pack) pk = *pack;
-  KVS_LAUNCH("combine", combine_kernel, dim3(units), dim3(128), 0, st, part, nsplit, D, lse, out, pk);
+  KVS_LAUNCH("combine", combine_kernel, dim3((unsigned)units), dim3(kCombineThreads), 0, st, part, nsplit, D, lse, out,
+             pk);
   return hipGetLastError();
 }
 

@@ -63,290 +63,12 @@ __device__ __forceinline__ void split_hi_lo(const float* x, bf16x8_t& hi, bf16x8
 }
 
 // ------------------------------------------------------------------ tiling ----
-// A workgroup is two tile groups of four waves (512 threads).  Group g takes the tiles
-// c0 + (2 i + g) * 64 of the workgroup's slot chunk, so each SIMD runs two waves while the
-// workgroup still produces one partial record per query.  A wave owns 32 window queries
-// (32x32x16 MFMA), so the four waves of a group cover 128 queries.  Each group
-// double-buffers its tiles in LDS: tile i + 1 is committed from registers and tile i + 2
-// is fetched while tile i is computed, with one barrier per step.
-constexpr int kGroupWaves = 4;
-constexpr int kGroups = 2;
-constexpr int kGT = 64 * kGroupWaves;              // threads per group
-constexpr int kThreads = kGT * kGroups;            // 512
-
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
-struct Cfg32 {
-  static constexpr int KS = D / 16;     // 16-wide k steps over the head dim
-  static constexpr int DB = D / 32;     // 32-wide blocks of the head dim
-  static constexpr int PITCH = D + 16;  // bf16 per LDS row: rows 8 banks apart
-  static constexpr int CPR = D / 8;     // 16-byte chunks per row
-  static constexpr int PPP = kGT / CPR; // pairs per commit pass
-  static constexpr int NPASS = (kTile / 2) / PPP;
-  static constexpr int TILE = kTile * PITCH;   // bf16 per K (or V) tile
-};
-
-// Per-thread staging of one tile for its group: thread gt holds 16-byte chunk gt % CPR of
-// the K and V rows of pair p = pass * PPP + gt / CPR (rows 2p and 2p + 1).
-template <int D>
-struct Stage {
-  using C = Cfg32<D>;
-  uint4 k[C::NPASS][2], v[C::NPASS][2];
-  float lg[2];   // log2 n of rows 2 * (gt % 32) and + 1 ... (only lanes gt < 32)
-
-  __device__ __forceinline__ void fetch(const bf16* Kp, const bf16* Vp, int64_t t0, int64_t lo, int64_t hi,
-                                        int gt) {
-    const int ch = gt % C::CPR;
-#pragma unroll
-    for (int ps = 0; ps < C::NPASS; ++ps)
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int row = 2 * (ps * C::PPP + gt / C::CPR) + r;
-        const int64_t s = t0 + row;
-        if (s >= lo && s < hi) {
-          k[ps][r] = load16(Kp + s * D + ch * 8);
-          v[ps][r] = load16(Vp + s * D + ch * 8);
-        } else {
-          k[ps][r] = v[ps][r] = make_uint4(0, 0, 0, 0);
-        }
-      }
-  }
-};
-
-template <int D>
-__device__ __forceinline__ void commit_rows(const Stage<D>& st, bf16* Kt, bf16* Vt, int gt) {
-  using C = Cfg32<D>;
-  const int ch = gt % C::CPR;
-#pragma unroll
-  for (int ps = 0; ps < C::NPASS; ++ps)
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = 2 * (ps * C::PPP + gt / C::CPR) + r;
-      *reinterpret_cast<uint4*>(Kt + row * C::PITCH + ch * 8) = st.k[ps][r];
-      *reinterpret_cast<uint4*>(Vt + row * C::PITCH + ch * 8) = st.v[ps][r];
-    }
-}
-
-// log2 n (0 when there are no counts) of every slot of the tile, -inf outside [lo, hi).
-template <bool HAS_N>
-__device__ __forceinline__ void tile_bias(const int32_t* np, int64_t t0, int64_t lo, int64_t hi, int gt, float* lgs) {
-  if (gt < kTile) {
-    const int64_t s = t0 + gt;
-    lgs[gt] = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)np[s]) : 0.f) : -INFINITY;
-  }
-}
-
-// Q rows as a 32x32x16 operand: lane l holds row[q][16 ks + 8 (l / 32) .. +7] of query q.
-template <int D>
-__device__ __forceinline__ void load_rows32(const bf16* Qp, int64_t GW, int64_t q, bf16x8_t (&op)[Cfg32<D>::KS]) {
-  const int h = (threadIdx.x & 63) >> 5;
-#pragma unroll
-  for (int ks = 0; ks < Cfg32<D>::KS; ++ks) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (q < GW) u = load16(Qp + q * D + ks * 16 + h * 8);
-    op[ks] = as_bf16x8(u);
-  }
-}
-
-// ------------------------------------------------------------------------- pass 1 --
-// grid: x = slot chunk, y = query block (128), z = (b, kv-head).  Partial records as the
-// VALU pass 1: {m (log2 units), l, -, -, o[D]} per (bh, query, chunk).
-template <int D, bool HAS_N>
-__global__ __launch_bounds__(kThreads, 1) void p1_mfma_kernel(P1Args a, int64_t base, CosArgs ca) {
-  using C = Cfg32<D>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[kGroups * 2 * 2 * C::TILE];
-  __shared__ __attribute__((aligned(16))) float lgs[kGroups * 2 * kTile];
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int grp = wv / kGroupWaves, gw = wv % kGroupWaves, gt = tid % kGT;
-  const int c32 = lane & 31, h = lane >> 5, G16 = lane >> 4, t16 = lane & 15;
-  const int64_t bh = blockIdx.z;
-  const int64_t b = bh / a.Hkv, hk = bh - b * a.Hkv;
-  const bf16* Kp = static_cast<const bf16*>(a.K) + b * a.sb + hk * a.sh;
-  const bf16* Vp = static_cast<const bf16*>(a.V) + b * a.sb + hk * a.sh;
-  const int32_t* np = HAS_N ? a.n + (b * a.sb + hk * a.sh) / D : nullptr;
-  const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + hk * a.G) * (int64_t)a.W) * D;
-
-  const int64_t q = (int64_t)blockIdx.y * kQB + gw * 32 + c32;
-  bf16x8_t qop[C::KS];
-  load_rows32<D>(Qp, a.GW, q, qop);
-
-  const float cs = a.scale * kLog2e;
-  float m = kNoMax, lsum = 0.f;
-  f32x16_t acc[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-
-  const int64_t c0 = base + (int64_t)blockIdx.x * a.chunk;
-  const int64_t c1 = c0 + a.chunk;
-  const int64_t lo = c0 > 0 ? c0 : 0;
-  const int64_t hi = c1 < a.N ? c1 : a.N;
-  const int64_t tend = hi;
-  const int ntiles = (int)((tend - c0 + kTile - 1) / kTile);
-  const int iters = (ntiles + 1) / 2;
-  const bool do_cos = ca.cos != nullptr && blockIdx.y == 0;
-  auto tile_of = [&](int i) { return c0 + (int64_t)(2 * i + grp) * kTile; };
-  auto Kt = [&](int s) { return smem + ((grp * 2 + s) * 2) * C::TILE; };
-  auto Vt = [&](int s) { return smem + ((grp * 2 + s) * 2 + 1) * C::TILE; };
-  auto Lg = [&](int s) { return lgs + (grp * 2 + s) * kTile; };
-
-  // commit one staged tile; the cosine of its candidate pairs comes from the staged rows
-  auto commit = [&](const Stage<D>& st, int s, int64_t t0) {
-    commit_rows<D>(st, Kt(s), Vt(s), gt);
-    tile_bias<HAS_N>(np, t0, lo, hi, gt, Lg(s));
-    if (do_cos) {
-#pragma unroll
-      for (int ps = 0; ps < C::NPASS; ++ps) {
-        float k0[8], k1[8];
-        unpack<bf16>(st.k[ps][0], k0);
-        unpack<bf16>(st.k[ps][1], k1);
-        const float cv = pair_cos<8, C::CPR>(k0, k1);
-        const int64_t m0 = t0 + 2 * (ps * C::PPP + gt / C::CPR);
-        const int64_t p = (m0 - ca.S) / 2;
-        if (gt % C::CPR == 0 && m0 >= ca.S && p < ca.P && m0 >= lo && m0 + 1 < hi) ca.cos[bh * ca.P + p] = cv;
-      }
-    }
-  };
-
-  auto compute = [&](int s, int64_t t0) {
-    const bf16* K_ = Kt(s);
-    const bf16* V_ = Vt(s);
-    const float* L_ = Lg(s);
-    const bool plain = !HAS_N && t0 >= lo && t0 + kTile <= hi;   // every slot valid, count 1
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      // S^T = K . Q^T for 32 slots: lane holds slots 32 sb + 8 (i / 4) + 4 h + i % 4 of query c32
-      f32x16_t st;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st[i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8_t ak = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + (sb * 32 + c32) * C::PITCH + ks * 16 + h * 8));
-        st = mfma32(ak, qop[ks], st);
-      }
-      float e[16];
-      float mx = kNoMax;
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const float4 l4 = plain ? make_float4(0.f, 0.f, 0.f, 0.f)
-                                : *reinterpret_cast<const float4*>(L_ + sb * 32 + k4 * 8 + h * 4);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[k4 * 4 + r] = __builtin_fmaf(st[k4 * 4 + r], cs, lv[r]);
-          mx = fmaxf(mx, e[k4 * 4 + r]);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (mx > m) {   // rescale only when the running max grows (finite sentinel: no NaN paths)
-        const float corr = __builtin_amdgcn_exp2f(m - mx);
-        lsum *= corr;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[db] *= corr;
-        m = mx;
-      }
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(e[i] - m);
-        lsum += p[i];
-      }
-      // O^T += V^T . P^T in two 16-slot k steps; k index (h, j) <-> slot
-      // 32 sb + 16 ks + 8 (j / 4) + 4 h + j % 4, i.e. the lane's own p[8 ks + j]
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8_t phi, plo;
-        split_hi_lo(p + 8 * ks, phi, plo);
-        // transposed read: source lane i = lane % 16 points at row r0 + i / 4 (and + 8),
-        // columns 32 db + 16 (G16 % 2) + 4 (i % 4); lane t receives column + t of 4 rows
-        const int r0 = sb * 32 + ks * 16 + 4 * h + (t16 >> 2);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-          const int col = db * 32 + 16 * (G16 & 1) + 4 * (t16 & 3);
-          const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(V_ + r0 * C::PITCH + col));
-          const bf16x4_t v1 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(V_ + (r0 + 8) * C::PITCH + col));
-          const bf16x8_t vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[db] = mfma32(vop, phi, acc[db]);
-          acc[db] = mfma32(vop, plo, acc[db]);
-        }
-      }
-    }
-  };
-
-  Stage<D> stg;
-  if (tile_of(0) < tend) {
-    stg.fetch(Kp, Vp, tile_of(0), lo, hi, gt);
-    commit(stg, 0, tile_of(0));
-  }
-  if (tile_of(1) < tend) stg.fetch(Kp, Vp, tile_of(1), lo, hi, gt);
-  for (int i = 0; i < iters; ++i) {
-    __syncthreads();
-    if (tile_of(i + 1) < tend) commit(stg, (i + 1) & 1, tile_of(i + 1));
-    if (tile_of(i + 2) < tend) stg.fetch(Kp, Vp, tile_of(i + 2), lo, hi, gt);
-    if (tile_of(i) < tend) compute(i & 1, tile_of(i));
-  }
-
-  // merge the two groups' running states through LDS, then write the partial record
-  float l = lsum + __shfl_xor(lsum, 32, 64);
-  __syncthreads();
-  float* xo = reinterpret_cast<float*>(smem);            // [128 queries][D]
-  float* xm = xo + kQB * D;                              // [128] max, [128] sum
-  const int qi = gw * 32 + c32;
-  if (grp == 1) {
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xo[qi * D + db * 32 + (i >> 2) * 8 + h * 4 + (i & 3)] = acc[db][i];
-    if (h == 0) {
-      xm[qi] = m;
-      xm[kQB + qi] = l;
-    }
-  }
-  __syncthreads();
-  if (grp == 0 && q < a.GW) {
-    const float m1 = xm[qi], l1 = xm[kQB + qi];
-    const float M = fmaxf(m, m1);
-    const float f0 = __builtin_amdgcn_exp2f(m - M), f1 = __builtin_amdgcn_exp2f(m1 - M);
-    float* rec = a.part + ((bh * a.GW + q) * a.nsplit + blockIdx.x) * (int64_t)(D + 4);
-    if (h == 0) {
-      rec[0] = M;
-      rec[1] = l * f0 + l1 * f1;
-    }
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int d = db * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-        rec[4 + d] = acc[db][i] * f0 + xo[qi * D + d] * f1;
-      }
-  }
-}
-
-// ------------------------------------------------------------------------- pass 2 --
-// S[q, slot] = Q . K^T and R[q, slot] = (-2 O) . V^T + ||o||^2 (+ ||v||^2) on 16x16x32 MFMA,
-// with the even and the odd slots of a 32-slot tile in separate products: lane l then
-// holds both slots of candidate pair l % 16 for 8 of the wave's 32 queries, so the pair
-// term needs no cross-lane exchange and the sums over queries are mostly in registers.
-//
-// A workgroup is four waves (128 queries) over one slot chunk; two workgroups share a CU.
-// K and V arrive by 16-byte buffer loads written straight into LDS (no register staging)
-// as 32-slot tiles in a four-deep ring: tile t is computed while t + 1 .. t + 3 are in
-// flight.  A tile's LDS row R holds slot 2 (R % 16) + R / 16 (even slots first).  Rows are
-// unpadded; the 16-byte chunks of row r sit at position c ^ swz(r), which keeps the MFMA
-// operand reads free of bank conflicts.  ||v||^2 and v_m . v_{m+1} come from the
-// diagonals of Gram products of the V operand registers, so a tile needs no setup pass
-// and one barrier.  Each wave keeps its per-slot sums in LDS; the four waves' sums are
-// added and written once, at the end, so the loop issues no global stores.  The query
-// operands come pre-packed in lane order from the log-sum-exp combine.
 constexpr int kT2 = 32;              // slots per tile
 constexpr int kRing2 = 4;            // tile buffers
 constexpr int kW2 = 4;               // waves per workgroup
@@ -416,6 +138,305 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Q rows as a 32x32x16 operand: lane l holds row[q][16 ks + 8 (l / 32) .. +7] of query q.
+template <int D>
+__device__ __forceinline__ void load_rows32(const bf16* Qp, int64_t GW, int64_t q, bf16x8_t (&op)[D / 16]) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (q < GW) u = load16(Qp + q * D + ks * 16 + h * 8);
+    op[ks] = as_bf16x8(u);
+  }
+}
+
+// Maximum of x over lanes l and l ^ 32 (the two halves of a 32x32 result column).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ------------------------------------------------------------------------- pass 1 --
+// Flash-style statistics of the window queries over one slot chunk.  A workgroup is two
+// tile groups of four waves (512 threads, one per CU); group g streams the g-th half of
+// the chunk through its own four-deep LDS ring of 32-slot tiles (16-byte buffer loads
+// written straight to LDS, rows XOR-swizzled, natural slot order), and the two groups'
+// softmax states are merged through LDS into one partial record per query at the end.
+// A wave owns 32 window queries on 32x32x16 MFMA in transposed form, S^T = K . Q^T, so
+// each lane's accumulators belong to one query.  The QK product of tile t + 1 is issued
+// before the softmax of tile t so that the matrix cores run while the vector units work.
+// The running maximum is raised only when it grows by more than 2^8 (P <= 256 in
+// between), which makes rescales of the output accumulators rare.  P is split into bf16
+// hi + lo parts; O^T += V^T . P^T reads V^T with LDS transpose reads.
+constexpr int kGroupWaves = 4;
+constexpr int kGroups = 2;
+constexpr int kGT = 64 * kGroupWaves;              // threads per group
+constexpr int kThreads = kGT * kGroups;            // 512
+constexpr float kLazyMax = 8.f;                    // log2 headroom of the running maximum
+
+// grid: one workgroup per (bh, slot chunk, query block), bh fastest.  Partial records
+// {m (log2 units), l, -, -, o[D]} per (bh, query, chunk).
+template <int D, bool HAS_N>
+__global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a, int64_t base, CosArgs ca, int BH) {
+  using M = Dma<D>;
+  constexpr int KS = D / 16;    // 16-wide k steps over the head dim
+  constexpr int DB = D / 32;    // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(1024))) uint8_t kr[kGroups * kRing2 * M::TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vr[kGroups * kRing2 * M::TILEB];
+  __shared__ __attribute__((aligned(16))) int32_t nr[kGroups * kRing2 * kT2];
+  __shared__ float xm[2 * kQB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv / kGroupWaves, gw = wv % kGroupWaves, gt = tid % kGT;
+  const int c32 = lane & 31, h = lane >> 5, G16 = lane >> 4, t16 = lane & 15;
+  const int64_t id = blockIdx.x;
+  const int64_t bh = id % BH, rest = id / BH;
+  const int64_t split = rest % a.nsplit, qb = rest / a.nsplit;
+  const int64_t b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const int64_t hoff = b * a.sb + hk * a.sh;
+  const int32_t* np = HAS_N ? a.n + hoff / D : nullptr;
+
+  // the two halves of the chunk; group 0's half is never shorter than group 1's
+  const int64_t c0 = base + split * a.chunk, half = a.chunk / kGroups;
+  auto tiles_of = [&](int g) {
+    const int64_t s0 = c0 + g * half;
+    const int64_t l0 = s0 > 0 ? s0 : 0, h0 = s0 + half < a.N ? s0 + half : a.N;
+    return h0 > l0 ? (int)((h0 - s0 + kT2 - 1) / kT2) : 0;
+  };
+  const int nt0 = tiles_of(0);
+  const int64_t g0 = c0 + grp * half;
+  const int64_t lo = g0 > 0 ? g0 : 0;
+  const int64_t hi = g0 + half < a.N ? g0 + half : a.N;
+  const int nt = tiles_of(grp);
+  const uint32_t span = hi > lo ? (uint32_t)(hi - lo) : 0u;
+  const u32x4_t rk = make_rsrc(static_cast<const bf16*>(a.K) + hoff + (hi > lo ? lo : 0) * D, span * M::ROWB);
+  const u32x4_t rv = make_rsrc(static_cast<const bf16*>(a.V) + hoff + (hi > lo ? lo : 0) * D, span * M::ROWB);
+  const u32x4_t rn = make_rsrc(HAS_N ? static_cast<const void*>(np + (hi > lo ? lo : 0)) : a.K, HAS_N ? span * 4u : 0u);
+  uint8_t* kr_g = kr + grp * kRing2 * M::TILEB;
+  uint8_t* vr_g = vr + grp * kRing2 * M::TILEB;
+  int32_t* nr_g = nr + grp * kRing2 * kT2;
+
+  auto issue = [&](int t) {
+    const int buf = t % kRing2;
+    const int64_t t0 = g0 + (int64_t)t * kT2;
+#pragma unroll
+    for (int j = 0; j < M::IPW; ++j) {
+      const int u = j * kGroupWaves + gw;
+      const int R = u * M::RPI + lane / M::CPR;
+      const int c = (lane % M::CPR) ^ swz<D>(R);
+      const uint32_t off = (uint32_t)((t0 + R - lo) * M::ROWB) + (uint32_t)(c << 4);
+      dma16(rk, lds_addr(kr_g + buf * M::TILEB + u * 1024), off);
+      dma16(rv, lds_addr(vr_g + buf * M::TILEB + u * 1024), off);
+    }
+    if (HAS_N && gw == 0 && lane < kT2) dma4(rn, lds_addr(nr_g + buf * kT2), (uint32_t)((t0 + lane - lo) * 4));
+  };
+  auto wait_tile = [&](int later) {   // tiles of this group issued after the awaited one: 0..2
+    if (HAS_N && gw == 0) {
+      if (later >= 2) wait_vm<2 * (2 * M::IPW + 1)>();
+      else if (later == 1) wait_vm<2 * M::IPW + 1>();
+      else wait_vm<0>();
+    } else {
+      if (later >= 2) wait_vm<2 * (2 * M::IPW)>();
+      else if (later == 1) wait_vm<2 * M::IPW>();
+      else wait_vm<0>();
+    }
+  };
+
+  if (nt > 0) issue(0);
+  if (nt > 1) issue(1);
+  if (nt > 2) issue(2);
+
+  const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + hk * a.G) * (int64_t)a.W) * D;
+  const int64_t q = qb * kQB + gw * 32 + c32;
+  bf16x8_t qop[KS];
+  load_rows32<D>(Qp, a.GW, q, qop);
+
+  const float cs = a.scale * kLog2e;
+  float m = kNoMax, lsum = 0.f;
+  f32x16_t acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  const bool do_cos = ca.cos != nullptr && qb == 0;
+
+  // S^T = K . Q^T of tile t: lane holds slots 8 (i / 4) + 4 h + i % 4 of query c32
+  auto qk = [&](int t) {
+    const uint8_t* K_ = kr_g + (t % kRing2) * M::TILEB;
+    f32x16_t st;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      st = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(c32, 2 * ks + h))), qop[ks], st);
+    return st;
+  };
+
+  // adjacent-key cosine of the tile's candidate pairs (shared routine of the merge pass)
+  auto cosines = [&](int t) {
+    const uint8_t* K_ = kr_g + (t % kRing2) * M::TILEB;
+    const int64_t t0 = g0 + (int64_t)t * kT2;
+    if (gt < (kT2 / 2) * M::CPR) {
+      const int pp = gt / M::CPR, ch = gt % M::CPR;
+      float k0[8], k1[8];
+      unpack<bf16>(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(2 * pp, ch)), k0);
+      unpack<bf16>(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(2 * pp + 1, ch)), k1);
+      const float cv = pair_cos<8, M::CPR>(k0, k1);
+      const int64_t m0 = t0 + 2 * pp;
+      const int64_t p = (m0 - ca.S) / 2;
+      if (ch == 0 && m0 >= ca.S && p < ca.P && m0 >= lo && m0 + 1 < hi) ca.cos[bh * ca.P + p] = cv;
+    }
+  };
+
+  auto softmax_pv = [&](int t, const f32x16_t& st) {
+    const int buf = t % kRing2;
+    const int64_t t0 = g0 + (int64_t)t * kT2;
+    const uint8_t* V_ = vr_g + buf * M::TILEB;
+    const bool plain = !HAS_N && t0 >= lo && t0 + kT2 <= hi;
+    float e[16];
+    float mx;
+    if (plain) {
+      mx = st[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st[i]);
+      mx = max_halves(mx) * cs;
+    } else {
+      mx = -INFINITY;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        int4 n4 = make_int4(1, 1, 1, 1);
+        if (HAS_N) n4 = *reinterpret_cast<const int4*>(nr_g + buf * kT2 + 8 * k4 + 4 * h);
+        const int nn[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t s = t0 + 8 * k4 + 4 * h + r;
+          const float lg = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)nn[r]) : 0.f) : -INFINITY;
+          e[4 * k4 + r] = __builtin_fmaf(st[4 * k4 + r], cs, lg);
+          mx = fmaxf(mx, e[4 * k4 + r]);
+        }
+      }
+      mx = max_halves(mx);
+    }
+    if (mx > m + kLazyMax) {   // raise the reference only when P could exceed 2^8
+      const float corr = __builtin_amdgcn_exp2f(m - mx);
+      lsum *= corr;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= corr;
+      m = mx;
+    }
+    float p[16];
+    if (plain) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], cs, -m));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(e[i] - m);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lsum += p[i];
+    // O^T += V^T . P^T in two 16-slot k steps; k index (h, j) <-> slot
+    // 16 ks + 8 (j / 4) + 4 h + j % 4, i.e. the lane's own p[8 ks + j]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t phi, plo;
+      split_hi_lo(p + 8 * ks, phi, plo);
+      // transposed read: source lane i = lane % 16 points at row r0 + i / 4 (and + 8),
+      // columns 32 db + 16 (G16 % 2) + 4 (i % 4); lane t receives column + t of 4 rows
+      const int r0 = ks * 16 + 4 * h + (t16 >> 2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+        const int col = db * 32 + 16 * (G16 & 1) + 4 * (t16 & 3);
+        const int cb = (col & 7) * 2;
+        const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4*)(V_ + chunk_off<D>(r0, col >> 3) + cb));
+        const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4*)(V_ + chunk_off<D>(r0 + 8, col >> 3) + cb));
+        const bf16x8_t vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[db] = mfma32(vop, phi, acc[db]);
+        acc[db] = mfma32(vop, plo, acc[db]);
+      }
+    }
+  };
+
+  if (nt > 0) wait_tile(nt - 1 < 2 ? nt - 1 : 2);
+  __syncthreads();
+  f32x16_t s_cur;
+  if (nt > 0) s_cur = qk(0);
+  for (int t = 0; t < nt0; ++t) {
+    const bool act = t < nt;
+    if (act && t + 1 < nt) {
+      const int issued = t + 2 < nt - 1 ? t + 2 : nt - 1;
+      wait_tile(issued - (t + 1));
+    }
+    __syncthreads();
+    if (act) {
+      if (t + 3 < nt) issue(t + 3);
+      if (do_cos) cosines(t);
+      f32x16_t s_next;
+      if (t + 1 < nt) s_next = qk(t + 1);
+      softmax_pv(t, s_cur);
+      s_cur = s_next;
+    }
+  }
+
+  // merge the two groups' running states through LDS, then write the partial record
+  const float l = sum_halves(lsum);
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(kr);              // [128 queries][D]
+  const int qi = gw * 32 + c32;
+  if (kGroups == 2 && grp == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xo[qi * D + db * 32 + (i >> 2) * 8 + h * 4 + (i & 3)] = acc[db][i];
+    if (h == 0) {
+      xm[qi] = m;
+      xm[kQB + qi] = l;
+    }
+  }
+  __syncthreads();
+  if (grp == 0 && q < a.GW) {
+    const float m1 = kGroups == 2 ? xm[qi] : kNoMax, l1 = kGroups == 2 ? xm[kQB + qi] : 0.f;
+    const float Mx = fmaxf(m, m1);
+    const float f0 = __builtin_amdgcn_exp2f(m - Mx), f1 = __builtin_amdgcn_exp2f(m1 - Mx);
+    float* rec = a.part + ((bh * a.GW + q) * a.nsplit + split) * (int64_t)(D + 4);
+    if (h == 0) {
+      rec[0] = Mx;
+      rec[1] = l * f0 + l1 * f1;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = db * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+        rec[4 + d] = kGroups == 2 ? acc[db][i] * f0 + xo[qi * D + d] * f1 : acc[db][i] * f0;
+      }
+  }
+}
+
+// ------------------------------------------------------------------------- pass 2 --
+// S[q, slot] = Q . K^T and R[q, slot] = (-2 O) . V^T + ||o||^2 (+ ||v||^2) on 16x16x32 MFMA,
+// with the even and the odd slots of a 32-slot tile in separate products: lane l then
+// holds both slots of candidate pair l % 16 for 8 of the wave's 32 queries, so the pair
+// term needs no cross-lane exchange and the sums over queries are mostly in registers.
+//
+// A workgroup is four waves (128 queries) over one slot chunk; two workgroups share a CU.
+// K and V arrive by 16-byte buffer loads written straight into LDS (no register staging)
+// as 32-slot tiles in a four-deep ring: tile t is computed while t + 1 .. t + 3 are in
+// flight.  A tile's LDS row R holds slot 2 (R % 16) + R / 16 (even slots first).  Rows are
+// unpadded; the 16-byte chunks of row r sit at position c ^ swz(r), which keeps the MFMA
+// operand reads free of bank conflicts.  ||v||^2 and v_m . v_{m+1} come from the
+// diagonals of Gram products of the V operand registers, so a tile needs no setup pass
+// and one barrier.  Each wave keeps its per-slot sums in LDS; the four waves' sums are
+// added and written once, at the end, so the loop issues no global stores.  The query
+// operands come pre-packed in lane order from the log-sum-exp combine.
 // LDS row R of a tile holds slot 2 (R % 16) + R / 16 of the tile.
 __device__ __forceinline__ int row_slot(int R) { return 2 * (R & 15) + (R >> 4); }
 
@@ -651,7 +672,7 @@ static void mfma_plan(const Shape& s, const RoundP& r, int64_t& base, int64_t& c
   int64_t want = (512 + BH * nqb - 1) / (BH * nqb);   // target chunks per (bh, query block)
   if (want < 1) want = 1;
   int64_t c = (span + want - 1) / want;
-  if (c < 1024) c = 1024;                               // keep partial records small
+  if (c < 512 * kGroups) c = 512 * kGroups;             // keep partial records small
   c = (c + kTile - 1) / kTile * kTile;
   chunk = c;
   nsplit = (int)((span + c - 1) / c);
@@ -696,11 +717,11 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
                                 const CosArgs& ca, int64_t base, float* lse, float* O, hipStream_t st) {
   const int64_t BH = (int64_t)s.B * s.Hkv;
   const int nqb = (int)((p1.GW + kQB - 1) / kQB);
-  const dim3 grid(p1.nsplit, nqb, (unsigned)BH);
+  const dim3 grid((unsigned)(BH * p1.nsplit * nqb));
   if (p1.n)
-    KVS_LAUNCH("score_pass1", (p1_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p1, base, ca);
+    KVS_LAUNCH("score_pass1", (p1_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p1, base, ca, (int)BH);
   else
-    KVS_LAUNCH("score_pass1", (p1_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p1, base, ca);
+    KVS_LAUNCH("score_pass1", (p1_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p1, base, ca, (int)BH);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PackP pk;
