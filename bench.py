@@ -238,7 +238,7 @@ def main():
         sets.append((K[None].contiguous(), V[None].contiguous(), Qw[None].contiguous(), q[None].contiguous()))
     bufs = pipeline.alloc_round(sets[0][0], Hq, W, S, R, M, want_flags=False)
     dec_cache = L.cache_desc(bufs.K, Hq, T)
-    dec_ws = torch.empty(max(L.workspace_bytes(L.KVS_OP_DECODE, dec_cache, None), 16), dtype=torch.uint8, device=dev)
+    dec_ws = torch.zeros(max(L.workspace_bytes(L.KVS_OP_DECODE, dec_cache, None), 16), dtype=torch.uint8, device=dev)
     dec_out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     cache = L.cache_desc(sets[0][0], Hq, N)
     rnd = L.round_desc(W, S, R, M, 1.0 / math.sqrt(D))

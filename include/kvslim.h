@@ -187,6 +187,7 @@ kvs_status kvs_merge_compact(const kvs_cache* cache, kvs_dtype in_dtype,
  *   out[b, hq, :] = sum_j softmax_j(sm_scale * q[b, hq] . k_j + ln n_j) v_j
  * over the cache->n_slots slots of kv head hq / G.  q: [B, H_q, D] in `dtype`;
  * out: [B, H_q, D] fp32.  Requires N >= 1 and G = H_q / H_kv in {1, 2, 4, 8}.
+ * Workspace: kvs_workspace_bytes(KVS_OP_DECODE) bytes (split partial records).
  */
 kvs_status kvs_decode_attn(const kvs_cache* cache, kvs_dtype dtype,
                            const void* K, const void* V, const int32_t* n,

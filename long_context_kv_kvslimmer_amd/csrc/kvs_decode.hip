@@ -11,6 +11,7 @@
 // Groups are merged in LDS into one partial record per (query head, split); the shared
 // log-sum-exp combine turns the records into the output.
 #include "kvs_common.h"
+#include "kvs_dma.h"
 #include "kvs_internal.h"
 
 namespace kvs {
@@ -34,7 +35,7 @@ static void decode_plan(const Shape& s, int64_t& chunk, int& nsplit) {
   if (s.bf16) {
     const int64_t BH = (int64_t)s.B * s.Hkv;
     c = (N * BH + 511) / 512;
-    c = (c + 127) / 128 * 128;
+    c = (c + 31) / 32 * 32;
     if (c < 128) c = 128;
   } else {
     c = (N + 255) / 256;
@@ -197,63 +198,75 @@ constexpr int kDecBlock = 32;     // slots per wave step
 constexpr int kDecWaves = 4;
 constexpr float kDecNoMax = -1e30f;
 
-template <int D, bool HAS_N>
-struct DecBlock {
-  static constexpr int KB = D / 32;
-  static constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  static constexpr int VPL = kDecBlock * CPR / 64;       // V chunks per lane
-  uint4 k[2][KB];      // A operand of S^T: slot 16 sb + l % 16, d = 32 kb + 8 (l / 16)
-  uint4 v[VPL];        // V rows in row layout, staged to LDS
-  int4 n[2];           // counts of slots 16 sb + 4 (l / 16) + 0..3
-
-  __device__ __forceinline__ void fetch(const bf16* Kp, const bf16* Vp, const int32_t* np, int64_t t, int64_t end) {
-    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      int64_t row = t + sb * 16 + c16;
-      row = row < end ? row : end - 1;   // clamped rows are masked by the bias
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) k[sb][kb] = load16(Kp + row * D + kb * 32 + g * 8);
-      if (HAS_N) {
-        int64_t r0 = t + sb * 16 + g * 4;
-        if (r0 + 4 <= end) {
-          n[sb] = *reinterpret_cast<const int4*>(np + r0);
-        } else {
-          n[sb].x = r0 < end ? np[r0] : 1;
-          n[sb].y = r0 + 1 < end ? np[r0 + 1] : 1;
-          n[sb].z = r0 + 2 < end ? np[r0 + 2] : 1;
-          n[sb].w = r0 + 3 < end ? np[r0 + 3] : 1;
-        }
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < VPL; ++it) {
-      const int idx = it * 64 + lane;
-      int64_t row = t + idx / CPR;
-      row = row < end ? row : end - 1;
-      v[it] = load16(Vp + row * D + (idx % CPR) * 8);
-    }
-  }
-};
+// Workgroup = four waves over one slot chunk of one (batch, kv-head), two workgroups per
+// CU.  K and V arrive as 32-slot tiles by 16-byte buffer loads written straight into a
+// four-deep LDS ring (rows XOR-swizzled).  Every wave computes S^T = K . Q^T and the
+// softmax of the whole tile (the G heads are the N side of 16x16x32 MFMA, padded to 16)
+// and accumulates its own quarter of the head dimension of O^T += V^T . P^T.  The running
+// maximum is raised only when it grows by more than 2^8.  Each workgroup writes one
+// partial record per query head for the log-sum-exp combine.
+constexpr int kDecThreads = 256;
+constexpr float kDecLazy = 8.f;
 
 template <int D, int G, bool HAS_N>
-__global__ __launch_bounds__(64 * kDecWaves, 2) void decode_mfma_kernel(DecArgs a) {
-  constexpr int KB = D / 32, DB = D / 16, CPR = D / 8, PITCH = D + 16;
-  constexpr int VPL = DecBlock<D, HAS_N>::VPL;
-  __shared__ __attribute__((aligned(16))) bf16 vt[kDecWaves][kDecBlock * PITCH];
-  __shared__ float wm[kDecWaves][16], wl[kDecWaves][16];
-  __shared__ float wo[kDecWaves][16][D];
+__global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(DecArgs a, int BH) {
+  using M = Dma<D>;
+  constexpr int KB = D / 32;          // k steps of S^T
+  constexpr int DB = D / 16;          // 16-row blocks of O^T
+  constexpr int DBW = DB / 4;         // per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kRing2 * M::TILEB];   // K tiles, then V tiles
+  __shared__ __attribute__((aligned(16))) int32_t nr[kRing2 * kT2];
+  uint8_t* const kr = ring;
+  uint8_t* const vr = ring + kRing2 * M::TILEB;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  const int64_t bh = blockIdx.y;
+  const int64_t id = blockIdx.x;
+  const int64_t bh = id % BH, split = id / BH;
   const int64_t b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const bf16* Kp = static_cast<const bf16*>(a.K) + b * a.sb + h * a.sh;
-  const bf16* Vp = static_cast<const bf16*>(a.V) + b * a.sb + h * a.sh;
-  const int32_t* np = HAS_N ? a.n + (b * a.sb + h * a.sh) / D : nullptr;
-  const bf16* qp = static_cast<const bf16*>(a.q) + (b * a.Hq + h * G) * (int64_t)D;
+  const int64_t hoff = b * a.sb + h * a.sh;
+  const int64_t s0 = split * a.chunk;
+  const int64_t s1 = s0 + a.chunk < a.N ? s0 + a.chunk : a.N;
+  const int ntiles = (int)((s1 - s0 + kT2 - 1) / kT2);
+  const uint32_t span = (uint32_t)(s1 - s0);
+  const u32x4_t rk = make_rsrc(static_cast<const bf16*>(a.K) + hoff + s0 * D, span * M::ROWB);
+  const u32x4_t rv = make_rsrc(static_cast<const bf16*>(a.V) + hoff + s0 * D, span * M::ROWB);
+  const int32_t* np = HAS_N ? a.n + hoff / D + s0 : nullptr;
+  const u32x4_t rn = make_rsrc(HAS_N ? static_cast<const void*>(np) : a.K, HAS_N ? span * 4u : 0u);
+
+  auto issue = [&](int t) {
+    const int buf = t % kRing2;
+    const int64_t t0 = (int64_t)t * kT2;
+#pragma unroll
+    for (int j = 0; j < M::IPW; ++j) {
+      const int u = j * kW2 + wv;
+      const int R = u * M::RPI + lane / M::CPR;
+      const int c = (lane % M::CPR) ^ swz<D>(R);
+      const uint32_t off = (uint32_t)((t0 + R) * M::ROWB) + (uint32_t)(c << 4);
+      dma16(rk, lds_addr(kr + buf * M::TILEB + u * 1024), off);
+      dma16(rv, lds_addr(vr + buf * M::TILEB + u * 1024), off);
+    }
+    if (HAS_N && wv == 0 && lane < kT2) dma4(rn, lds_addr(nr + buf * kT2), (uint32_t)((t0 + lane) * 4));
+  };
+  auto wait_tile = [&](int later) {
+    if (HAS_N && wv == 0) {
+      if (later >= 2) wait_vm<2 * (2 * M::IPW + 1)>();
+      else if (later == 1) wait_vm<2 * M::IPW + 1>();
+      else wait_vm<0>();
+    } else {
+      if (later >= 2) wait_vm<2 * (2 * M::IPW)>();
+      else if (later == 1) wait_vm<2 * M::IPW>();
+      else wait_vm<0>();
+    }
+  };
+
+  issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
 
   // B operand of S^T: lane l holds q[head l % 16][d = 32 kb + 8 (l / 16) .. +7], zero padding
+  const bf16* qp = static_cast<const bf16*>(a.q) + (b * a.Hq + h * G) * (int64_t)D;
   dbf16x8_t qop[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -263,43 +276,39 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_mfma_kernel(DecArgs 
   }
   const float cs = a.scale * kLog2e;
   float m = kDecNoMax, lsum = 0.f;
-  df32x4_t acc[DB];
+  df32x4_t acc[DBW];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = df32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < DBW; ++i) acc[i] = df32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t s0 = (int64_t)blockIdx.x * a.chunk;
-  const int64_t s1 = min(a.N, s0 + a.chunk);
-  bf16* V_ = vt[wv];
-  DecBlock<D, HAS_N> cur, nxt;
-  int64_t t = s0 + (int64_t)wv * kDecBlock;
-  if (t < s1) cur.fetch(Kp, Vp, np, t, s1);
-  for (; t < s1; t += kDecWaves * kDecBlock) {
-    const int64_t tn = t + kDecWaves * kDecBlock;
-    if (tn < s1) nxt.fetch(Kp, Vp, np, tn, s1);
-    // stage V rows (row layout) in the wave's LDS tile
-#pragma unroll
-    for (int it = 0; it < VPL; ++it) {
-      const int idx = it * 64 + lane;
-      *reinterpret_cast<uint4*>(V_ + (idx / CPR) * PITCH + (idx % CPR) * 8) = cur.v[it];
-    }
+  for (int t = 0; t < ntiles; ++t) {
+    wait_tile(ntiles - 1 - t < 2 ? ntiles - 1 - t : 2);
+    __syncthreads();
+    if (t + 3 < ntiles) issue(t + 3);
+    const int buf = t % kRing2;
+    const uint8_t* K_ = kr + buf * M::TILEB;
+    const uint8_t* V_ = vr + buf * M::TILEB;
+    const int64_t t0 = s0 + (int64_t)t * kT2;
     // S^T = K . Q^T: lane holds slots 16 sb + 4 g + r of head c16
     df32x4_t st[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       st[sb] = df32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) st[sb] = d_mfma(d_as_bf16x8(cur.k[sb][kb]), qop[kb], st[sb]);
+      for (int kb = 0; kb < KB; ++kb)
+        st[sb] = d_mfma(d_as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(16 * sb + c16, 4 * kb + g))),
+                        qop[kb], st[sb]);
     }
     float e[8];
     float mx = kDecNoMax;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      const int ns[4] = {cur.n[sb].x, cur.n[sb].y, cur.n[sb].z, cur.n[sb].w};
+      int4 n4 = make_int4(1, 1, 1, 1);
+      if (HAS_N) n4 = *reinterpret_cast<const int4*>(nr + buf * kT2 + 16 * sb + 4 * g);
+      const int ns[4] = {n4.x, n4.y, n4.z, n4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t slot = t + sb * 16 + g * 4 + r;
-        float bias = 0.f;
-        if (HAS_N) bias = __log2f((float)ns[r]);
+        const int64_t slot = t0 + 16 * sb + 4 * g + r;
+        float bias = HAS_N ? __log2f((float)ns[r]) : 0.f;
         if (slot >= s1) bias = -INFINITY;
         e[sb * 4 + r] = __builtin_fmaf(st[sb][r], cs, bias);
         mx = fmaxf(mx, e[sb * 4 + r]);
@@ -307,11 +316,11 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_mfma_kernel(DecArgs 
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (mx > m) {
+    if (mx > m + kDecLazy) {
       const float corr = __builtin_amdgcn_exp2f(m - mx);
       lsum *= corr;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= corr;
+      for (int i = 0; i < DBW; ++i) acc[i] *= corr;
       m = mx;
     }
     float pv[8];
@@ -328,58 +337,42 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_mfma_kernel(DecArgs 
       phi[j] = hv;
       plo[j] = (__bf16)(pv[j] - (float)hv);
     }
-    __builtin_amdgcn_wave_barrier();
     // V^T operand by transposed reads: source lane i points at row 4 g + i / 4 (and + 16),
     // columns 16 db + 4 (i % 4); lane t receives column 16 db + t of four consecutive rows
     const int srow = 4 * g + (c16 >> 2);
     const int scol = 4 * (c16 & 3);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int i = 0; i < DBW; ++i) {
       typedef __attribute__((address_space(3))) dbf16x4_t lds_t;
-      const dbf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + srow * PITCH + db * 16 + scol));
+      const int col = (wv * DBW + i) * 16 + scol;
+      const int cb = (col & 7) * 2;
+      const dbf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + chunk_off<D>(srow, col >> 3) + cb));
       const dbf16x4_t v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + (srow + 16) * PITCH + db * 16 + scol));
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + chunk_off<D>(srow + 16, col >> 3) + cb));
       const dbf16x8_t vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[db] = d_mfma(vop, phi, acc[db]);
-      acc[db] = d_mfma(vop, plo, acc[db]);
+      acc[i] = d_mfma(vop, phi, acc[i]);
+      acc[i] = d_mfma(vop, plo, acc[i]);
     }
-    __builtin_amdgcn_wave_barrier();
-    cur = nxt;
   }
 
-  // merge the waves: per head c16, O^T rows d = 16 db + 4 g + r
+  // partial record per query head c16: {m, l, -, -, o[D]}, O^T rows d = 16 db + 4 g + r
   float l = lsum;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (g == 0) {
-    wm[wv][c16] = m;
-    wl[wv][c16] = l;
-  }
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wo[wv][c16][db * 16 + g * 4 + r] = acc[db][r];
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 64 * kDecWaves) {
-    const int hd = idx / D, d = idx % D;
-    float M = kDecNoMax;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, wm[w][hd]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(wm[w][hd] - M);
-      L = __builtin_fmaf(wl[w][hd], f, L);
-      O = __builtin_fmaf(wo[w][hd][d], f, O);
+  const int64_t nsplit = a.nsplit;
+  if (c16 < G) {
+    float* rec = a.part + ((bh * G + c16) * nsplit + split) * (int64_t)(D + 4);
+    if (wv == 0 && g == 0) {
+      rec[0] = m;
+      rec[1] = l;
     }
-    float* rec = a.part + ((bh * G + hd) * a.nsplit + blockIdx.x) * (int64_t)(D + 4);
-    rec[4 + d] = O;
-    if (d == 0) {
-      rec[0] = M;
-      rec[1] = L;
-    }
+#pragma unroll
+    for (int i = 0; i < DBW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rec[4 + (wv * DBW + i) * 16 + g * 4 + r] = acc[i][r];
   }
 }
+
 
 template <typename T, int D, int G>
 static hipError_t launch_dec_g(const DecArgs& a, const Shape& s, hipStream_t st) {
@@ -393,11 +386,12 @@ static hipError_t launch_dec_g(const DecArgs& a, const Shape& s, hipStream_t st)
 
 template <int D, int G>
 static hipError_t launch_dec_mfma_g(const DecArgs& a, const Shape& s, hipStream_t st) {
-  const dim3 grid(a.nsplit, (unsigned)(s.B * s.Hkv));
+  const int BH = s.B * s.Hkv;
+  const dim3 grid((unsigned)(a.nsplit * (int64_t)BH));
   if (a.n)
-    KVS_LAUNCH("decode", (decode_mfma_kernel<D, G, true>), grid, dim3(64 * kDecWaves), 0, st, a);
+    KVS_LAUNCH("decode", (decode_mfma_kernel<D, G, true>), grid, dim3(kDecThreads), 0, st, a, BH);
   else
-    KVS_LAUNCH("decode", (decode_mfma_kernel<D, G, false>), grid, dim3(64 * kDecWaves), 0, st, a);
+    KVS_LAUNCH("decode", (decode_mfma_kernel<D, G, false>), grid, dim3(kDecThreads), 0, st, a, BH);
   return hipGetLastError();
 }
 

@@ -1,0 +1,77 @@
+// Tile streaming helpers for gfx950 kernels: 16-byte buffer loads written straight into
+// LDS (no register staging), 32-slot tiles in a ring, XOR-swizzled rows.
+#pragma once
+
+#include "kvs_common.h"
+
+namespace kvs {
+
+constexpr int kT2 = 32;              // slots per tile
+constexpr int kRing2 = 4;            // tile buffers
+constexpr int kW2 = 4;               // waves that share one tile's loads
+
+template <int D>
+struct Dma {
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int ROWB = 2 * D;               // bytes per row
+  static constexpr int TILEB = kT2 * ROWB;         // bytes per K (or V) tile
+  static constexpr int RPI = 1024 / ROWB;          // rows filled by one wave-wide 16-byte load
+  static constexpr int IPW = TILEB / 1024 / kW2;   // such loads per wave per K (or V) tile
+};
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// byte offset of 16-byte chunk c of row r inside a tile
+template <int D>
+__device__ __forceinline__ int chunk_off(int r, int c) {
+  return r * (2 * D) + ((c ^ swz<D>(r)) << 4);
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes from `base` (stride 0): loads beyond the range
+// return zeros.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4_t r;
+  r.x = (uint32_t)a;
+  r.y = (uint32_t)(a >> 32) & 0xffffu;
+  r.z = bytes;
+  r.w = 0x00020000u;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uint64_t>((const lds_u8*)p);
+}
+
+// Buffer loads written straight to LDS: lane i's 16 (or 4) bytes land at lds + 16 i (4 i).
+// They are issued as inline assembly with no register results, so the compiler does not
+// order them against unrelated LDS reads; the caller tracks completion with wait_vm.
+__device__ __forceinline__ void dma16(const u32x4_t& rs, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(off), "s"(rs)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const u32x4_t& rs, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(off), "s"(rs)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (loads
+// return in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+}  // namespace kvs

@@ -92,7 +92,7 @@ def decode(K, V, n, q, n_slots: int | None = None, sm_scale: float | None = None
     N = cap if n_slots is None else n_slots
     cache = L.cache_desc(K, Hq, N)
     if workspace is None:
-        workspace = torch.empty(max(L.workspace_bytes(L.KVS_OP_DECODE, cache, None), 16), dtype=torch.uint8,
+        workspace = torch.zeros(max(L.workspace_bytes(L.KVS_OP_DECODE, cache, None), 16), dtype=torch.uint8,
                                 device=K.device)
     if out is None:
         out = torch.empty(B, Hq, D, dtype=torch.float32, device=K.device)
