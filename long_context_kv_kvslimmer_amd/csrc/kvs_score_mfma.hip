@@ -118,10 +118,13 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
   using M = Dma<D>;
   constexpr int KS = D / 16;    // 16-wide k steps over the head dim
   constexpr int DB = D / 32;    // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(1024))) uint8_t kr[kGroups * kRing2 * M::TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vr[kGroups * kRing2 * M::TILEB];
+  // K tiles, then V tiles; after the loop the whole ring holds the records being merged
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kGroups * kRing2 * M::TILEB];
   __shared__ __attribute__((aligned(16))) int32_t nr[kGroups * kRing2 * kT2];
   __shared__ float xm[2 * kQB];
+  static_assert(kQB * (D + 4) * 4 <= 2 * kGroups * kRing2 * M::TILEB, "record staging exceeds the ring");
+  uint8_t* const kr = ring;
+  uint8_t* const vr = ring + kGroups * kRing2 * M::TILEB;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -180,14 +183,16 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     }
   };
 
+  // tile 0 and the query operands travel together; later tiles are issued once they are in
+  // (loads complete in order, so waiting on the queries waits on tile 0 as well)
   if (nt > 0) issue(0);
-  if (nt > 1) issue(1);
-  if (nt > 2) issue(2);
-
   const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + hk * a.G) * (int64_t)a.W) * D;
   const int64_t q = qb * kQB + gw * 32 + c32;
   bf16x8_t qop[KS];
   load_rows32<D>(Qp, a.GW, q, qop);
+  asm volatile("" ::"v"(qop[KS - 1]));
+  if (nt > 1) issue(1);
+  if (nt > 2) issue(2);
 
   const float cs = a.scale * kLog2e;
   float m = kNoMax, lsum = 0.f;
@@ -226,10 +231,10 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     }
   };
 
-  auto softmax_pv = [&](int t, const f32x16_t& st) {
+  // softmax of tile t from S^T in registers: P^T operands (bf16 hi + lo, two 16-slot k steps)
+  auto softmax = [&](int t, const f32x16_t& st, bf16x8_t (&phi)[2], bf16x8_t (&plo)[2]) {
     const int buf = t % kRing2;
     const int64_t t0 = g0 + (int64_t)t * kT2;
-    const uint8_t* V_ = vr_g + buf * M::TILEB;
     const bool plain = !HAS_N && t0 >= lo && t0 + kT2 <= hi;
     float e[16];
     float mx;
@@ -272,28 +277,26 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) lsum += p[i];
-    // O^T += V^T . P^T in two 16-slot k steps; k index (h, j) <-> slot
-    // 16 ks + 8 (j / 4) + 4 h + j % 4, i.e. the lane's own p[8 ks + j]
+    // k index (h, j) of step ks <-> slot 16 ks + 8 (j / 4) + 4 h + j % 4: the lane's p[8 ks + j]
+    split_hi_lo(p, phi[0], plo[0]);
+    split_hi_lo(p + 8, phi[1], plo[1]);
+  };
+
+  // V^T operands of one 16-slot k step by transposed reads: source lane i = lane % 16 points
+  // at row r0 + i / 4 (and + 8), columns 32 db + 16 (G16 % 2) + 4 (i % 4); lane t receives
+  // column + t of 4 consecutive rows
+  auto read_vt = [&](int t, int ks, bf16x8_t (&vop)[DB]) {
+    const uint8_t* V_ = vr_g + (t % kRing2) * M::TILEB;
+    const int r0 = ks * 16 + 4 * h + (t16 >> 2);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t phi, plo;
-      split_hi_lo(p + 8 * ks, phi, plo);
-      // transposed read: source lane i = lane % 16 points at row r0 + i / 4 (and + 8),
-      // columns 32 db + 16 (G16 % 2) + 4 (i % 4); lane t receives column + t of 4 rows
-      const int r0 = ks * 16 + 4 * h + (t16 >> 2);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-        const int col = db * 32 + 16 * (G16 & 1) + 4 * (t16 & 3);
-        const int cb = (col & 7) * 2;
-        const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(V_ + chunk_off<D>(r0, col >> 3) + cb));
-        const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(V_ + chunk_off<D>(r0 + 8, col >> 3) + cb));
-        const bf16x8_t vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[db] = mfma32(vop, phi, acc[db]);
-        acc[db] = mfma32(vop, plo, acc[db]);
-      }
+    for (int db = 0; db < DB; ++db) {
+      typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+      const int col = db * 32 + 16 * (G16 & 1) + 4 * (t16 & 3);
+      const int cb = (col & 7) * 2;
+      const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(V_ + chunk_off<D>(r0, col >> 3) + cb));
+      const bf16x4_t v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(V_ + chunk_off<D>(r0 + 8, col >> 3) + cb));
+      vop[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
 
@@ -311,45 +314,88 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     if (act) {
       if (t + 3 < nt) issue(t + 3);
       if (do_cos) cosines(t);
+      const bool more = t + 1 < nt;
+      // 1. operand reads first: K rows of tile t + 1 and V^T of tile t (first k step)
+      bf16x8_t ka[KS], v0[DB], v1[DB];
+      if (more) {
+        const uint8_t* K_ = kr_g + ((t + 1) % kRing2) * M::TILEB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(c32, 2 * ks + h)));
+      }
+      read_vt(t, 0, v0);
+      __builtin_amdgcn_sched_barrier(0);
+      // 2. softmax of tile t (vector units) while the reads land
+      bf16x8_t phi[2], plo[2];
+      softmax(t, s_cur, phi, plo);
+      __builtin_amdgcn_sched_barrier(0);
+      // 3. S^T of tile t + 1 on the matrix cores, then the second V^T k step is read
       f32x16_t s_next;
-      if (t + 1 < nt) s_next = qk(t + 1);
-      softmax_pv(t, s_cur);
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_next[i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s_next = mfma32(ka[ks], qop[ks], s_next);
+      }
+      read_vt(t, 1, v1);
+      // 4. O^T += V^T . P^T for tile t
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        acc[db] = mfma32(v0[db], phi[0], acc[db]);
+        acc[db] = mfma32(v0[db], plo[0], acc[db]);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        acc[db] = mfma32(v1[db], phi[1], acc[db]);
+        acc[db] = mfma32(v1[db], plo[1], acc[db]);
+      }
       s_cur = s_next;
     }
   }
 
-  // merge the two groups' running states through LDS, then write the partial record
+  // merge the two groups' running states through LDS, then write the partial records with
+  // 16-byte stores (one record = {m, l, -, -, o[D]} is D + 4 contiguous floats)
   const float l = sum_halves(lsum);
   __syncthreads();
-  float* xo = reinterpret_cast<float*>(kr);              // [128 queries][D]
+  float* xo = reinterpret_cast<float*>(ring);            // [128 queries][D + 4]
+  constexpr int RS = D + 4;
   const int qi = gw * 32 + c32;
   if (kGroups == 2 && grp == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xo[qi * D + db * 32 + (i >> 2) * 8 + h * 4 + (i & 3)] = acc[db][i];
+      for (int i = 0; i < 16; ++i) xo[qi * RS + 4 + db * 32 + (i >> 2) * 8 + h * 4 + (i & 3)] = acc[db][i];
     if (h == 0) {
       xm[qi] = m;
       xm[kQB + qi] = l;
     }
   }
   __syncthreads();
-  if (grp == 0 && q < a.GW) {
+  if (grp == 0) {
     const float m1 = kGroups == 2 ? xm[qi] : kNoMax, l1 = kGroups == 2 ? xm[kQB + qi] : 0.f;
     const float Mx = fmaxf(m, m1);
     const float f0 = __builtin_amdgcn_exp2f(m - Mx), f1 = __builtin_amdgcn_exp2f(m1 - Mx);
-    float* rec = a.part + ((bh * a.GW + q) * a.nsplit + split) * (int64_t)(D + 4);
     if (h == 0) {
-      rec[0] = Mx;
-      rec[1] = l * f0 + l1 * f1;
+      xo[qi * RS] = Mx;
+      xo[qi * RS + 1] = l * f0 + l1 * f1;
+      xo[qi * RS + 2] = 0.f;
+      xo[qi * RS + 3] = 0.f;
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int d = db * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-        rec[4 + d] = kGroups == 2 ? acc[db][i] * f0 + xo[qi * D + d] * f1 : acc[db][i] * f0;
+        xo[qi * RS + 4 + d] = kGroups == 2 ? acc[db][i] * f0 + xo[qi * RS + 4 + d] * f1 : acc[db][i] * f0;
       }
+  }
+  __syncthreads();
+  const int64_t qbase = qb * kQB;
+  const int nq = (int)(a.GW - qbase < kQB ? a.GW - qbase : kQB);
+  for (int idx = tid; idx < nq * (RS / 4); idx += kThreads) {
+    const int qq = idx / (RS / 4), c = idx % (RS / 4);
+    float* rec = a.part + ((bh * a.GW + qbase + qq) * a.nsplit + split) * (int64_t)RS;
+    *reinterpret_cast<float4*>(rec + 4 * c) = *reinterpret_cast<const float4*>(xo + qq * RS + 4 * c);
   }
 }
 
@@ -439,8 +485,6 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
   };
 
   issue(0);
-  if (ntiles > 1) issue(1);
-  if (ntiles > 2) issue(2);
 
   // the wave's 32 queries as A operands (two 16-query blocks): lane l holds query
   // 16 qb2 + l % 16, head-dim chunk 4 ks + l / 16 of Q and of -2 O (bf16 hi + lo), read
@@ -486,6 +530,10 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       }
     }
   }
+  // tile 0 and the operands travel together; later tiles are issued once they are in
+  asm volatile("" ::"v"(olo[1][KS - 1]), "v"(nbq[1][3]));
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
   const float cs = a.scale * kLog2e;
 
   auto compute = [&](int t) {
@@ -549,12 +597,9 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
         gx = __builtin_fmaf(ae * ao, __builtin_amdgcn_sqrtf(fabsf(rc)), gx);
       }
     // sum the four lane groups (queries 4 g + r)
-    gse += __shfl_xor(gse, 16, 64);
-    gso += __shfl_xor(gso, 16, 64);
-    gx += __shfl_xor(gx, 16, 64);
-    gse += __shfl_xor(gse, 32, 64);
-    gso += __shfl_xor(gso, 32, 64);
-    gx += __shfl_xor(gx, 32, 64);
+    gse = sum_xor32(sum_xor16(gse));
+    gso = sum_xor32(sum_xor16(gso));
+    gx = sum_xor32(sum_xor16(gx));
     if (g4 == 0) {
       red_s[wv * kChunk2Max + t * kT2 + 2 * n16] = gse;
       red_s[wv * kChunk2Max + t * kT2 + 2 * n16 + 1] = gso;
