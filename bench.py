@@ -37,6 +37,8 @@ def kernel_bytes(N, H, D, P, T, GW, has_n=False, elt=2):
         "score_pass2": N * H * (row + nb) + (N + P) * H * 4,       # K, V once; g_self, g_cross out
         "select": 0,                                              # a full round selects by rule
         "merge_compact": N * H * (row + 4 + nb) + P * H * 4 + T * H * (row + 4 + 4),
+        # pass 2 with the merge folded in: K, V once; g_self, g_cross and the compacted cache out
+        "score_pass2_merge": N * H * (row + nb) + (N + P) * H * 4 + T * H * (row + 4 + 4),
         "decode": T * H * (row + 4),
     }
 
@@ -248,6 +250,16 @@ def main():
     cos_out = bufs.cos if 0 < M < P else None
 
     def step(i):
+        """One round: statistics, weights, merge and compaction in kvs_score_merge (a full
+        round: every candidate pair merges), then one decode step over the merged cache."""
+        K, V, Qw, q = sets[i % len(sets)]
+        L.kvs_score_merge(cache, K, V, None, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, out_desc,
+                          bufs.K, bufs.V, bufs.n, bufs.src, bufs.score_ws)
+        L.kvs_decode_attn(dec_cache, bufs.K, bufs.V, bufs.n, q, 1.0 / math.sqrt(D), dec_out, dec_ws)
+
+    def step_separate(i):
+        """The same round through the separate calls (kvs_score, kvs_merge_weights,
+        kvs_merge_compact): measured in warm-up for the standalone merge pass."""
         K, V, Qw, q = sets[i % len(sets)]
         L.kvs_score(cache, K, V, None, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, cos_out, bufs.score_ws)
         L.kvs_merge_weights(cache, rnd, bufs.g_self, bufs.g_cross, cos_out, None, None, bufs.sel_state)
@@ -268,6 +280,17 @@ def main():
     for name, ms in every.times():
         tot, cnt = per_kernel.get(name, (0.0, 0))
         per_kernel[name] = (tot + ms, cnt + 1)
+    step_separate(0)            # first launches of these kernels load their code
+    torch.cuda.synchronize()
+    sep = L.KernelMarks(max_launches=16 * max(n_marked, 1))
+    with sep:
+        for i in range(n_marked):
+            step_separate(i)
+    torch.cuda.synchronize()
+    separate = {}
+    for name, ms in sep.times():
+        tot, cnt = separate.get(name, (0.0, 0))
+        separate[name] = (tot + ms, cnt + 1)
     dominant = max(per_kernel, key=lambda n: per_kernel[n][0]) if per_kernel else None
 
     # timed region: K whole steps; the library records HIP events right before and after
@@ -296,6 +319,13 @@ def main():
         kernels[name] = {"launches_per_step": cnt // max(n_marked, 1), "avg_ms": round(avg, 4),
                          "algorithmic_MB": round(by / 1e6, 2),
                          "GBps": round(by / (avg * 1e-3) / 1e9, 1) if by else None}
+    kernels_separate = {}
+    for name, (tot, cnt) in separate.items():
+        avg = tot / cnt
+        by = kb.get(name, 0)
+        kernels_separate[name] = {"avg_ms": round(avg, 4), "algorithmic_MB": round(by / 1e6, 2),
+                                  "GBps": round(by / (avg * 1e-3) / 1e9, 1) if by else None,
+                                  "hbm_frac": round(by / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if by else None}
     dom_ms = sum(timed) / len(timed)
     dom_gbps = kb[dominant] / (dom_ms * 1e-3) / 1e9
     step_bytes = sum(kb[n] * kernels[n]["launches_per_step"] for n in kernels if n in kb)
@@ -312,13 +342,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "C2: one Llama-3.1-8B layer, 32K ctx, merge to 50% keeping 32 recent, "
-                               "then one decode step", "batch": B, "kv_heads": H, "q_heads": Hq, "head_dim": D,
+        "config": {"workload": "C2: one Llama-3.1-8B layer, 32K ctx, merge to 50% keeping 32 recent "
+                               "(kvs_score_merge), then one decode step", "batch": B, "kv_heads": H, "q_heads": Hq, "head_dim": D,
                    "n_slots": N, "window": W, "n_merge": M, "out_slots": T, "input_sets": len(sets),
                    "accumulate": "f32"},
         "hbm_GBps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "gpu_ms_per_step": round(gpu_ms, 4),
         "kernels_warmup_marked": kernels,
+        "kernels_separate_calls": kernels_separate,
         "roofline": {"kernel": dominant, "avg_ms": round(dom_ms, 4), "launches": len(timed),
                      "algorithmic_bytes": kb[dominant], "bound": "hbm", "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBS, 4),

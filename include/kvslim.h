@@ -6,6 +6,7 @@
  *
  *   kvs_score          window attention statistics (lse, o) and the forward-only
  *                      Hessian-norm sums g_self / g_cross, plus adjacent-key cosine
+ *   kvs_score_merge    kvs_score + kvs_merge_compact of a full round in one call
  *   kvs_merge_weights  pair selection (top-M adjacent pairs by cosine) and the
  *                      closed-form key-merge weights
  *   kvs_merge_compact  key merge, lossless value-slot merge, stream compaction
@@ -124,6 +125,25 @@ kvs_status kvs_score(const kvs_cache* cache, kvs_dtype dtype,
                      const void* Qw, const kvs_round* round,
                      float* lse, float* O, float* g_self, float* g_cross, float* cos,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_score_merge — one full merge round (n_merge == P: every candidate pair merges) in
+ * one call: the statistics of kvs_score (lse, O, g_self, g_cross; no cosine, nothing is
+ * chosen) and the outputs of kvs_merge_compact (K_out, V_out, n_out, src_out), computed
+ * with the same arithmetic, so every output equals that of kvs_score followed by
+ * kvs_merge_compact bit for bit.  For bf16 caches with head_dim 64 or 128 and at most 128
+ * window queries per kv head (G * window <= 128), the merge runs inside the scorer's
+ * second pass on the K/V tiles it has already loaded, which saves one read of the cache;
+ * other shapes run the two passes one after the other.  Arguments as in kvs_score and
+ * kvs_merge_compact; workspace: kvs_workspace_bytes(KVS_OP_SCORE).  Errors as theirs, and
+ * KVS_ERR_SHAPE if n_merge != P.
+ */
+kvs_status kvs_score_merge(const kvs_cache* cache, kvs_dtype dtype,
+                           const void* K, const void* V, const int32_t* n, const void* Qw,
+                           const kvs_round* round, float* lse, float* O, float* g_self, float* g_cross,
+                           const kvs_cache* out, kvs_dtype out_dtype,
+                           void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kvs_merge_weights — pair selection and closed-form weights.

@@ -12,6 +12,7 @@
 
 #include "../../include/kvslim.h"
 #include "kvs_internal.h"
+#include "kvs_score_impl.h"
 
 namespace {
 
@@ -202,6 +203,46 @@ kvs_status kvs_score(const kvs_cache* cache, kvs_dtype dtype, const void* K, con
   return hip_status(kvs::launch_score(s, r, K, V, n, Qw, lse, O, g_self, g_cross, cos, workspace,
                                       static_cast<hipStream_t>(stream)),
                     "kvs_score");
+}
+
+kvs_status kvs_score_merge(const kvs_cache* cache, kvs_dtype dtype, const void* K, const void* V, const int32_t* n,
+                           const void* Qw, const kvs_round* round, float* lse, float* O, float* g_self,
+                           float* g_cross, const kvs_cache* out, kvs_dtype out_dtype, void* K_out, void* V_out,
+                           int32_t* n_out, int32_t* src_out, void* workspace, size_t workspace_bytes, void* stream) {
+  kvs::Shape s, so;
+  kvs::RoundP r;
+  kvs_status st = check_cache(cache, dtype, s);
+  if (st) return st;
+  if ((st = check_round(round, s, r, true))) return st;
+  if (r.M != r.P)
+    return fail(KVS_ERR_SHAPE, "kvs_score_merge merges every candidate pair: n_merge %lld must equal P = %lld",
+                (long long)r.M, (long long)r.P);
+  if (s.N < 1) return fail(KVS_ERR_SHAPE, "kvs_score_merge needs n_slots >= 1");
+  if (!K || !V || !Qw || !lse || !O || !g_self || (r.P > 0 && !g_cross))
+    return fail(KVS_ERR_NULL, "kvs_score_merge: K, V, Qw, lse, O, g_self and g_cross are required");
+  if (!out) return fail(KVS_ERR_NULL, "kvs_score_merge: out layout is NULL");
+  if ((st = check_cache(out, out_dtype, so))) return st;
+  if (so.B != s.B || so.Hkv != s.Hkv || so.D != s.D)
+    return fail(KVS_ERR_SHAPE, "out layout must match batch, n_kv_heads and head_dim of the input");
+  if (so.N != s.N - r.M)
+    return fail(KVS_ERR_SHAPE, "out n_slots %lld != N - M = %lld", (long long)so.N, (long long)(s.N - r.M));
+  if (!K_out || !V_out || !n_out || !src_out)
+    return fail(KVS_ERR_NULL, "kvs_score_merge: K_out, V_out, n_out, src_out are required");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(Qw) || !aligned16(K_out) || !aligned16(V_out))
+    return fail(KVS_ERR_ALIGN, "K, V, Qw, K_out, V_out must be 16-byte aligned");
+  const size_t need = kvs::score_workspace_bytes(s, r);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(KVS_ERR_WORKSPACE, "kvs_score_merge needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  kvs::OutP op{so.sb, so.sh, so.bf16};
+  if (kvs::fused_round_ok(s, r))
+    return hip_status(kvs::launch_score_merge_mfma(s, r, K, V, n, Qw, lse, O, g_self, g_cross, workspace, op, K_out,
+                                                   V_out, n_out, src_out, hs),
+                      "kvs_score_merge");
+  // the same round as two passes on the GPU (scorer, then the merge pass)
+  hipError_t e = kvs::launch_score(s, r, K, V, n, Qw, lse, O, g_self, g_cross, nullptr, workspace, hs);
+  if (e == hipSuccess) e = kvs::launch_merge(s, r, K, V, n, g_self, g_cross, nullptr, op, K_out, V_out, n_out, src_out, hs);
+  return hip_status(e, "kvs_score_merge");
 }
 
 kvs_status kvs_merge_weights(const kvs_cache* cache, const kvs_round* round, const float* g_self,

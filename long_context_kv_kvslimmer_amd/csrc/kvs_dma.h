@@ -74,6 +74,10 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until every LDS operation of this wave has completed (lgkmcnt 0; vmcnt and expcnt
+// left at their maxima).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 // x[l] + x[l ^ 16] and x[l] + x[l ^ 32] by lane swaps (no LDS round trip); both lanes of a
 // pair add the same two values in the same order, so they hold identical bits.
 __device__ __forceinline__ float sum_xor16(float x) {

@@ -31,6 +31,12 @@ struct P2Args {
   int64_t N, S, P, sb, sh, GW;
   int Hkv, Hq, G, W;
   float scale;
+  // merge outputs of a full round fused into pass 2 (kvs_score_merge); unused otherwise
+  void* Ko;
+  void* Vo;
+  int32_t* no;
+  int32_t* so;
+  int64_t osb, osh;
 };
 
 struct CosArgs {
@@ -54,6 +60,13 @@ inline void valu_pass1_plan(int64_t N, int64_t& chunk, int& nsplit) {
 
 bool use_mfma_scorer(const Shape& s);
 size_t mfma_score_workspace_bytes(const Shape& s, const RoundP& r);
+// Whole full round (n_merge == P) fused: pass 1, combine, pass 2 with the merge and
+// compaction folded in.  Requires use_mfma_scorer and at most 128 window queries per kv head.
+bool fused_round_ok(const Shape& s, const RoundP& r);
+hipError_t launch_score_merge_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                                   const void* Qw, float* lse, float* O, float* g_self, float* g_cross, void* ws,
+                                   const OutP& o, void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
+                                   hipStream_t st);
 hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
                              const void* Qw, float* lse, float* O, float* g_self, float* g_cross, float* cos,
                              void* ws, hipStream_t st);

@@ -422,7 +422,9 @@ __device__ __forceinline__ int row_slot(int R) { return 2 * (R & 15) + (R >> 4);
 
 // grid: one workgroup per (bh, slot chunk, query block), bh fastest so that the blocks of
 // one head land on one XCD.
-template <int D, bool HAS_N>
+// MERGE: also merge every candidate pair of the chunk (a full round) and write the
+// compacted K/V rows (type TO), counts and sources, reusing the tiles already in LDS.
+template <int D, bool HAS_N, bool MERGE, typename TO>
 __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t base, int64_t chunk, int nsplit,
                                                              int BH) {
   using M = Dma<D>;
@@ -607,13 +609,96 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     }
   };
 
+  // Merge of tile tt (its g sums complete, its rows still in the ring): every candidate
+  // pair becomes one slot k* = w_0 k_m + w_1 k_{m+1}, v* = count-weighted mean, n* = n_m +
+  // n_{m+1} at output row S + p; protected slots are copied to row i (sinks) or i - P.
+  // Thread = (pair n, 16-byte chunk ch) of the tile; the arithmetic is the merge pass's.
+  auto merge_tile = [&](int tt) {
+    constexpr int CPR = M::CPR, E = 8;
+    if (tid >= (kT2 / 2) * CPR) return;
+    const int pn = tid / CPR, ch = tid % CPR;
+    const int buf = tt % kRing2;
+    const int64_t m0 = c0 + (int64_t)tt * kT2 + 2 * pn;
+    const uint8_t* K_ = kr + buf * M::TILEB;
+    const uint8_t* V_ = vr + buf * M::TILEB;
+    const int64_t hoff_o = b * a.osb + hk * a.osh;
+    TO* Ko = static_cast<TO*>(a.Ko) + hoff_o;
+    TO* Vo = static_cast<TO*>(a.Vo) + hoff_o;
+    int32_t* no = a.no + hoff_o / D;
+    int32_t* so = a.so + hoff_o / D;
+    const int64_t pend = a.S + 2 * a.P;   // first slot after the candidate pairs
+    const int n0 = HAS_N ? nr[buf * kT2 + pn] : 1, n1 = HAS_N ? nr[buf * kT2 + 16 + pn] : 1;
+    const uint4 k0 = *reinterpret_cast<const uint4*>(K_ + chunk_off<D>(pn, ch));
+    const uint4 k1 = *reinterpret_cast<const uint4*>(K_ + chunk_off<D>(16 + pn, ch));
+    const uint4 v0 = *reinterpret_cast<const uint4*>(V_ + chunk_off<D>(pn, ch));
+    const uint4 v1 = *reinterpret_cast<const uint4*>(V_ + chunk_off<D>(16 + pn, ch));
+    if (m0 >= a.S && m0 + 1 < pend && m0 >= lo && m0 + 1 < hi) {
+      const int ls = tt * kT2 + 2 * pn;
+      float g0 = 0.f, g1 = 0.f, gx = 0.f;
+#pragma unroll
+      for (int w = 0; w < kW2; ++w) {
+        g0 += red_s[w * kChunk2Max + ls];
+        g1 += red_s[w * kChunk2Max + ls + 1];
+        gx += red_x[w * (kChunk2Max / 2) + tt * (kT2 / 2) + pn];
+      }
+      float w0, w1;
+      closed_form_weights(g0, gx, g1, w0, w1);
+      float kf0[E], kf1[E], vf0[E], vf1[E], ko[E], vo[E];
+      unpack<bf16>(k0, kf0);
+      unpack<bf16>(k1, kf1);
+      unpack<bf16>(v0, vf0);
+      unpack<bf16>(v1, vf1);
+#pragma unroll
+      for (int e = 0; e < E; ++e) ko[e] = __builtin_fmaf(w0, kf0[e], w1 * kf1[e]);
+      const int nt = n0 + n1;
+      if constexpr (HAS_N) {
+        const float c0f = (float)n0, c1f = (float)n1, ct = (float)nt;
+#pragma unroll
+        for (int e = 0; e < E; ++e) vo[e] = __builtin_fmaf(c0f, vf0[e], c1f * vf1[e]) / ct;
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) vo[e] = (vf0[e] + vf1[e]) * 0.5f;
+      }
+      const int64_t pos = a.S + (m0 - a.S) / 2;
+      store_elems<TO, E>(Ko + pos * D + ch * E, ko);
+      store_elems<TO, E>(Vo + pos * D + ch * E, vo);
+      if (ch == 0) {
+        no[pos] = nt;
+        so[pos] = (int32_t)m0;
+      }
+    } else {
+      // slots outside the candidate pairs (or a pair cut by the chunk edge) are copied
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int64_t i = m0 + r;
+        if (i < lo || i >= hi || (i >= a.S && i < pend)) continue;
+        const int64_t pos = i < a.S ? i : i - a.P;
+        const uint4 kc = r ? k1 : k0, vc = r ? v1 : v0;
+        float f[E];
+        unpack<bf16>(kc, f);
+        store_elems<TO, E>(Ko + pos * D + ch * E, f);
+        unpack<bf16>(vc, f);
+        store_elems<TO, E>(Vo + pos * D + ch * E, f);
+        if (ch == 0) {
+          no[pos] = r ? n1 : n0;
+          so[pos] = (int32_t)i;
+        }
+      }
+    }
+  };
+
   for (int t = 0; t < ntiles; ++t) {
     wait_tile(ntiles - 1 - t < 2 ? ntiles - 1 - t : 2);   // tile t landed
     __syncthreads();
+    if (MERGE && t > 0) {
+      merge_tile(t - 1);
+      wait_lds();   // its LDS reads are done before the ring slot is refilled
+    }
     if (t + 3 < ntiles) issue(t + 3);
     compute(t);
   }
   __syncthreads();
+  if (MERGE) merge_tile(ntiles - 1);
 
   // per-slot totals of the chunk -> global (several query blocks accumulate)
   const bool acc = gridDim.x > (unsigned)(BH * nsplit);
@@ -691,9 +776,10 @@ size_t mfma_score_workspace_bytes(const Shape& s, const RoundP& r) {
   return part_bytes(s, r) + pack_ops_bytes(s, r) + (size_t)s.B * s.Hkv * pack_blocks(s, r) * 32 * 2 * sizeof(float);
 }
 
+// merge: 0 = plain pass 2; 1 = fused merge with bf16 output; 2 = fused merge with fp32 output
 template <int D>
 static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p1, const P2Args& p2,
-                                const CosArgs& ca, int64_t base, float* lse, float* O, hipStream_t st) {
+                                const CosArgs& ca, int64_t base, float* lse, float* O, int merge, hipStream_t st) {
   const int64_t BH = (int64_t)s.B * s.Hkv;
   const int nqb = (int)((p1.GW + kQB - 1) / kQB);
   const dim3 grid((unsigned)(BH * p1.nsplit * nqb));
@@ -716,6 +802,7 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
   e = launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st, &pk);
   if (e != hipSuccess) return e;
   if (nqb > 1) {
+    if (merge) return hipErrorInvalidValue;   // the fused merge needs every query in one workgroup
     // several query blocks accumulate into the same sums
     e = launch_fill_zero(p2.g_self, BH * s.N, st);
     if (e == hipSuccess) e = launch_fill_zero(p2.g_cross, BH * r.P, st);
@@ -725,18 +812,35 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
   int nsplit2;
   p2_plan(s, r, chunk2, nsplit2);
   const dim3 grid2((unsigned)(BH * nsplit2 * nqb));
-  if (p2.n)
-    KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, true>), grid2, dim3(kW2 * 64), 0, st, p2, base, chunk2, nsplit2,
-               (int)BH);
-  else
-    KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, false>), grid2, dim3(kW2 * 64), 0, st, p2, base, chunk2, nsplit2,
-               (int)BH);
+  const dim3 blk(kW2 * 64);
+  const int bhi = (int)BH;
+  if (merge == 0) {
+    if (p2.n)
+      KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, true, false, bf16>), grid2, blk, 0, st, p2, base, chunk2, nsplit2, bhi);
+    else
+      KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, false, false, bf16>), grid2, blk, 0, st, p2, base, chunk2, nsplit2, bhi);
+  } else if (merge == 1) {
+    if (p2.n)
+      KVS_LAUNCH("score_pass2_merge", (p2_mfma_kernel<D, true, true, bf16>), grid2, blk, 0, st, p2, base, chunk2, nsplit2,
+                 bhi);
+    else
+      KVS_LAUNCH("score_pass2_merge", (p2_mfma_kernel<D, false, true, bf16>), grid2, blk, 0, st, p2, base, chunk2,
+                 nsplit2, bhi);
+  } else {
+    if (p2.n)
+      KVS_LAUNCH("score_pass2_merge", (p2_mfma_kernel<D, true, true, float>), grid2, blk, 0, st, p2, base, chunk2,
+                 nsplit2, bhi);
+    else
+      KVS_LAUNCH("score_pass2_merge", (p2_mfma_kernel<D, false, true, float>), grid2, blk, 0, st, p2, base, chunk2,
+                 nsplit2, bhi);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
-                             const void* Qw, float* lse, float* O, float* g_self, float* g_cross, float* cos,
-                             void* ws, hipStream_t st) {
+static hipError_t launch_score_any(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                                   const void* Qw, float* lse, float* O, float* g_self, float* g_cross, float* cos,
+                                   void* ws, const OutP* o, void* K_out, void* V_out, int32_t* n_out,
+                                   int32_t* src_out, hipStream_t st) {
   int64_t base;
   P1Args p1;
   p1.K = K;
@@ -754,7 +858,7 @@ hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, con
   p1.GW = (int64_t)s.G * r.W;
   p1.scale = r.scale;
   mfma_plan(s, r, base, p1.chunk, p1.nsplit);
-  P2Args p2;
+  P2Args p2{};
   p2.nwb = pack_blocks(s, r);
   p2.ops = reinterpret_cast<const uint4*>(static_cast<uint8_t*>(ws) + part_bytes(s, r));
   p2.qc = reinterpret_cast<const float*>(static_cast<uint8_t*>(ws) + part_bytes(s, r) + pack_ops_bytes(s, r));
@@ -777,6 +881,16 @@ hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, con
   p2.W = r.W;
   p2.GW = p1.GW;
   p2.scale = r.scale;
+  int merge = 0;
+  if (o) {
+    p2.Ko = K_out;
+    p2.Vo = V_out;
+    p2.no = n_out;
+    p2.so = src_out;
+    p2.osb = o->sb;
+    p2.osh = o->sh;
+    merge = o->bf16 ? 1 : 2;
+  }
   CosArgs ca;
   ca.K = K;
   ca.cos = r.P > 0 ? cos : nullptr;
@@ -785,8 +899,27 @@ hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, con
   ca.sb = s.sb;
   ca.sh = s.sh;
   ca.Hkv = s.Hkv;
-  return s.D == 64 ? launch_mfma_d<64>(s, r, p1, p2, ca, base, lse, O, st)
-                   : launch_mfma_d<128>(s, r, p1, p2, ca, base, lse, O, st);
+  return s.D == 64 ? launch_mfma_d<64>(s, r, p1, p2, ca, base, lse, O, merge, st)
+                   : launch_mfma_d<128>(s, r, p1, p2, ca, base, lse, O, merge, st);
+}
+
+hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                             const void* Qw, float* lse, float* O, float* g_self, float* g_cross, float* cos,
+                             void* ws, hipStream_t st) {
+  return launch_score_any(s, r, K, V, n, Qw, lse, O, g_self, g_cross, cos, ws, nullptr, nullptr, nullptr, nullptr,
+                          nullptr, st);
+}
+
+bool fused_round_ok(const Shape& s, const RoundP& r) {
+  return use_mfma_scorer(s) && r.M == r.P && (int64_t)s.G * r.W <= kQB;
+}
+
+hipError_t launch_score_merge_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                                   const void* Qw, float* lse, float* O, float* g_self, float* g_cross, void* ws,
+                                   const OutP& o, void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
+                                   hipStream_t st) {
+  return launch_score_any(s, r, K, V, n, Qw, lse, O, g_self, g_cross, nullptr, ws, &o, K_out, V_out, n_out, src_out,
+                          st);
 }
 
 }  // namespace kvs

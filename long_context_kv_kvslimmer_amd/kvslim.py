@@ -20,7 +20,7 @@ KVS_OK, KVS_ERR_NULL, KVS_ERR_SHAPE, KVS_ERR_DTYPE, KVS_ERR_STRIDE, KVS_ERR_ALIG
 KVS_BF16, KVS_F32 = 0, 1
 KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE = range(4)
 
-EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_merge_weights", "kvs_merge_compact",
+EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_score_merge", "kvs_merge_weights", "kvs_merge_compact",
            "kvs_decode_attn", "kvs_marks_begin", "kvs_marks_end", "kvs_mark_name", "kvs_mark_ms", "kvs_status_str",
            "kvs_last_error", "kvs_version")
 
@@ -52,6 +52,8 @@ def _load():
         "kvs_num_pairs": (I64, [I64, I64, I64]),
         "kvs_workspace_bytes": (SZ, [ctypes.c_int, C, R]),
         "kvs_score": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, R, P, P, P, P, P, P, SZ, P]),
+        "kvs_score_merge": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, R, P, P, P, P, C, ctypes.c_int, P, P, P, P, P,
+                                            SZ, P]),
         "kvs_merge_weights": (ctypes.c_int, [C, R, P, P, P, P, P, P, SZ, P, SZ, P]),
         "kvs_merge_compact": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, P, R, P, C, ctypes.c_int, P, P, P, P, P]),
         "kvs_decode_attn": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, F, P, P, SZ, P]),
@@ -168,6 +170,18 @@ def kvs_score(cache: KvsCache, K, V, n, Qw, rnd: KvsRound, lse, O, g_self, g_cro
     _check(_lib.kvs_score(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(Qw),
                           ctypes.byref(rnd), _ptr(lse), _ptr(O), _ptr(g_self), _ptr(g_cross), _ptr(cos),
                           _ptr(workspace), ws_bytes, _stream()))
+
+
+def kvs_score_merge(cache: KvsCache, K, V, n, Qw, rnd: KvsRound, lse, O, g_self, g_cross,
+                    out: KvsCache, K_out, V_out, n_out, src_out, workspace):
+    _same_layout(K, V)
+    if K_out.dtype != V_out.dtype:
+        raise ValueError("K_out and V_out must share a dtype")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.kvs_score_merge(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(Qw),
+                                ctypes.byref(rnd), _ptr(lse), _ptr(O), _ptr(g_self), _ptr(g_cross),
+                                ctypes.byref(out), dtype_code(K_out), _ptr(K_out), _ptr(V_out), _ptr(n_out),
+                                _ptr(src_out), _ptr(workspace), ws_bytes, _stream()))
 
 
 def kvs_merge_weights(cache: KvsCache, rnd: KvsRound, g_self, g_cross, cos, w, selected, sel_state):

@@ -77,6 +77,20 @@ def run_round(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: i
     return bufs
 
 
+def run_full_round_fused(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: int,
+                         bufs: RoundBuffers, n_slots: int | None = None):
+    """A full round (every candidate pair merges) through kvs_score_merge."""
+    B, H, cap, D = K.shape
+    N = cap if n_slots is None else n_slots
+    P = L.num_pairs(N, n_sink, n_recent)
+    cache = L.cache_desc(K, n_q_heads, N)
+    rnd = L.round_desc(window, n_sink, n_recent, P, 1.0 / math.sqrt(D))
+    out = L.cache_desc(bufs.K, n_q_heads, N - P)
+    L.kvs_score_merge(cache, K, V, n, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, out,
+                      bufs.K, bufs.V, bufs.n, bufs.src, bufs.score_ws)
+    return bufs
+
+
 def merge_round(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: int, n_merge: int,
                 n_slots: int | None = None, out_dtype=None, out_capacity: int | None = None,
                 want_flags: bool = True) -> RoundBuffers:

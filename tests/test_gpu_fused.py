@@ -1,0 +1,66 @@
+"""GPU: kvs_score_merge (a full round in one call; the merge runs inside the scorer's
+second pass when the shape allows) against kvs_score followed by kvs_merge_compact,
+bit for bit, and against the oracle.  Shapes that the fused kernel does not take (fp32,
+more than 128 window queries per kv head) exercise the two-pass path of the same call."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvs_oracle as O
+from tests.parity import check_round_slice
+from tests.test_gpu_parity import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, B, Hkv, Hq, D, N, cap, W, S, R, dtype, counts, out dtype
+    ("c2-like", 1, 8, 32, 128, 4096, 4096, 32, 0, 32, torch.bfloat16, False, torch.bfloat16),
+    ("odd-sinks-counts", 1, 2, 8, 128, 1001, 1001, 8, 3, 7, torch.bfloat16, True, torch.float32),
+    ("d64-sinks", 1, 3, 6, 64, 1500, 1536, 4, 32, 32, torch.bfloat16, False, torch.float32),
+    ("tiny-N3", 1, 1, 4, 128, 3, 3, 2, 0, 0, torch.bfloat16, False, torch.bfloat16),
+    ("multi-chunk-counts", 1, 2, 8, 128, 40000, 40000, 16, 0, 32, torch.bfloat16, True, torch.bfloat16),
+    ("batch2-d64", 2, 2, 4, 64, 2000, 2048, 16, 0, 0, torch.bfloat16, False, torch.bfloat16),
+    ("two-pass-f32", 1, 1, 8, 128, 513, 520, 3, 1, 0, torch.float32, True, torch.float32),
+    ("two-pass-gw256", 1, 1, 8, 128, 700, 700, 32, 0, 0, torch.bfloat16, False, torch.bfloat16),
+]
+
+
+def _same(a, b, what):
+    assert torch.equal(a, b), f"{what}: {(a != b).sum().item()} elements differ"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fused_round_matches_two_calls(case):
+    from long_context_kv_kvslimmer_amd import pipeline
+    name, B, Hkv, Hq, D, N, cap, W, S, R, dtype, counts, odt = case
+    print(f"\n[fused] {name}", flush=True)
+    K, V, n, Qw = make_inputs(zlib.crc32(name.encode()) % 10000, B, Hkv, Hq, D, N, cap, W, dtype, counts)
+    P = O.num_pairs(N, S, R)
+    T = N - P
+    ref = pipeline.merge_round(K, V, n, Qw, Hq, W, S, R, P, n_slots=N, out_dtype=odt, want_flags=False)
+    fused = pipeline.alloc_round(K, Hq, W, S, R, P, n_slots=N, out_dtype=odt)
+    pipeline.run_full_round_fused(K, V, n, Qw, Hq, W, S, R, fused, n_slots=N)
+    torch.cuda.synchronize()
+    _same(fused.lse, ref.lse, "lse")
+    _same(fused.O, ref.O, "O")
+    _same(fused.g_self, ref.g_self, "g_self")
+    _same(fused.g_cross[..., :P], ref.g_cross[..., :P], "g_cross")
+    _same(fused.K[:, :, :T], ref.K[:, :, :T], "K_out")
+    _same(fused.V[:, :, :T], ref.V[:, :, :T], "V_out")
+    _same(fused.n[:, :, :T], ref.n[:, :, :T], "n_out")
+    _same(fused.src[:, :, :T], ref.src[:, :, :T], "src_out")
+
+
+def test_fused_round_against_oracle():
+    from long_context_kv_kvslimmer_amd import pipeline
+    B, Hkv, Hq, D, N, W, S, R = 1, 2, 8, 128, 1001, 8, 3, 7
+    K, V, n, Qw = make_inputs(4242, B, Hkv, Hq, D, N, N, W, torch.bfloat16, True)
+    P = O.num_pairs(N, S, R)
+    bufs = pipeline.alloc_round(K, Hq, W, S, R, P, n_slots=N, out_dtype=torch.float32, want_flags=False)
+    pipeline.run_full_round_fused(K, V, n, Qw, Hq, W, S, R, bufs, n_slots=N)
+    torch.cuda.synchronize()
+    for h in range(Hkv):
+        check_round_slice(bufs, K, V, n, Qw, 0, h, N, S, R, P, 1 / math.sqrt(D), label=f"fused h{h}", with_cos=False)

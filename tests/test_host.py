@@ -155,3 +155,21 @@ def test_timing_marks_validation(L):
     assert lib.kvs_marks_end() == 0
     assert lib.kvs_mark_name(0) == b""
     assert lib.kvs_mark_ms(0) == -1.0
+
+
+def test_score_merge_validation(L):
+    f = L._lib.kvs_score_merge
+    c = L.KvsCache(1, 2, 8, 128, 1000, 2 * 1000 * 128, 1000 * 128)
+    o = L.KvsCache(1, 2, 8, 128, 500, 2 * 500 * 128, 500 * 128)
+    r_partial = L.round_desc(8, 0, 0, 100, 0.1)
+    args = [FAKE, FAKE, None, FAKE]
+    assert f(ctypes.byref(c), L.KVS_BF16, *args, ctypes.byref(r_partial), FAKE, FAKE, FAKE, FAKE, ctypes.byref(o),
+             L.KVS_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == L.KVS_ERR_SHAPE
+    r_full = L.round_desc(8, 0, 0, 500, 0.1)
+    bad_out = L.KvsCache(1, 2, 8, 128, 499, 2 * 500 * 128, 500 * 128)
+    assert f(ctypes.byref(c), L.KVS_BF16, *args, ctypes.byref(r_full), FAKE, FAKE, FAKE, FAKE, ctypes.byref(bad_out),
+             L.KVS_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == L.KVS_ERR_SHAPE
+    assert f(ctypes.byref(c), L.KVS_BF16, *args, ctypes.byref(r_full), FAKE, FAKE, FAKE, FAKE, ctypes.byref(o),
+             L.KVS_BF16, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == L.KVS_ERR_NULL
+    assert f(ctypes.byref(c), L.KVS_BF16, *args, ctypes.byref(r_full), FAKE, FAKE, FAKE, FAKE, ctypes.byref(o),
+             L.KVS_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == L.KVS_ERR_WORKSPACE
