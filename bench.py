@@ -16,6 +16,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -57,6 +58,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_c2_layer32k.md")
 def kernel_label(rocprof_name):
     if "kvs::" not in rocprof_name:
         return None
+    # pass 2 with the merge folded in: p2_mfma_kernel<D, HAS_N, MERGE = true, ...>
+    if re.search(r"kvs::p2_mfma_kernel<\d+, (true|false), true", rocprof_name):
+        return "score_pass2_merge"
     for key, label in KERNEL_LABELS:
         if "kvs::" + key in rocprof_name:
             return label

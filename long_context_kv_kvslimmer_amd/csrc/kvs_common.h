@@ -20,12 +20,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 values -> two bf16 (a in the low half), round to nearest even: one packed
+// hardware conversion on gfx950.
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_hw_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T>
@@ -85,16 +85,13 @@ __device__ __forceinline__ void store_elems<float, 8>(float* p, const float* f) 
 
 template <>
 __device__ __forceinline__ void store_elems<bf16, 4>(bf16* p, const float* f) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16),
-                                            f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16));
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
 }
 
 template <>
 __device__ __forceinline__ void store_elems<bf16, 8>(bf16* p, const float* f) {
-  *reinterpret_cast<uint4*>(p) = make_uint4(f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16),
-                                            f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16),
-                                            f32_to_bf16_bits(f[4]) | (f32_to_bf16_bits(f[5]) << 16),
-                                            f32_to_bf16_bits(f[6]) | (f32_to_bf16_bits(f[7]) << 16));
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                            pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
 }
 
 // Cross-lane moves inside a 16-lane row (DPP): lane i reads lane i^1, i^2, the mirror
@@ -181,6 +178,22 @@ __device__ __forceinline__ void closed_form_weights(float g11, float g12, float 
   } else {
     w0 = (g11 - g12) / A;
     w1 = (g22 - g12) / A;
+  }
+}
+
+// One merged slot, E elements of it: k* = w0 k_m + w1 k_{m+1}; v* = the count-weighted
+// mean, with weights n_m / (n_m + n_{m+1}) and n_{m+1} / (n_m + n_{m+1}) formed once (equal
+// counts, or no counts, give exactly 1/2 each).
+template <int E>
+__device__ __forceinline__ void merge_pair_elems(const float* kf0, const float* kf1, const float* vf0,
+                                                 const float* vf1, float w0, float w1, int n0, int n1,
+                                                 float* ko, float* vo) {
+  const float ct = (float)(n0 + n1);
+  const float u0 = (float)n0 / ct, u1 = (float)n1 / ct;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    ko[e] = __builtin_fmaf(w0, kf0[e], w1 * kf1[e]);
+    vo[e] = __builtin_fmaf(u0, vf0[e], u1 * vf1[e]);
   }
 }
 

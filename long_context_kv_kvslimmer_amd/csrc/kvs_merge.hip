@@ -155,17 +155,8 @@ __global__ __launch_bounds__(256) void merge_compact_kernel(MergeArgs a) {
             float vf0[E], vf1[E], ko[E], vo[E];
             unpack<TI>(va[u], vf0);
             unpack<TI>(vb[u], vf1);
-#pragma unroll
-            for (int e = 0; e < E; ++e) ko[e] = __builtin_fmaf(w0, kf0[e], w1 * kf1[e]);
+            merge_pair_elems<E>(kf0, kf1, vf0, vf1, w0, w1, n0[u], n1[u], ko, vo);
             const int nt = n0[u] + n1[u];
-            if constexpr (HAS_N) {
-              const float c0 = (float)n0[u], c1 = (float)n1[u], ct = (float)nt;
-#pragma unroll
-              for (int e = 0; e < E; ++e) vo[e] = __builtin_fmaf(c0, vf0[e], c1 * vf1[e]) / ct;
-            } else {
-#pragma unroll
-              for (int e = 0; e < E; ++e) vo[e] = (vf0[e] + vf1[e]) * 0.5f;
-            }
             store_elems<TO, E>(Ko + pos * D + j * E, ko);
             store_elems<TO, E>(Vo + pos * D + j * E, vo);
             if (j == 0) {

@@ -205,11 +205,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
         const float x0 = osh[tid * 8 + 2 * j], x1 = osh[tid * 8 + 2 * j + 1];
         on = __builtin_fmaf(x0, x0, __builtin_fmaf(x1, x1, on));
         const float m0 = -2.f * x0, m1 = -2.f * x1;
-        const uint32_t h0 = f32_to_bf16_bits(m0), h1 = f32_to_bf16_bits(m1);
-        const uint32_t l0 = f32_to_bf16_bits(m0 - __uint_as_float(h0 << 16));
-        const uint32_t l1 = f32_to_bf16_bits(m1 - __uint_as_float(h1 << 16));
-        hi[j] = h0 | (h1 << 16);
-        lo[j] = l0 | (l1 << 16);
+        hi[j] = pack_bf16x2(m0, m1);
+        lo[j] = pack_bf16x2(m0 - bf16_lo(hi[j]), m1 - bf16_hi(hi[j]));
       }
       pk.ops[pack_ops_index(bh, pk.nwb, q, 0, tid, KS)] = *reinterpret_cast<const uint4*>(qrow + tid * 8);
       pk.ops[pack_ops_index(bh, pk.nwb, q, 1, tid, KS)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);

@@ -648,17 +648,8 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       unpack<bf16>(k1, kf1);
       unpack<bf16>(v0, vf0);
       unpack<bf16>(v1, vf1);
-#pragma unroll
-      for (int e = 0; e < E; ++e) ko[e] = __builtin_fmaf(w0, kf0[e], w1 * kf1[e]);
+      merge_pair_elems<E>(kf0, kf1, vf0, vf1, w0, w1, n0, n1, ko, vo);
       const int nt = n0 + n1;
-      if constexpr (HAS_N) {
-        const float c0f = (float)n0, c1f = (float)n1, ct = (float)nt;
-#pragma unroll
-        for (int e = 0; e < E; ++e) vo[e] = __builtin_fmaf(c0f, vf0[e], c1f * vf1[e]) / ct;
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) vo[e] = (vf0[e] + vf1[e]) * 0.5f;
-      }
       const int64_t pos = a.S + (m0 - a.S) / 2;
       store_elems<TO, E>(Ko + pos * D + ch * E, ko);
       store_elems<TO, E>(Vo + pos * D + ch * E, vo);
