@@ -27,15 +27,19 @@ struct DecArgs {
   float scale;
 };
 
-// Split plan: every split is non-empty.  The bf16 MFMA kernel aims at ~512 workgroups
-// over all (batch, kv-head) slices (two per CU), in multiples of 128 slots.
+constexpr int kDecCUs = 256;   // compute units of the chip: workgroups the bf16 decode aims at
+
+// Split plan: every split is non-empty.  The bf16 MFMA kernel (one workgroup per CU) aims
+// at about one workgroup per CU over all (batch, kv-head) slices, at least 128 slots each;
+// chunks need not be whole tiles (a partial last tile is masked).
 static void decode_plan(const Shape& s, int64_t& chunk, int& nsplit) {
   const int64_t N = s.N;
   int64_t c;
   if (s.bf16) {
     const int64_t BH = (int64_t)s.B * s.Hkv;
-    c = (N * BH + 511) / 512;
-    c = (c + 31) / 32 * 32;
+    int64_t want = kDecCUs / BH;
+    if (want < 1) want = 1;
+    c = (N + want - 1) / want;
     if (c < 128) c = 128;
   } else {
     c = (N + 255) / 256;
@@ -176,11 +180,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a) {
 // ----------------------------------------------------------------- bf16 MFMA --
 // gfx950 decode for bf16 caches: v_mfma_f32_16x16x32_bf16 with the G query heads of a
 // kv head as the N side (padded to 16; the padding costs MFMA cycles, which decode has
-// to spare).  Each wave streams 32-slot blocks: K rows go straight from HBM into the A
-// operand of S^T = K . Q^T (lane l: slot 16 sb + l % 16, 64 contiguous bytes per row per
-// load), V rows are staged in a wave-private LDS tile and read back transposed
-// (ds_read_tr16_b64) as the A operand of O^T += V^T . P^T, with P split into bf16 hi + lo.
-// The next block's K/V registers are fetched while the current block is computed.
+// to spare).  S^T = K . Q^T takes K rows as the A operand (lane l: slot 16 sb + l % 16,
+// 16 contiguous bytes); O^T += V^T . P^T reads V transposed from LDS (ds_read_tr16_b64)
+// as the A operand, with P split into bf16 hi + lo so the probabilities keep fp32
+// accuracy.
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 dbf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 dbf16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float df32x4_t;
@@ -194,30 +197,42 @@ __device__ __forceinline__ df32x4_t d_mfma(const dbf16x8_t& a, const dbf16x8_t& 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-constexpr int kDecBlock = 32;     // slots per wave step
 constexpr int kDecWaves = 4;
+constexpr int kDecThreads = 64 * kDecWaves;
 constexpr float kDecNoMax = -1e30f;
-
-// Workgroup = four waves over one slot chunk of one (batch, kv-head), two workgroups per
-// CU.  K and V arrive as 32-slot tiles by 16-byte buffer loads written straight into a
-// four-deep LDS ring (rows XOR-swizzled).  Every wave computes S^T = K . Q^T and the
-// softmax of the whole tile (the G heads are the N side of 16x16x32 MFMA, padded to 16)
-// and accumulates its own quarter of the head dimension of O^T += V^T . P^T.  The running
-// maximum is raised only when it grows by more than 2^8.  Each workgroup writes one
-// partial record per query head for the log-sum-exp combine.
-constexpr int kDecThreads = 256;
 constexpr float kDecLazy = 8.f;
 
+// Tile buffers per wave: 32 KB of K + V (two 32-slot tiles at D = 128, four at D = 64), so
+// the four waves of a workgroup hold 128 KB of LDS.
+template <int D>
+struct DecRing {
+  static constexpr int R = D == 128 ? 2 : 4;
+};
+
+// One workgroup of four waves per CU over a slot chunk of one (batch, kv-head).  Each
+// wave owns every fourth 32-slot tile of the chunk and streams it on its own: 16-byte
+// buffer loads written straight into the wave's LDS ring (rows XOR-swizzled), completion
+// tracked by the wave's own load counter, so the loop has no workgroup barrier and no
+// tile is computed twice.  Per tile the wave computes S^T for all G heads, the online
+// softmax (running maximum raised only when it grows by more than 2^8) and O^T over the
+// whole head dimension.  At the end the four waves' (max, sum, O) are merged in LDS
+// into one partial record per query head for the log-sum-exp combine.
 template <int D, int G, bool HAS_N>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(DecArgs a, int BH) {
+__global__ __launch_bounds__(kDecThreads, 1) void decode_mfma_kernel(DecArgs a, int BH) {
   using M = Dma<D>;
-  constexpr int KB = D / 32;          // k steps of S^T
-  constexpr int DB = D / 16;          // 16-row blocks of O^T
-  constexpr int DBW = DB / 4;         // per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kRing2 * M::TILEB];   // K tiles, then V tiles
-  __shared__ __attribute__((aligned(16))) int32_t nr[kRing2 * kT2];
-  uint8_t* const kr = ring;
-  uint8_t* const vr = ring + kRing2 * M::TILEB;
+  constexpr int R = DecRing<D>::R;
+  constexpr int KB = D / 32;                  // k steps of S^T
+  constexpr int DB = D / 16;                  // 16-row blocks of O^T
+  constexpr int KI = M::TILEB / 1024;         // wave-wide 16-byte loads per K (or V) tile
+  constexpr int QBYTES = G * D * 2;           // the G query rows
+  constexpr int QI = (QBYTES + 1023) / 1024;  // wave-wide loads for them
+  constexpr int PER_TILE = 2 * KI + (HAS_N ? 1 : 0);
+  constexpr int WAVEB = 2 * R * M::TILEB;     // LDS bytes of one wave's ring
+  static_assert(PER_TILE * R + QI < 64, "load counter range");
+  static_assert((32 + G * D) * 4 <= WAVEB, "merge area fits a wave's ring");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kDecWaves * WAVEB];
+  __shared__ __attribute__((aligned(16))) uint8_t qsh[kDecWaves * QI * 1024];
+  __shared__ __attribute__((aligned(16))) int32_t nsh[kDecWaves * R * kT2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -229,65 +244,76 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(DecArgs a, 
   const int64_t s0 = split * a.chunk;
   const int64_t s1 = s0 + a.chunk < a.N ? s0 + a.chunk : a.N;
   const int ntiles = (int)((s1 - s0 + kT2 - 1) / kT2);
+  const int nmine = ntiles > wv ? (ntiles - wv + kDecWaves - 1) / kDecWaves : 0;   // tiles wv, wv + 4, ...
   const uint32_t span = (uint32_t)(s1 - s0);
   const u32x4_t rk = make_rsrc(static_cast<const bf16*>(a.K) + hoff + s0 * D, span * M::ROWB);
   const u32x4_t rv = make_rsrc(static_cast<const bf16*>(a.V) + hoff + s0 * D, span * M::ROWB);
   const int32_t* np = HAS_N ? a.n + hoff / D + s0 : nullptr;
   const u32x4_t rn = make_rsrc(HAS_N ? static_cast<const void*>(np) : a.K, HAS_N ? span * 4u : 0u);
-
-  auto issue = [&](int t) {
-    const int buf = t % kRing2;
-    const int64_t t0 = (int64_t)t * kT2;
-#pragma unroll
-    for (int j = 0; j < M::IPW; ++j) {
-      const int u = j * kW2 + wv;
-      const int R = u * M::RPI + lane / M::CPR;
-      const int c = (lane % M::CPR) ^ swz<D>(R);
-      const uint32_t off = (uint32_t)((t0 + R) * M::ROWB) + (uint32_t)(c << 4);
-      dma16(rk, lds_addr(kr + buf * M::TILEB + u * 1024), off);
-      dma16(rv, lds_addr(vr + buf * M::TILEB + u * 1024), off);
-    }
-    if (HAS_N && wv == 0 && lane < kT2) dma4(rn, lds_addr(nr + buf * kT2), (uint32_t)((t0 + lane) * 4));
-  };
-  auto wait_tile = [&](int later) {
-    if (HAS_N && wv == 0) {
-      if (later >= 2) wait_vm<2 * (2 * M::IPW + 1)>();
-      else if (later == 1) wait_vm<2 * M::IPW + 1>();
-      else wait_vm<0>();
-    } else {
-      if (later >= 2) wait_vm<2 * (2 * M::IPW)>();
-      else if (later == 1) wait_vm<2 * M::IPW>();
-      else wait_vm<0>();
-    }
-  };
-
-  issue(0);
-  if (ntiles > 1) issue(1);
-  if (ntiles > 2) issue(2);
-
-  // B operand of S^T: lane l holds q[head l % 16][d = 32 kb + 8 (l / 16) .. +7], zero padding
   const bf16* qp = static_cast<const bf16*>(a.q) + (b * a.Hq + h * G) * (int64_t)D;
-  dbf16x8_t qop[KB];
+  const u32x4_t rq = make_rsrc(qp, (uint32_t)QBYTES);
+
+  uint8_t* const kw = ring + wv * WAVEB;       // K buffers of this wave, then its V buffers
+  uint8_t* const vw = kw + R * M::TILEB;
+  int32_t* const nw = nsh + wv * R * kT2;
+  uint8_t* const qw = qsh + wv * QI * 1024;
+
+  // wave-local tile i (chunk tile wv + 4 i) -> buffer i % R; rows past the chunk read as zeros
+  auto issue = [&](int i) {
+    const int buf = i % R;
+    const uint32_t t0 = (uint32_t)(wv + kDecWaves * i) * kT2;
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (c16 < G) u = load16(qp + c16 * D + kb * 32 + g * 8);
-    qop[kb] = d_as_bf16x8(u);
-  }
+    for (int u = 0; u < KI; ++u) {
+      const int r = u * M::RPI + lane / M::CPR;
+      const int c = (lane % M::CPR) ^ swz<D>(r);
+      const uint32_t off = (t0 + r) * M::ROWB + (uint32_t)(c << 4);
+      dma16(rk, lds_addr(kw + buf * M::TILEB + u * 1024), off);
+      dma16(rv, lds_addr(vw + buf * M::TILEB + u * 1024), off);
+    }
+    if (HAS_N && lane < kT2) dma4(rn, lds_addr(nw + buf * kT2), (t0 + lane) * 4u);
+  };
+  // wait for wave-local tile i while `later` (0 .. R - 1) tiles issued after it are in flight
+  auto wait_tile = [&](int later) {
+    if (R > 3 && later >= 3) wait_vm<3 * PER_TILE>();
+    else if (R > 2 && later == 2) wait_vm<2 * PER_TILE>();
+    else if (later == 1) wait_vm<PER_TILE>();
+    else wait_vm<0>();
+  };
+
+#pragma unroll
+  for (int u = 0; u < QI; ++u) dma16(rq, lds_addr(qw + u * 1024), (uint32_t)(u * 1024 + lane * 16));
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i < nmine) issue(i);
+
   const float cs = a.scale * kLog2e;
   float m = kDecNoMax, lsum = 0.f;
-  df32x4_t acc[DBW];
+  df32x4_t acc[DB];
 #pragma unroll
-  for (int i = 0; i < DBW; ++i) acc[i] = df32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < DB; ++i) acc[i] = df32x4_t{0.f, 0.f, 0.f, 0.f};
+  // B operand of S^T: lane l holds q[head l % 16][d = 32 kb + 8 (l / 16) .. +7], zero padding
+  dbf16x8_t qop[KB];
 
-  for (int t = 0; t < ntiles; ++t) {
-    wait_tile(ntiles - 1 - t < 2 ? ntiles - 1 - t : 2);
-    __syncthreads();
-    if (t + 3 < ntiles) issue(t + 3);
-    const int buf = t % kRing2;
-    const uint8_t* K_ = kr + buf * M::TILEB;
-    const uint8_t* V_ = vr + buf * M::TILEB;
-    const int64_t t0 = s0 + (int64_t)t * kT2;
+  // V^T operand by transposed reads: source lane i points at row 4 g + i / 4 (and + 16),
+  // columns 16 db + 4 (i % 4); lane t receives column 16 db + t of four consecutive rows
+  const int srow = 4 * g + (c16 >> 2);
+  const int scol = 4 * (c16 & 3);
+
+  for (int i = 0; i < nmine; ++i) {
+    const int later = nmine - 1 - i < R - 1 ? nmine - 1 - i : R - 1;
+    wait_tile(later);
+    if (i == 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (c16 < G) u = *reinterpret_cast<const uint4*>(qw + (c16 * D + kb * 32 + g * 8) * 2);
+        qop[kb] = d_as_bf16x8(u);
+      }
+    }
+    const int buf = i % R;
+    const uint8_t* K_ = kw + buf * M::TILEB;
+    const uint8_t* V_ = vw + buf * M::TILEB;
+    const int64_t t0 = s0 + (int64_t)(wv + kDecWaves * i) * kT2;
     // S^T = K . Q^T: lane holds slots 16 sb + 4 g + r of head c16
     df32x4_t st[2];
 #pragma unroll
@@ -303,7 +329,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(DecArgs a, 
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       int4 n4 = make_int4(1, 1, 1, 1);
-      if (HAS_N) n4 = *reinterpret_cast<const int4*>(nr + buf * kT2 + 16 * sb + 4 * g);
+      if (HAS_N) n4 = *reinterpret_cast<const int4*>(nw + buf * kT2 + 16 * sb + 4 * g);
       const int ns[4] = {n4.x, n4.y, n4.z, n4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -320,56 +346,78 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(DecArgs a, 
       const float corr = __builtin_amdgcn_exp2f(m - mx);
       lsum *= corr;
 #pragma unroll
-      for (int i = 0; i < DBW; ++i) acc[i] *= corr;
+      for (int k = 0; k < DB; ++k) acc[k] *= corr;
       m = mx;
     }
-    float pv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pv[j] = __builtin_amdgcn_exp2f(e[j] - m);
-      lsum += pv[j];
-    }
-    // P^T operand: k index (g, j) <-> slot 16 (j / 4) + 4 g + j % 4, the lane's own pv[j]
+    // P^T operand: k index (g, j) <-> slot 16 (j / 4) + 4 g + j % 4, the lane's own p[j]
     dbf16x8_t phi, plo;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const __bf16 hv = (__bf16)pv[j];
+      const float p = __builtin_amdgcn_exp2f(e[j] - m);
+      lsum += p;
+      const __bf16 hv = (__bf16)p;
       phi[j] = hv;
-      plo[j] = (__bf16)(pv[j] - (float)hv);
+      plo[j] = (__bf16)(p - (float)hv);
     }
-    // V^T operand by transposed reads: source lane i points at row 4 g + i / 4 (and + 16),
-    // columns 16 db + 4 (i % 4); lane t receives column 16 db + t of four consecutive rows
-    const int srow = 4 * g + (c16 >> 2);
-    const int scol = 4 * (c16 & 3);
 #pragma unroll
-    for (int i = 0; i < DBW; ++i) {
+    for (int db = 0; db < DB; ++db) {
       typedef __attribute__((address_space(3))) dbf16x4_t lds_t;
-      const int col = (wv * DBW + i) * 16 + scol;
+      const int col = db * 16 + scol;
       const int cb = (col & 7) * 2;
       const dbf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + chunk_off<D>(srow, col >> 3) + cb));
       const dbf16x4_t v1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + chunk_off<D>(srow + 16, col >> 3) + cb));
       const dbf16x8_t vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[i] = d_mfma(vop, phi, acc[i]);
-      acc[i] = d_mfma(vop, plo, acc[i]);
+      acc[db] = d_mfma(vop, phi, acc[db]);
+      acc[db] = d_mfma(vop, plo, acc[db]);
+    }
+    if (i + R < nmine) {
+      wait_lds();   // this buffer's LDS reads are done before it is refilled
+      issue(i + R);
     }
   }
+  wait_vm<0>();
 
-  // partial record per query head c16: {m, l, -, -, o[D]}, O^T rows d = 16 db + 4 g + r
+  // merge the four waves: each writes {m[16], l[16], O[G][D]} over its own ring, then the
+  // workgroup forms one record {M, L, -, -, o[D]} per query head (O^T rows d = 16 db + 4 g + r)
   float l = lsum;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  const int64_t nsplit = a.nsplit;
+  float* const mine = reinterpret_cast<float*>(kw);
+  if (g == 0) {
+    mine[c16] = m;
+    mine[16 + c16] = l;
+  }
   if (c16 < G) {
-    float* rec = a.part + ((bh * G + c16) * nsplit + split) * (int64_t)(D + 4);
-    if (wv == 0 && g == 0) {
-      rec[0] = m;
-      rec[1] = l;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<float4*>(mine + 32 + c16 * D + db * 16 + 4 * g) =
+          make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+  }
+  __syncthreads();
+  const int64_t nsplit = a.nsplit;
+  for (int k = tid; k < G * D; k += kDecThreads) {
+    const int hh = k / D, d = k - hh * D;
+    float mw[kDecWaves], Mx = kDecNoMax;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      mw[w] = reinterpret_cast<const float*>(ring + w * WAVEB)[hh];
+      Mx = fmaxf(Mx, mw[w]);
     }
+    float o = 0.f, L = 0.f;
 #pragma unroll
-    for (int i = 0; i < DBW; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rec[4 + (wv * DBW + i) * 16 + g * 4 + r] = acc[i][r];
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float* pw = reinterpret_cast<const float*>(ring + w * WAVEB);
+      const float f = __builtin_amdgcn_exp2f(mw[w] - Mx);
+      o = __builtin_fmaf(f, pw[32 + hh * D + d], o);
+      L = __builtin_fmaf(f, pw[16 + hh], L);
+    }
+    float* rec = a.part + ((bh * G + hh) * nsplit + split) * (int64_t)(D + 4);
+    rec[4 + d] = o;
+    if (d == 0) {
+      rec[0] = Mx;
+      rec[1] = L;
+    }
   }
 }
 

@@ -119,55 +119,72 @@ __global__ __launch_bounds__(256) void pass1_valu_kernel(P1Args a) {
 }
 
 // --------------------------------------------------------- log-sum-exp combine --
-// One block of D threads per unit; partial records {m (log2 units), l, -, -, o[D]}.
-// The split weights 2^(m_s - M) are staged in LDS, so each thread's pass over the
-// splits issues independent loads.  Writes lse (natural log, nullable) and the row.
+// Partial records {m (log2 units), l, -, -, o[D]} of every split of a unit become the
+// unit's output row; lse (natural log, nullable) is written too.
 constexpr int kMaxSplit = 1024;
 
-// One 256-thread workgroup per unit (row of `out`).  All split maxima and sums are loaded
-// in one round, reduced in LDS to M and the weights f_s = exp2(m_s - M); then thread t
-// accumulates head-dim element t % D over its own share of the splits (all of its loads
-// issued together) and the shares are added in LDS in a fixed order, so results do not
-// depend on timing.
+// One 256-thread workgroup per unit (row of `out`).  Every load of the first round is
+// issued together: the thread's split maxima and sums, and the first kCombineUnroll
+// records of its share of the output elements (thread t: element t % D over splits
+// t / D, t / D + 256 / D, ...).  M and the weights f_s = exp2(m_s - M) are reduced in LDS,
+// then each thread sums its share and the shares are added in LDS in a fixed order, so
+// results do not depend on timing.  Splits beyond the first round are read in further
+// rounds of kCombineUnroll.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineUnroll = 16;
+constexpr int kCombineML = kMaxSplit / kCombineThreads;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part, int nsplit, int D,
                                                                  float* __restrict__ lse, float* __restrict__ out,
                                                                  PackP pk) {
   __shared__ float wsh[kMaxSplit];
-  __shared__ float red[kCombineThreads];
+  __shared__ float red[8];
   __shared__ float osh[kCombineThreads];
   const int64_t u = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t rs = D + 4;
   const float* r = part + u * nsplit * rs;
-  float mx = -INFINITY;
-  for (int s = tid; s < nsplit; s += kCombineThreads) {
-    const float v = r[s * rs];
-    wsh[s] = v;
-    mx = fmaxf(mx, v);
+  const int d = tid % D, g = tid / D, ng = kCombineThreads / D;
+  float2 ml[kCombineML];
+#pragma unroll
+  for (int k = 0; k < kCombineML; ++k) {
+    const int s = tid + k * kCombineThreads;
+    ml[k] = s < nsplit ? *reinterpret_cast<const float2*>(r + s * rs) : make_float2(-INFINITY, 0.f);
   }
+  float o[kCombineUnroll];
+#pragma unroll
+  for (int k = 0; k < kCombineUnroll; ++k) {
+    const int s = g + k * ng;
+    o[k] = s < nsplit ? r[s * rs + 4 + d] : 0.f;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kCombineML; ++k) mx = fmaxf(mx, ml[k].x);
   mx = group_max<64>(mx);
   if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float L = 0.f;
-  for (int s = tid; s < nsplit; s += kCombineThreads) {
-    const float w = wsh[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wsh[s] - M);
-    wsh[s] = w;
-    L = __builtin_fmaf(r[s * rs + 1], w, L);
+#pragma unroll
+  for (int k = 0; k < kCombineML; ++k) {
+    const int s = tid + k * kCombineThreads;
+    if (s < nsplit) {
+      const float w = ml[k].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - M);
+      wsh[s] = w;
+      L = __builtin_fmaf(ml[k].y, w, L);
+    }
   }
   L = group_sum<64>(L);
-  __syncthreads();
   if ((tid & 63) == 0) red[4 + (tid >> 6)] = L;
   __syncthreads();
   L = (red[4] + red[5]) + (red[6] + red[7]);
-  // thread t: element d = t % D over splits s = g, g + ng, ... (g = t / D, ng = 256 / D)
-  const int d = tid % D, g = tid / D, ng = kCombineThreads / D;
   float acc = 0.f;
-  for (int s0 = g; s0 < nsplit; s0 += ng * kCombineUnroll) {
-    float o[kCombineUnroll];
+#pragma unroll
+  for (int k = 0; k < kCombineUnroll; ++k) {
+    const int s = g + k * ng;
+    if (s < nsplit) acc = __builtin_fmaf(o[k], wsh[s], acc);
+  }
+  for (int s0 = g + kCombineUnroll * ng; s0 < nsplit; s0 += ng * kCombineUnroll) {
 #pragma unroll
     for (int k = 0; k < kCombineUnroll; ++k) {
       const int s = s0 + k * ng;

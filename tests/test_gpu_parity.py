@@ -115,6 +115,9 @@ DECODE_CASES = [
     ("bf16-g8-d64", 1, 2, 16, 64, 33, 40, torch.bfloat16, True),
     ("bf16-g2", 2, 3, 6, 128, 1, 8, torch.bfloat16, False),
     ("f32-g4", 1, 2, 8, 128, 300, 300, torch.float32, True),
+    # several tiles per wave, so every ring buffer is refilled; chunks that are not whole tiles
+    ("bf16-g4-long", 1, 8, 32, 128, 16400, 16400, torch.bfloat16, True),
+    ("bf16-g4-d64-long", 1, 4, 16, 64, 40000, 40000, torch.bfloat16, False),
 ]
 
 
