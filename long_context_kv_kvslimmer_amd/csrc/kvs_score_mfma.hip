@@ -157,7 +157,10 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
   uint8_t* vr_g = vr + grp * kRing2 * M::TILEB;
   int32_t* nr_g = nr + grp * kRing2 * kT2;
 
-  auto issue = [&](int t) {
+  // K tile j (with its counts) and V tile j go to ring slot j % 4 of their own ring.  The
+  // loop below issues K(t + 3) and V(t + 2) at the top of iteration t, in that order: V is
+  // consumed one iteration after K, so its ring slot turns over one iteration later.
+  auto issue_k = [&](int t) {
     const int buf = t % kRing2;
     const int64_t t0 = g0 + (int64_t)t * kT2;
 #pragma unroll
@@ -165,34 +168,53 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
       const int u = j * kGroupWaves + gw;
       const int R = u * M::RPI + lane / M::CPR;
       const int c = (lane % M::CPR) ^ swz<D>(R);
-      const uint32_t off = (uint32_t)((t0 + R - lo) * M::ROWB) + (uint32_t)(c << 4);
-      dma16(rk, lds_addr(kr_g + buf * M::TILEB + u * 1024), off);
-      dma16(rv, lds_addr(vr_g + buf * M::TILEB + u * 1024), off);
+      dma16(rk, lds_addr(kr_g + buf * M::TILEB + u * 1024), (uint32_t)((t0 + R - lo) * M::ROWB) + (uint32_t)(c << 4));
     }
     if (HAS_N && gw == 0 && lane < kT2) dma4(rn, lds_addr(nr_g + buf * kT2), (uint32_t)((t0 + lane - lo) * 4));
   };
-  auto wait_tile = [&](int later) {   // tiles of this group issued after the awaited one: 0..2
-    if (HAS_N && gw == 0) {
-      if (later >= 2) wait_vm<2 * (2 * M::IPW + 1)>();
-      else if (later == 1) wait_vm<2 * M::IPW + 1>();
-      else wait_vm<0>();
+  auto issue_v = [&](int t) {
+    const int buf = t % kRing2;
+    const int64_t t0 = g0 + (int64_t)t * kT2;
+#pragma unroll
+    for (int j = 0; j < M::IPW; ++j) {
+      const int u = j * kGroupWaves + gw;
+      const int R = u * M::RPI + lane / M::CPR;
+      const int c = (lane % M::CPR) ^ swz<D>(R);
+      dma16(rv, lds_addr(vr_g + buf * M::TILEB + u * 1024), (uint32_t)((t0 + R - lo) * M::ROWB) + (uint32_t)(c << 4));
+    }
+  };
+  // Wait at the top of iteration t until K(t + 1) has landed (and with it every earlier
+  // load, V(t - 1) included); issued after K(t + 1) are V(t), K(t + 2) if it exists, and
+  // V(t + 1).  In the last iteration everything is awaited (V(t) feeds the final product).
+  const bool nload = HAS_N && gw == 0;   // this wave also loads the counts with each K tile
+  auto wait_top = [&](int t) {
+    if (t + 1 >= nt) {
+      wait_vm<0>();
+    } else if (t + 2 < nt) {
+      if (nload) wait_vm<3 * M::IPW + 1>();
+      else wait_vm<3 * M::IPW>();
     } else {
-      if (later >= 2) wait_vm<2 * (2 * M::IPW)>();
-      else if (later == 1) wait_vm<2 * M::IPW>();
-      else wait_vm<0>();
+      wait_vm<2 * M::IPW>();
     }
   };
 
-  // tile 0 and the query operands travel together; later tiles are issued once they are in
-  // (loads complete in order, so waiting on the queries waits on tile 0 as well)
-  if (nt > 0) issue(0);
+  // K(0), K(1), V(0) and the query operands travel together (loads complete in order, so
+  // waiting on the queries waits on the tiles as well); then K(2), V(1), the loads of
+  // iteration -1
+  {   // the first iteration reads V^T from ring slot 3 and multiplies it by a zero P^T: keep it finite
+    uint4* z = reinterpret_cast<uint4*>(vr_g + (kRing2 - 1) * M::TILEB);
+    for (int i = gt; i < M::TILEB / 16; i += kGT) z[i] = make_uint4(0, 0, 0, 0);
+  }
+  if (nt > 0) issue_k(0);
+  if (nt > 1) issue_k(1);
+  if (nt > 0) issue_v(0);
   const bf16* Qp = static_cast<const bf16*>(a.Qw) + ((b * a.Hq + hk * a.G) * (int64_t)a.W) * D;
   const int64_t q = qb * kQB + gw * 32 + c32;
   bf16x8_t qop[KS];
   load_rows32<D>(Qp, a.GW, q, qop);
   asm volatile("" ::"v"(qop[KS - 1]));
-  if (nt > 1) issue(1);
-  if (nt > 2) issue(2);
+  if (nt > 2) issue_k(2);
+  if (nt > 1) issue_v(1);
 
   const float cs = a.scale * kLog2e;
   float m = kNoMax, lsum = 0.f;
@@ -231,20 +253,18 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     }
   };
 
-  // softmax of tile t from S^T in registers: P^T operands (bf16 hi + lo, two 16-slot k steps)
-  auto softmax = [&](int t, const f32x16_t& st, bf16x8_t (&phi)[2], bf16x8_t (&plo)[2]) {
+  // logits of tile t in log2 units are e[i] * sc: inside the group's range without counts
+  // e = S^T and sc = scale * log2(e); otherwise e carries the scale, the count bias and
+  // -inf for slots outside the range, and sc = 1
+  auto logits = [&](int t, const f32x16_t& st, float (&e)[16], float& sc) {
     const int buf = t % kRing2;
     const int64_t t0 = g0 + (int64_t)t * kT2;
-    const bool plain = !HAS_N && t0 >= lo && t0 + kT2 <= hi;
-    float e[16];
-    float mx;
-    if (plain) {
-      mx = st[0];
+    if (!HAS_N && t0 >= lo && t0 + kT2 <= hi) {
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st[i]);
-      mx = max_halves(mx) * cs;
+      for (int i = 0; i < 16; ++i) e[i] = st[i];
+      sc = cs;
     } else {
-      mx = -INFINITY;
+      sc = 1.f;
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
         int4 n4 = make_int4(1, 1, 1, 1);
@@ -255,28 +275,30 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
           const int64_t s = t0 + 8 * k4 + 4 * h + r;
           const float lg = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)nn[r]) : 0.f) : -INFINITY;
           e[4 * k4 + r] = __builtin_fmaf(st[4 * k4 + r], cs, lg);
-          mx = fmaxf(mx, e[4 * k4 + r]);
         }
       }
-      mx = max_halves(mx);
     }
-    if (mx > m + kLazyMax) {   // raise the reference only when P could exceed 2^8
-      const float corr = __builtin_amdgcn_exp2f(m - mx);
-      lsum *= corr;
+  };
+
+  // softmax of one tile from its logits, with no branch: the reference maximum m rises only
+  // when the tile maximum exceeds it by more than 2^8 (then corr = 2^(m_old - m_new) < 1,
+  // otherwise corr = 1 exactly); the caller rescales the output accumulators by corr.
+  // P^T operands come out as bf16 hi + lo for two 16-slot k steps.
+  auto softmax = [&](const float (&e)[16], float sc, bf16x8_t (&phi)[2], bf16x8_t (&plo)[2], float& corr) {
+    float mx = e[0];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= corr;
-      m = mx;
-    }
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, e[i]);
+    mx = max_halves(mx) * sc;
+    const float mn = mx > m + kLazyMax ? mx : m;
+    corr = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
     float p[16];
-    if (plain) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[i], cs, -m));
-    } else {
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(e[i], sc, -m));
+    float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(e[i] - m);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) lsum += p[i];
+    for (int i = 0; i < 16; ++i) ls += p[i];
+    lsum = __builtin_fmaf(lsum, corr, ls);
     // k index (h, j) of step ks <-> slot 16 ks + 8 (j / 4) + 4 h + j % 4: the lane's p[8 ks + j]
     split_hi_lo(p, phi[0], plo[0]);
     split_hi_lo(p + 8, phi[1], plo[1]);
@@ -300,57 +322,91 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     }
   };
 
-  if (nt > 0) wait_tile(nt - 1 < 2 ? nt - 1 : 2);
-  __syncthreads();
+  // O^T += V^T . P^T of one tile
+  auto pv = [&](const bf16x8_t (&vop)[2][DB], const bf16x8_t (&phi)[2], const bf16x8_t (&plo)[2]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        acc[db] = mfma32(vop[ks][db], phi[ks], acc[db]);
+        acc[db] = mfma32(vop[ks][db], plo[ks], acc[db]);
+      }
+  };
+
+  // Software pipeline: iteration t computes the softmax of tile t on the vector units while
+  // the matrix cores run S^T of tile t + 1 and O^T += V^T . P^T of tile t - 1.  The three
+  // are independent, so the scheduler interleaves the MFMAs with the softmax instructions
+  // in one straight block; the first iteration multiplies a zero P^T.
+  __syncthreads();   // K(0) of both groups is in (each wave waited on its own loads)
   f32x16_t s_cur;
   if (nt > 0) s_cur = qk(0);
+  bf16x8_t pphi[2], pplo[2];
+  {
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      pphi[ks] = as_bf16x8(zero);
+      pplo[ks] = as_bf16x8(zero);
+    }
+  }
   for (int t = 0; t < nt0; ++t) {
     const bool act = t < nt;
-    if (act && t + 1 < nt) {
-      const int issued = t + 2 < nt - 1 ? t + 2 : nt - 1;
-      wait_tile(issued - (t + 1));
-    }
+    if (act) wait_top(t);
     __syncthreads();
     if (act) {
-      if (t + 3 < nt) issue(t + 3);
+      if (t + 3 < nt) issue_k(t + 3);
+      if (t + 2 < nt) issue_v(t + 2);
       if (do_cos) cosines(t);
-      const bool more = t + 1 < nt;
-      // 1. operand reads first: K rows of tile t + 1 and V^T of tile t (first k step)
-      bf16x8_t ka[KS], v0[DB], v1[DB];
-      if (more) {
+      float e[16], sc;
+      logits(t, s_cur, e, sc);
+      // operands: K rows of tile t + 1 (stale past the last tile; that product is unused)
+      // and V^T of tile t - 1 (stale in the first iteration, where P^T is zero)
+      bf16x8_t ka[KS], vop[2][DB];
+      {
         const uint8_t* K_ = kr_g + ((t + 1) % kRing2) * M::TILEB;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(c32, 2 * ks + h)));
       }
-      read_vt(t, 0, v0);
+      read_vt(t + kRing2 - 1, 0, vop[0]);
+      read_vt(t + kRing2 - 1, 1, vop[1]);
       __builtin_amdgcn_sched_barrier(0);
-      // 2. softmax of tile t (vector units) while the reads land
-      bf16x8_t phi[2], plo[2];
-      softmax(t, s_cur, phi, plo);
-      __builtin_amdgcn_sched_barrier(0);
-      // 3. S^T of tile t + 1 on the matrix cores, then the second V^T k step is read
       f32x16_t s_next;
-      if (more) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s_next[i] = 0.f;
+      for (int i = 0; i < 16; ++i) s_next[i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s_next = mfma32(ka[ks], qop[ks], s_next);
+      for (int ks = 0; ks < KS; ++ks) s_next = mfma32(ka[ks], qop[ks], s_next);
+      bf16x8_t phi[2], plo[2];
+      float corr;
+      softmax(e, sc, phi, plo, corr);
+      pv(vop, pphi, pplo);
+      // the softmax starts while the operand reads land, then MFMAs and softmax alternate
+      __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+#pragma unroll
+      for (int i = 0; i < KS + 4 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // then softmax instructions
       }
-      read_vt(t, 1, v1);
-      // 4. O^T += V^T . P^T for tile t
+      __builtin_amdgcn_sched_barrier(0);
+      // the softmax results are needed here, so nothing of it sinks below the branch
+      asm volatile("" ::"v"(phi[0]), "v"(phi[1]), "v"(plo[0]), "v"(plo[1]), "v"(lsum));
+      if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        acc[db] = mfma32(v0[db], phi[0], acc[db]);
-        acc[db] = mfma32(v0[db], plo[0], acc[db]);
+        for (int db = 0; db < DB; ++db) acc[db] *= corr;
       }
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        acc[db] = mfma32(v1[db], phi[1], acc[db]);
-        acc[db] = mfma32(v1[db], plo[1], acc[db]);
+      for (int ks = 0; ks < 2; ++ks) {
+        pphi[ks] = phi[ks];
+        pplo[ks] = plo[ks];
       }
       s_cur = s_next;
     }
+  }
+  if (nt > 0) {
+    bf16x8_t vop[2][DB];
+    read_vt(nt - 1, 0, vop[0]);
+    read_vt(nt - 1, 1, vop[1]);
+    pv(vop, pphi, pplo);
   }
 
   // merge the two groups' running states through LDS, then write the partial records with
@@ -632,6 +688,9 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     const uint4 k1 = *reinterpret_cast<const uint4*>(K_ + chunk_off<D>(16 + pn, ch));
     const uint4 v0 = *reinterpret_cast<const uint4*>(V_ + chunk_off<D>(pn, ch));
     const uint4 v1 = *reinterpret_cast<const uint4*>(V_ + chunk_off<D>(16 + pn, ch));
+    // tile start: its pairs go to rows pos0 + pn (c0 - S is even, so is the tile start - S)
+    const int64_t t0m = c0 + (int64_t)tt * kT2;
+    const int64_t pos0 = a.S + (t0m - a.S) / 2;
     if (m0 >= a.S && m0 + 1 < pend && m0 >= lo && m0 + 1 < hi) {
       const int ls = tt * kT2 + 2 * pn;
       float g0 = 0.f, g1 = 0.f, gx = 0.f;
@@ -650,12 +709,12 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       unpack<bf16>(v1, vf1);
       merge_pair_elems<E>(kf0, kf1, vf0, vf1, w0, w1, n0, n1, ko, vo);
       const int nt = n0 + n1;
-      const int64_t pos = a.S + (m0 - a.S) / 2;
-      store_elems<TO, E>(Ko + pos * D + ch * E, ko);
-      store_elems<TO, E>(Vo + pos * D + ch * E, vo);
+      const int lofs = pn * D + ch * E;
+      store_elems<TO, E>(Ko + pos0 * D + lofs, ko);
+      store_elems<TO, E>(Vo + pos0 * D + lofs, vo);
       if (ch == 0) {
-        no[pos] = nt;
-        so[pos] = (int32_t)m0;
+        no[pos0 + pn] = nt;
+        so[pos0 + pn] = (int32_t)m0;
       }
     } else {
       // slots outside the candidate pairs (or a pair cut by the chunk edge) are copied
