@@ -25,6 +25,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV tokens merged/sec + achieved HBM GB/s (Llama-3.1-8B layer, 32K ctx)"
 HBM_PEAK_GBS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+SIMDS = 1024                    # 256 CUs x 4 SIMDs
+PEAK_CLOCK_GHZ = 2.4
 
 
 def kernel_bytes(N, H, D, P, T, GW, has_n=False, elt=2):
@@ -165,6 +168,47 @@ def summarize_trace(stats_csv, bench_json, cmd):
     return "\n".join(out) + "\n"
 
 
+def summarize_mfma(sq_csv, stats_csv, cmd):
+    """Markdown summary of a rocprofv3 --pmc run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and
+    SQ_VALU_MFMA_BUSY_CYCLES (per-dispatch sums over the chip) next to each kernel's mean
+    duration from a kernel-trace run: bf16 MFMA work per launch, achieved rate against the
+    dense bf16 peak, and matrix-core busy cycles per SIMD against the launch duration."""
+    import csv
+    import statistics
+    per = {}
+    for r in csv.DictReader(open(sq_csv)):
+        lab = kernel_label(r["Kernel_Name"])
+        if lab:
+            per.setdefault((lab, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    dur = {}
+    for r in csv.DictReader(open(stats_csv)):
+        lab = kernel_label(r["Name"])
+        if lab:
+            c, t = dur.get(lab, (0, 0.0))
+            dur[lab] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
+    out = ["# MFMA work and utilisation of the scorer, C2 layer (32K ctx, 8x128 KV heads, bf16)", "", "Made by:", "",
+           "```", cmd, "```", "",
+           f"Peak: dense bf16 MFMA {PEAK_MFMA_BF16_TFLOPS} TFLOP/s; {SIMDS} SIMDs at {PEAK_CLOCK_GHZ} GHz.  FLOP per "
+           "launch = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the counter's unit).  Busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+           "SIMDs / (mean duration x peak clock).", "",
+           "| kernel | MFMA instructions | GFLOP per launch | mean us | TFLOP/s | of peak | MFMA busy per SIMD |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for lab in sorted({k[0] for k in per}):
+        mops = per.get((lab, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+        if not mops or statistics.mean(mops) == 0 or lab not in dur:
+            continue
+        flop = statistics.mean(mops) * 512
+        inst = statistics.mean(per.get((lab, "SQ_INSTS_MFMA"), [float("nan")]))
+        busy = statistics.mean(per.get((lab, "SQ_VALU_MFMA_BUSY_CYCLES"), [float("nan")]))
+        c, t = dur[lab]
+        us = t / c / 1e3
+        tf = flop / (us * 1e-6) / 1e12
+        frac_busy = busy / SIMDS / (us * 1e-6 * PEAK_CLOCK_GHZ * 1e9)
+        out.append(f"| {lab} | {inst:.0f} | {flop / 1e9:.2f} | {us:.2f} | {tf:.1f} | {tf / PEAK_MFMA_BF16_TFLOPS:.3f} | "
+                   f"{frac_busy:.3f} |")
+    return "\n".join(out) + "\n"
+
+
 def copy_calibration(dev):
     """A plain copy of known size for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -199,6 +243,123 @@ def cpu_baseline(cfg, K, V, Qw, heads=2):
                       f"one decode query, fp64 NumPy, 1 BLAS thread, {dt:.1f} s"}
 
 
+def per_config(dev, which, reps=5):
+    """Per-config GPU timings (not the bench line): every merge round of one layer of each
+    seeded workload, on the fastest entry points the library offers (kvs_score_merge for full
+    rounds, kvs_score -> kvs_merge_weights -> kvs_merge_compact for partial ones), timed with
+    events on the library's stream over `reps` repetitions after one warm-up; all layers of a
+    config have the same shape, so the whole-model time is the per-layer time x layers.  The
+    decode workload (C5) appends one token per step and times each kvs_decode_attn."""
+    import statistics
+    import torch
+    from long_context_kv_kvslimmer_amd import configs, pipeline, synth
+    from long_context_kv_kvslimmer_amd import kvslim as L
+    lines = []
+    for idx in which:
+        cfg = configs.CONFIGS[idx]
+        layer = 0
+        K0, V0, last = pipeline.config_cache(cfg, layer, dev)
+        elt = K0.element_size()
+        row = 2 * cfg.head_dim * elt           # K + V bytes of one slot
+        plan = []
+        K, V, n, N = K0, V0, None, cfg.n_slots
+        alg = 0
+        for r, M in enumerate(cfg.rounds):
+            Qw = torch.stack([synth.window_queries(cfg, layer, b, r, dev) for b in range(cfg.batch)])
+            cap = N - M + (cfg.decode_steps if r == len(cfg.rounds) - 1 else 0)
+            bufs = pipeline.alloc_round(K, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, n_slots=N,
+                                        out_capacity=cap, want_flags=False)
+            P = L.num_pairs(N, cfg.n_sink, cfg.n_recent)
+            full = M == P
+            # K and V are read by both scorer passes (and once more by a separate merge), the
+            # merged rows are written once
+            reads = (2 if full else 3) * N * row + (N * 4 if n is not None else 0)
+            alg += cfg.batch * cfg.kv_heads * (reads + (N - M) * (row + 8))
+            plan.append((K, V, n, Qw, M, N, full, bufs))
+            K, V, n, N = bufs.K, bufs.V, bufs.n, N - M
+
+        def rounds():
+            for (Ki, Vi, ni, Qw, M, Ni, full, bufs) in plan:
+                if full:
+                    pipeline.run_full_round_fused(Ki, Vi, ni, Qw, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent,
+                                                  bufs, n_slots=Ni)
+                else:
+                    pipeline.run_round(Ki, Vi, ni, Qw, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, bufs,
+                                       n_slots=Ni)
+
+        rounds()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rounds()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = statistics.median(times)
+        tokens = cfg.batch * cfg.n_slots
+        res = {"config": f"C{cfg.idx} {cfg.name}", "batch": cfg.batch, "layers": cfg.layers,
+               "rounds": list(cfg.rounds), "merge_ms_per_layer": round(ms, 4),
+               "merge_ms_all_layers": round(ms * cfg.layers, 3),
+               "merge_tokens_per_s": round(tokens / (ms * 1e-3), 1),
+               "merge_algorithmic_MB_per_layer": round(alg / 1e6, 2),
+               "merge_GBps": round(alg / (ms * 1e-3) / 1e9, 1)}
+        if cfg.decode_steps:
+            bufs = plan[-1][7]
+            Kc, Vc, nc = bufs.K, bufs.V, bufs.n
+            steps = cfg.decode_steps
+            k_new, v_new = synth.decode_tokens(cfg, layer, 0, last[0], steps, dev)
+            # step t reads only the first N + t + 1 slots, so every token can be appended first
+            # and the steps enqueued back to back
+            Kc[0, :, N:N + steps] = k_new
+            Vc[0, :, N:N + steps] = v_new
+            nc[0, :, N:N + steps] = 1
+            descs = [L.cache_desc(Kc, cfg.q_heads, N + t + 1) for t in range(steps)]
+            qs = [synth.decode_query(cfg, layer, 0, t, dev)[None].contiguous() for t in range(steps)]
+            ws = torch.zeros(max(L.workspace_bytes(L.KVS_OP_DECODE, descs[-1], None), 16), dtype=torch.uint8,
+                             device=dev)
+            out = torch.empty(cfg.batch, cfg.q_heads, cfg.head_dim, dtype=torch.float32, device=dev)
+            scale = 1.0 / math.sqrt(cfg.head_dim)
+
+            def decode_all():
+                for t in range(steps):
+                    L.kvs_decode_attn(descs[t], Kc, Vc, nc, qs[t], scale, out, ws)
+
+            decode_all()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            decode_all()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            marks = L.KernelMarks(max_launches=4 * steps)
+            with marks:
+                decode_all()
+            torch.cuda.synchronize()
+            kt = {}
+            for name, kms in marks.times():
+                kt.setdefault(name, []).append(kms * 1e3)
+            mid = steps // 2
+            dbytes = cfg.batch * cfg.kv_heads * (N + mid + 1) * (row + 4)
+            kd = statistics.median(kt["decode"])
+            res.update({"decode_steps": steps, "decode_slots": [N + 1, N + steps],
+                        "decode_us_per_layer_step": round(us, 2),
+                        "decode_ms_per_step_all_layers": round(us * cfg.layers / 1e3, 4),
+                        "decode_kernel_us": round(kd, 2),
+                        "decode_combine_us": round(statistics.median(kt["combine"]), 2),
+                        "decode_kernel_GBps": round(dbytes / (kd * 1e-6) / 1e9, 1),
+                        "decode_step_GBps": round(dbytes / (us * 1e-6) / 1e9, 1),
+                        "decode_note": "per step: kvs_decode_attn calls enqueued back to back (decode kernel + "
+                                       "combine); kernel times from library event marks (include ~1 us of mark gap)"})
+        lines.append(res)
+        print(json.dumps(res), flush=True)
+        del plan, K0, V0
+        torch.cuda.empty_cache()
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,7 +371,13 @@ def main():
                     help="run a plain 1 GiB copy first (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "CMD"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "BENCH_JSON", "CMD"))
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("SQ_CSV", "STATS_CSV", "CMD"))
+    ap.add_argument("--per-config", type=str, default=None, metavar="1,2,3,4,5",
+                    help="print per-config merge and decode timings (one JSON line per config) instead of the bench line")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        sys.stdout.write(summarize_mfma(*args.summarize_mfma))
+        return
     if args.summarize_counters:
         sys.stdout.write(summarize_counters(*args.summarize_counters))
         return
@@ -219,7 +386,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported (each (batch, layer, "
-              f"kv-head) slice is independent, see DESIGN.md for how the path shards)", file=sys.stderr)
+              f"kv-head) slice is independent: shard by KV head, layer or batch, one process per GPU)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -228,6 +396,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.per_config:
+        per_config(dev, [int(x) for x in args.per_config.split(",")])
+        return
     cfg = configs.C2
     if args.copy_calibration:
         copy_calibration(dev)
