@@ -209,6 +209,36 @@ def summarize_mfma(sq_csv, stats_csv, cmd):
     return "\n".join(out) + "\n"
 
 
+def summarize_per_config(jsonl, cmd):
+    """Markdown table of the JSON lines printed by `bench.py --per-config`."""
+    rows = [json.loads(line) for line in open(jsonl) if line.startswith("{")]
+    out = ["# Per-config GPU timings (one layer of each seeded workload)", "", "Made by:", "", "```", cmd, "```", "",
+           "Merge rounds use kvs_score_merge for full rounds and kvs_score -> kvs_merge_weights -> kvs_merge_compact "
+           "for partial ones; median of 5 repetitions after a warm-up, events around the layer's rounds.  All layers "
+           "of a config have one shape, so the model-wide time is the per-layer time x layers.  Algorithmic MB: K "
+           "and V read by each pass that reads them (2 for a fused round, 3 for a partial round), merged rows "
+           "written once.", "",
+           "| config | batch x layers | rounds (pairs merged) | merge ms / layer | merge ms, all layers | tokens/s | "
+           "algorithmic MB / layer | GB/s |",
+           "|---|---|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| {r['config']} | {r['batch']} x {r['layers']} | {r['rounds']} | {r['merge_ms_per_layer']} | "
+                   f"{r['merge_ms_all_layers']} | {r['merge_tokens_per_s']:.3g} | "
+                   f"{r['merge_algorithmic_MB_per_layer']} | {r['merge_GBps']} |")
+    for r in rows:
+        if "decode_steps" in r:
+            out += ["", f"Decode ({r['config']}): {r['decode_steps']} steps over {r['decode_slots'][0]}.."
+                        f"{r['decode_slots'][1]} slots per head.", "",
+                    "| measure | value |", "|---|---:|",
+                    f"| per layer-step, calls back to back (decode kernel + combine) | "
+                    f"{r['decode_us_per_layer_step']} us, {r['decode_step_GBps']} GB/s |",
+                    f"| decode kernel (library event marks) | {r['decode_kernel_us']} us, "
+                    f"{r['decode_kernel_GBps']} GB/s |",
+                    f"| combine (library event marks) | {r['decode_combine_us']} us |",
+                    f"| per step, all {r['layers']} layers | {r['decode_ms_per_step_all_layers']} ms |"]
+    return "\n".join(out) + "\n"
+
+
 def copy_calibration(dev):
     """A plain copy of known size for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -372,9 +402,13 @@ def main():
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "CMD"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "BENCH_JSON", "CMD"))
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("SQ_CSV", "STATS_CSV", "CMD"))
+    ap.add_argument("--summarize-per-config", nargs=2, metavar=("JSONL", "CMD"))
     ap.add_argument("--per-config", type=str, default=None, metavar="1,2,3,4,5",
                     help="print per-config merge and decode timings (one JSON line per config) instead of the bench line")
     args = ap.parse_args()
+    if args.summarize_per_config:
+        sys.stdout.write(summarize_per_config(*args.summarize_per_config))
+        return
     if args.summarize_mfma:
         sys.stdout.write(summarize_mfma(*args.summarize_mfma))
         return
