@@ -225,6 +225,11 @@ def summarize_per_config(jsonl, cmd):
         out.append(f"| {r['config']} | {r['batch']} x {r['layers']} | {r['rounds']} | {r['merge_ms_per_layer']} | "
                    f"{r['merge_ms_all_layers']} | {r['merge_tokens_per_s']:.3g} | "
                    f"{r['merge_algorithmic_MB_per_layer']} | {r['merge_GBps']} |")
+    out += ["", "Kernel time per layer, summed over the layer's rounds (library event marks, one marked run; each "
+                "mark adds ~1 us):", "", "| config | kernels (us) |", "|---|---|"]
+    for r in rows:
+        ks = ", ".join(f"{k} {v}" for k, v in r.get("kernel_us_per_layer", {}).items())
+        out.append(f"| {r['config']} | {ks} |")
     for r in rows:
         if "decode_steps" in r:
             out += ["", f"Decode ({r['config']}): {r['decode_steps']} steps over {r['decode_slots'][0]}.."
@@ -328,13 +333,21 @@ def per_config(dev, which, reps=5):
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
         ms = statistics.median(times)
+        marks = L.KernelMarks(max_launches=64)
+        with marks:
+            rounds()
+        torch.cuda.synchronize()
+        per_kernel = {}
+        for name, kms in marks.times():
+            per_kernel[name] = round(per_kernel.get(name, 0.0) + kms * 1e3, 2)
         tokens = cfg.batch * cfg.n_slots
         res = {"config": f"C{cfg.idx} {cfg.name}", "batch": cfg.batch, "layers": cfg.layers,
                "rounds": list(cfg.rounds), "merge_ms_per_layer": round(ms, 4),
                "merge_ms_all_layers": round(ms * cfg.layers, 3),
                "merge_tokens_per_s": round(tokens / (ms * 1e-3), 1),
                "merge_algorithmic_MB_per_layer": round(alg / 1e6, 2),
-               "merge_GBps": round(alg / (ms * 1e-3) / 1e9, 1)}
+               "merge_GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+               "kernel_us_per_layer": per_kernel}
         if cfg.decode_steps:
             bufs = plan[-1][7]
             Kc, Vc, nc = bufs.K, bufs.V, bufs.n

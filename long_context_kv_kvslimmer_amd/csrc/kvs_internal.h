@@ -37,8 +37,13 @@ struct RoundP {
 };
 
 inline int64_t n_chunks(int64_t P) { return P > 0 ? (P + kChunkPairs - 1) / kChunkPairs : 1; }
-// int32 per (b, h) in the selection state: header + chunk offsets (n_chunks + 1), padded to 4.
-inline int64_t sel_stride_ints(int64_t P) { return ((kSelHeaderInts + n_chunks(P) + 1) + 3) / 4 * 4; }
+// Selection state per (b, h), in int32: header, chunk offsets (n_chunks + 1), padded to 4;
+// then the selection's own scratch: four 256-bin digit histograms and, per chunk, the
+// counts of keys equal to and above the threshold key.
+inline int64_t sel_hist_off(int64_t P) { return ((kSelHeaderInts + n_chunks(P) + 1) + 3) / 4 * 4; }
+inline int64_t sel_eq_off(int64_t P) { return sel_hist_off(P) + 4 * 256; }
+inline int64_t sel_gt_off(int64_t P) { return sel_eq_off(P) + n_chunks(P); }
+inline int64_t sel_stride_ints(int64_t P) { return (sel_gt_off(P) + n_chunks(P) + 3) / 4 * 4; }
 
 // ---- scorer ----
 size_t score_workspace_bytes(const Shape& s, const RoundP& r);

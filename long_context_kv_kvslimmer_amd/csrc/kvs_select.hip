@@ -3,31 +3,30 @@
 // Selection: in each (batch, kv-head) the n_merge candidate pairs with the largest
 // adjacent-key cosine, ties to the lower pair index (KVSlimmer deep-dive, section
 // 数学主线二: merge homogeneous adjacent keys; section 局限与边界: one uniform ratio for
-// every head).  One workgroup per (batch, head) runs an MSB-first radix select over the
-// order-preserving 32-bit image of the cosine (four 8-bit digit passes with an LDS
-// histogram), then finds the tie cut-off index with a block scan, then counts the
-// selected pairs of every 64-pair chunk and publishes their exclusive scan; the merge
-// pass uses those offsets for its cross-wave compaction.
+// every head).  An MSB-first radix select over the order-preserving 32-bit image of the
+// cosine finds the threshold key tau and how many keys equal to tau are taken: four
+// digit passes, each a grid of workgroups of 4096 pairs over every head that adds its
+// LDS histogram of one 8-bit digit into the head's global histogram (cosines of
+// neighbouring pairs share their leading digits, so each wave adds its most common digit
+// with one atomic); every later workgroup replays the earlier digit choices from those
+// histograms.  A count pass writes, per 64-pair chunk, the keys equal to and above tau;
+// one workgroup per head then scans them for the tie cut-off index and the exclusive
+// offsets of the selected pairs of every chunk, which the merge pass uses for its
+// compaction.  The histograms and counts live in the selection state after its header.
 #include "kvs_common.h"
 #include "kvs_internal.h"
 
 namespace kvs {
 
-struct SelArgs {
-  const float* g_self;
-  const float* g_cross;
-  const float* cos;
-  float* w;
-  uint8_t* selected;
-  int32_t* st;
-  int64_t N, S, P, M, nchunks, sel_stride;
-};
+constexpr int kSelThreads = 1024;                      // final workgroup (one per head)
+constexpr int kHistThreads = 256;                      // histogram and count passes
+constexpr int kHistKeys = 16;                          // keys per thread there
+constexpr int kHistBlock = kHistThreads * kHistKeys;   // pairs per workgroup (64 chunks)
 
-constexpr int kSelThreads = 1024;
-
-// Exclusive block-wide scan of one int per thread (kSelThreads threads); returns the
-// exclusive prefix, writes the block total to *total (same value in every thread).
-__device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 16 ints */) {
+// Exclusive scan of one int per thread over a workgroup of T threads; returns the
+// exclusive prefix and writes the workgroup total to *total.  Every thread must call it.
+template <int T>
+__device__ int block_exclusive_scan(int v, int* total, int* lds /* >= T / 64 ints */) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -38,7 +37,7 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 16 ints */
   if (lane == 63) lds[wv] = x;
   __syncthreads();
   int wave_pre = 0, tot = 0;
-  for (int k = 0; k < kSelThreads / 64; ++k) {
+  for (int k = 0; k < T / 64; ++k) {
     const int t = lds[k];
     if (k < wv) wave_pre += t;
     tot += t;
@@ -48,86 +47,164 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds /* >= 16 ints */
   return wave_pre + x - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
-  const int64_t bh = blockIdx.x;
+// Adds 1 to hist[d] for every lane with ok set: the digit of the wave's first such lane
+// with one atomic for all lanes that share it, the other lanes one atomic each.
+__device__ __forceinline__ void wave_hist_add(uint32_t* hist, bool ok, uint32_t d) {
+  const uint64_t act = __ballot(ok);
+  if (act == 0) return;
+  const int leader = __ffsll((unsigned long long)act) - 1;
+  const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+  const uint64_t same = __ballot(ok && d == ld);
+  if ((int)(threadIdx.x & 63) == leader) atomicAdd(&hist[ld], (uint32_t)__popcll(same));
+  if (ok && d != ld) atomicAdd(&hist[d], 1u);
+}
+
+// The radix select's state after `passes` digit passes, replayed from the head's global
+// histograms: prefix = the chosen leading digits, remaining = how many keys with that
+// prefix are still to be taken.  Digit s is the largest d whose count of keys >= d (among
+// keys with the prefix so far) reaches `remaining`.  All T threads call it.
+template <int T>
+__device__ void replay_digits(const int32_t* ghist, int passes, uint32_t M, uint32_t& prefix, uint32_t& remaining,
+                              uint32_t* sh /* 2 */, int* lds) {
   const int tid = threadIdx.x;
-  const float* cs = a.cos + bh * a.P;
-  int32_t* st = a.st + bh * a.sel_stride;
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_prefix, sh_remaining;
-  __shared__ int32_t sh_ptau;
-  __shared__ int scan_lds[16];
-
-  uint32_t tau;
-  int32_t p_tau;
-  if (a.M == 0) {
-    tau = 0xffffffffu;
-    p_tau = -1;
-  } else if (a.M == a.P) {
-    tau = 0u;
-    p_tau = (int32_t)(a.P - 1);
-  } else {
-    uint32_t prefix = 0, mask = 0, remaining = (uint32_t)a.M;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int d = tid; d < 256; d += kSelThreads) hist[d] = 0;
-      __syncthreads();
-      for (int64_t p = tid; p < a.P; p += kSelThreads) {
-        const uint32_t k = order_key(cs[p]);
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0;
-        int digit = 0;
-        for (int d = 255; d >= 0; --d) {
-          if (cum + hist[d] >= remaining) {
-            digit = d;
-            break;
-          }
-          cum += hist[d];
-        }
-        sh_prefix = prefix | ((uint32_t)digit << shift);
-        sh_remaining = remaining - cum;
-      }
-      __syncthreads();
-      prefix = sh_prefix;
-      remaining = sh_remaining;
-      mask |= 255u << shift;
+  prefix = 0;
+  remaining = M;
+  for (int s = 0; s < passes; ++s) {
+    const uint32_t v = tid < 256 ? (uint32_t)ghist[s * 256 + 255 - tid] : 0u;
+    int tot;
+    const uint32_t x = (uint32_t)block_exclusive_scan<T>((int)v, &tot, lds) + v;   // keys with digit >= 255 - tid
+    if (tid < 256 && x >= remaining && x - v < remaining) {
+      sh[0] = prefix | ((uint32_t)(255 - tid) << (24 - 8 * s));
+      sh[1] = remaining - (x - v);
     }
-    tau = prefix;
-    // the `remaining`-th smallest index among keys equal to tau
-    if (tid == 0) sh_ptau = -1;
     __syncthreads();
-    int base_count = 0;
-    for (int64_t base = 0; base < a.P; base += kSelThreads) {
-      const int64_t p = base + tid;
-      const int f = (p < a.P && order_key(cs[p]) == tau) ? 1 : 0;
-      int tot;
-      const int ex = block_exclusive_scan(f, &tot, scan_lds);
-      if (f && (uint32_t)(base_count + ex + 1) == remaining) sh_ptau = (int32_t)p;
-      base_count += tot;
-      __syncthreads();
-      if (sh_ptau >= 0) break;
-    }
-    p_tau = sh_ptau;
+    prefix = sh[0];
+    remaining = sh[1];
+    __syncthreads();
   }
-  SelHeader hd;
-  hd.tau_key = tau;
-  hd.p_tau = p_tau;
-  hd.n_merge = (int32_t)a.M;
-  hd.n_chunks = (int32_t)a.nchunks;
+}
 
-  // per-chunk selected counts -> exclusive offsets
+struct SelArgs {
+  const float* g_self;
+  const float* g_cross;
+  const float* cos;
+  float* w;
+  uint8_t* selected;
+  int32_t* st;
+  int64_t N, S, P, M, nchunks, sel_stride, hist_off, eq_off, gt_off;
+};
+
+// Clears the four digit histograms of every head.
+__global__ __launch_bounds__(kHistThreads) void sel_clear_kernel(SelArgs a) {
+  int32_t* h = a.st + (int64_t)blockIdx.x * a.sel_stride + a.hist_off;
+  for (int i = threadIdx.x; i < 4 * 256; i += kHistThreads) h[i] = 0;
+}
+
+// Digit pass `pass` (0 = the top 8 bits) over 4096 pairs of one head: LDS histogram of
+// the keys that carry the prefix chosen so far, added into the head's global histogram.
+__global__ __launch_bounds__(kHistThreads) void sel_hist_kernel(SelArgs a, int pass) {
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  int32_t* st = a.st + bh * a.sel_stride;
+  const float* cs = a.cos + bh * a.P;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[2];
+  __shared__ int lds[kHistThreads / 64];
+  uint32_t prefix, remaining;
+  replay_digits<kHistThreads>(st + a.hist_off, pass, (uint32_t)a.M, prefix, remaining, sh, lds);
+  const uint32_t mask = pass == 0 ? 0u : 0xffffffffu << (32 - 8 * pass);
+  const int shift = 24 - 8 * pass;
+  hist[tid] = 0;
+  __syncthreads();
+  const int64_t b0 = (int64_t)blockIdx.x * kHistBlock;
+#pragma unroll
+  for (int j = 0; j < kHistKeys; ++j) {
+    const int64_t p = b0 + j * kHistThreads + tid;
+    const uint32_t k = p < a.P ? order_key(cs[p]) : 0u;
+    wave_hist_add(hist, p < a.P && (k & mask) == prefix, (k >> shift) & 255u);
+  }
+  __syncthreads();
+  const uint32_t v = hist[tid];
+  if (v) atomicAdd(reinterpret_cast<uint32_t*>(st + a.hist_off + pass * 256 + tid), v);
+}
+
+// Per-chunk counts of keys equal to and above the threshold key tau.  Wave w at step j
+// holds the 64 pairs of chunk 64 blockIdx.x + 4 j + w.
+__global__ __launch_bounds__(kHistThreads) void sel_count_kernel(SelArgs a) {
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* st = a.st + bh * a.sel_stride;
+  const float* cs = a.cos + bh * a.P;
+  __shared__ uint32_t sh[2];
+  __shared__ int lds[kHistThreads / 64];
+  uint32_t tau, remaining;
+  replay_digits<kHistThreads>(st + a.hist_off, 4, (uint32_t)a.M, tau, remaining, sh, lds);
+  const int64_t b0 = (int64_t)blockIdx.x * kHistBlock;
+#pragma unroll
+  for (int j = 0; j < kHistKeys; ++j) {
+    const int64_t p = b0 + j * kHistThreads + tid;
+    const uint32_t k = p < a.P ? order_key(cs[p]) : 0u;
+    const uint64_t eq = __ballot(p < a.P && k == tau);
+    const uint64_t gt = __ballot(p < a.P && k > tau);
+    const int64_t c = b0 / kChunkPairs + j * (kHistThreads / 64) + wv;
+    if (lane == 0 && c < a.nchunks) {
+      st[a.eq_off + c] = __popcll(eq);
+      st[a.gt_off + c] = __popcll(gt);
+    }
+  }
+}
+
+// Tie cut-off index and chunk offsets of one head (one workgroup per head).
+__global__ __launch_bounds__(kSelThreads) void sel_final_kernel(SelArgs a) {
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* st = a.st + bh * a.sel_stride;
+  const float* cs = a.cos + bh * a.P;
+  __shared__ uint32_t sh[2];
+  __shared__ int lds[kSelThreads / 64];
+  __shared__ int64_t sh_ct;
+  __shared__ int32_t sh_rank, sh_ptau;
+  uint32_t tau, remaining;
+  replay_digits<kSelThreads>(st + a.hist_off, 4, (uint32_t)a.M, tau, remaining, sh, lds);
+  // the chunk that holds the `remaining`-th key equal to tau, and its rank there
+  if (tid == 0) {
+    sh_ct = -1;
+    sh_ptau = -1;
+  }
   int carry = 0;
   for (int64_t c0 = 0; c0 < a.nchunks; c0 += kSelThreads) {
     const int64_t c = c0 + tid;
-    int cnt = 0;
-    if (c < a.nchunks) {
-      const int64_t pe = min(a.P, (c + 1) * kChunkPairs);
-      for (int64_t p = c * kChunkPairs; p < pe; ++p) cnt += is_selected(order_key(cs[p]), p, hd) ? 1 : 0;
-    }
+    const int v = c < a.nchunks ? st[a.eq_off + c] : 0;
     int tot;
-    const int ex = block_exclusive_scan(cnt, &tot, scan_lds);
+    const uint32_t before = (uint32_t)(carry + block_exclusive_scan<kSelThreads>(v, &tot, lds));
+    if (v > 0 && before < remaining && remaining <= before + (uint32_t)v) {
+      sh_ct = c;
+      sh_rank = (int32_t)(remaining - before);   // 1-based
+    }
+    carry += tot;
+  }
+  __syncthreads();
+  const int64_t ct = sh_ct;
+  if (wv == 0 && ct >= 0) {   // the index of that key: wave 0 reads the chunk's 64 keys
+    const int64_t p = ct * kChunkPairs + lane;
+    const bool e = p < a.P && order_key(cs[p]) == tau;
+    const uint64_t m = __ballot(e);
+    if (e && __popcll(m & ((1ull << lane) - 1ull)) + 1 == sh_rank) sh_ptau = (int32_t)p;
+  }
+  __syncthreads();
+  SelHeader hd;
+  hd.tau_key = tau;
+  hd.p_tau = sh_ptau;
+  hd.n_merge = (int32_t)a.M;
+  hd.n_chunks = (int32_t)a.nchunks;
+  // selected per chunk: every key above tau, and the keys equal to tau up to the cut-off
+  carry = 0;
+  for (int64_t c0 = 0; c0 < a.nchunks; c0 += kSelThreads) {
+    const int64_t c = c0 + tid;
+    int v = 0;
+    if (c < a.nchunks) v = st[a.gt_off + c] + (c < ct ? st[a.eq_off + c] : c == ct ? sh_rank : 0);
+    int tot;
+    const int ex = block_exclusive_scan<kSelThreads>(v, &tot, lds);
     if (c < a.nchunks) st[kSelHeaderInts + c] = carry + ex;
     carry += tot;
   }
@@ -138,14 +215,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
     st[3] = hd.n_chunks;
     st[kSelHeaderInts + a.nchunks] = carry;
   }
-
   // optional per-pair outputs
   if (a.selected || a.w) {
     for (int64_t p = tid; p < a.P; p += kSelThreads) {
-      if (a.selected) {
-        const bool s = (a.M == a.P) || (a.M != 0 && is_selected(order_key(cs[p]), p, hd));
-        a.selected[bh * a.P + p] = s ? 1 : 0;
-      }
+      if (a.selected) a.selected[bh * a.P + p] = is_selected(order_key(cs[p]), p, hd) ? 1 : 0;
       if (a.w) {
         const int64_t m = a.S + 2 * p;
         float w0, w1;
@@ -198,12 +271,21 @@ hipError_t launch_select(const Shape& s, const RoundP& r, const float* g_self, c
   a.M = r.M;
   a.nchunks = n_chunks(r.P);
   a.sel_stride = sel_stride_ints(r.P);
-  const int blocks = s.B * s.Hkv;
-  if (blocks == 0) return hipSuccess;
-  if (cos == nullptr)
-    KVS_LAUNCH("select", select_fixed_kernel, dim3(blocks), dim3(kSelThreads), 0, st, a);
-  else
-    KVS_LAUNCH("select", select_kernel, dim3(blocks), dim3(kSelThreads), 0, st, a);
+  a.hist_off = sel_hist_off(r.P);
+  a.eq_off = sel_eq_off(r.P);
+  a.gt_off = sel_gt_off(r.P);
+  const int heads = s.B * s.Hkv;
+  if (heads == 0) return hipSuccess;
+  if (cos == nullptr || r.M == 0 || r.M == r.P) {
+    KVS_LAUNCH("select", select_fixed_kernel, dim3(heads), dim3(kSelThreads), 0, st, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((r.P + kHistBlock - 1) / kHistBlock), (unsigned)heads);
+  KVS_LAUNCH("select", sel_clear_kernel, dim3(heads), dim3(kHistThreads), 0, st, a);
+  for (int pass = 0; pass < 4; ++pass)
+    KVS_LAUNCH("select", sel_hist_kernel, grid, dim3(kHistThreads), 0, st, a, pass);
+  KVS_LAUNCH("select", sel_count_kernel, grid, dim3(kHistThreads), 0, st, a);
+  KVS_LAUNCH("select", sel_final_kernel, dim3(heads), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -58,10 +58,11 @@ def test_workspace_sizes(L):
     r = L.round_desc(32, 0, 32, 16368, 128 ** -0.5)
     assert L.workspace_bytes(L.KVS_OP_SCORE, c, r) > 0
     assert L.workspace_bytes(L.KVS_OP_SELECT, c, r) == 0
-    # selection state: header + one offset per 64-pair chunk + total, per (b, h)
+    # selection state per (b, h): header + one offset per 64-pair chunk + total (padded to
+    # 4 ints), then four 256-bin digit histograms and two counts per chunk
     P = 16368
     chunks = (P + 63) // 64
-    per = ((4 + chunks + 1) + 3) // 4 * 4
+    per = (((4 + chunks + 1) + 3) // 4 * 4 + 4 * 256 + 2 * chunks + 3) // 4 * 4
     assert L.workspace_bytes(L.KVS_OP_SEL_STATE, c, r) == 8 * per * 4
     assert L.workspace_bytes(L.KVS_OP_DECODE, c, None) > 0
     bad = _cache(D=96)
