@@ -187,16 +187,17 @@ __device__ __forceinline__ void closed_form_weights(float g11, float g12, float 
 // mean, with weights n_m / (n_m + n_{m+1}) and n_{m+1} / (n_m + n_{m+1}) formed once per
 // pair from one division (no counts: both weights are 1/2 exactly).
 template <int E>
-__device__ __forceinline__ void merge_pair_elems(const float* kf0, const float* kf1, const float* vf0,
-                                                 const float* vf1, float w0, float w1, int n0, int n1,
-                                                 float* ko, float* vo) {
+__device__ __forceinline__ void merge_keys(const float* kf0, const float* kf1, float w0, float w1, float* ko) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) ko[e] = __builtin_fmaf(w0, kf0[e], w1 * kf1[e]);
+}
+
+template <int E>
+__device__ __forceinline__ void merge_values(const float* vf0, const float* vf1, int n0, int n1, float* vo) {
   const float inv = 1.f / (float)(n0 + n1);
   const float u0 = (float)n0 * inv, u1 = (float)n1 * inv;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    ko[e] = __builtin_fmaf(w0, kf0[e], w1 * kf1[e]);
-    vo[e] = __builtin_fmaf(u0, vf0[e], u1 * vf1[e]);
-  }
+  for (int e = 0; e < E; ++e) vo[e] = __builtin_fmaf(u0, vf0[e], u1 * vf1[e]);
 }
 
 // Selection threshold of one (batch, head), written by the selection kernel.

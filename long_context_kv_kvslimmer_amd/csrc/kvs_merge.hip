@@ -155,7 +155,8 @@ __global__ __launch_bounds__(256) void merge_compact_kernel(MergeArgs a) {
             float vf0[E], vf1[E], ko[E], vo[E];
             unpack<TI>(va[u], vf0);
             unpack<TI>(vb[u], vf1);
-            merge_pair_elems<E>(kf0, kf1, vf0, vf1, w0, w1, n0[u], n1[u], ko, vo);
+            merge_keys<E>(kf0, kf1, w0, w1, ko);
+            merge_values<E>(vf0, vf1, n0[u], n1[u], vo);
             const int nt = n0[u] + n1[u];
             store_elems<TO, E>(Ko + pos * D + j * E, ko);
             store_elems<TO, E>(Vo + pos * D + j * E, vo);

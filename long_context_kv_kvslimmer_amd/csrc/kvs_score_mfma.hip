@@ -593,6 +593,7 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
   if (ntiles > 1) issue(1);
   if (ntiles > 2) issue(2);
   const float cs = a.scale * kLog2e;
+  const float ics = 1.f / cs;
 
   auto compute = [&](int t) {
     const int buf = t % kRing2;
@@ -607,6 +608,10 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       lgo = (se_ + 1 >= lo && se_ + 1 < hi) ? (HAS_N ? __log2f((float)nr[buf * kT2 + 16 + n16]) : 0.f) : -INFINITY;
     }
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    // the slot's log2 count enters S^T through the accumulator's starting value (divided
+    // by the logit scale), so each exponent argument is one fma
+    const f32x4_t be = {lge * ics, lge * ics, lge * ics, lge * ics};
+    const f32x4_t bo = {lgo * ics, lgo * ics, lgo * ics, lgo * ics};
     f32x4_t se[2], so[2], re[2], ro[2], gee = z, goo = z, geo = z;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -617,8 +622,8 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       const bf16x8_t vo = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(16 + n16, ch)));
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
-        se[q2] = mfma(qop[q2][ks], ke, ks == 0 ? z : se[q2]);
-        so[q2] = mfma(qop[q2][ks], ko, ks == 0 ? z : so[q2]);
+        se[q2] = mfma(qop[q2][ks], ke, ks == 0 ? be : se[q2]);
+        so[q2] = mfma(qop[q2][ks], ko, ks == 0 ? bo : so[q2]);
         re[q2] = mfma(ohi[q2][ks], ve, ks == 0 ? onv[q2] : re[q2]);
         ro[q2] = mfma(ohi[q2][ks], vo, ks == 0 ? onv[q2] : ro[q2]);
         re[q2] = mfma(olo[q2][ks], ve, re[q2]);
@@ -645,8 +650,8 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float ae = __builtin_amdgcn_exp2f(__builtin_fmaf(se[q2][r], cs, nbq[q2][r] + lge));
-        const float ao = __builtin_amdgcn_exp2f(__builtin_fmaf(so[q2][r], cs, nbq[q2][r] + lgo));
+        const float ae = __builtin_amdgcn_exp2f(__builtin_fmaf(se[q2][r], cs, nbq[q2][r]));
+        const float ao = __builtin_amdgcn_exp2f(__builtin_fmaf(so[q2][r], cs, nbq[q2][r]));
         const float rre = re[q2][r] + vne, rro = ro[q2][r] + vno;
         gse = __builtin_fmaf(ae * fabsf(__builtin_fmaf(-2.f, ae, 1.f)), __builtin_amdgcn_sqrtf(fabsf(rre)), gse);
         gso = __builtin_fmaf(ao * fabsf(__builtin_fmaf(-2.f, ao, 1.f)), __builtin_amdgcn_sqrtf(fabsf(rro)), gso);
@@ -702,16 +707,22 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       }
       float w0, w1;
       closed_form_weights(g0, gx, g1, w0, w1);
-      float kf0[E], kf1[E], vf0[E], vf1[E], ko[E], vo[E];
-      unpack<bf16>(k0, kf0);
-      unpack<bf16>(k1, kf1);
-      unpack<bf16>(v0, vf0);
-      unpack<bf16>(v1, vf1);
-      merge_pair_elems<E>(kf0, kf1, vf0, vf1, w0, w1, n0, n1, ko, vo);
-      const int nt = n0 + n1;
       const int lofs = pn * D + ch * E;
-      store_elems<TO, E>(Ko + pos0 * D + lofs, ko);
-      store_elems<TO, E>(Vo + pos0 * D + lofs, vo);
+      {   // keys, then values: half the live temporaries
+        float f0[E], f1[E], o[E];
+        unpack<bf16>(k0, f0);
+        unpack<bf16>(k1, f1);
+        merge_keys<E>(f0, f1, w0, w1, o);
+        store_elems<TO, E>(Ko + pos0 * D + lofs, o);
+      }
+      {
+        float f0[E], f1[E], o[E];
+        unpack<bf16>(v0, f0);
+        unpack<bf16>(v1, f1);
+        merge_values<E>(f0, f1, n0, n1, o);
+        store_elems<TO, E>(Vo + pos0 * D + lofs, o);
+      }
+      const int nt = n0 + n1;
       if (ch == 0) {
         no[pos0 + pn] = nt;
         so[pos0 + pn] = (int32_t)m0;
