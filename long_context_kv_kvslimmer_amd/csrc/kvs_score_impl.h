@@ -46,10 +46,10 @@ struct CosArgs {
   int Hkv;
 };
 
-// Slot splits of the VALU pass 1: about 512 slots per workgroup, at most 256 splits,
+// Slot splits of the VALU pass 1: at least 64 slots per workgroup, at most 256 splits,
 // every split non-empty.
 inline void valu_pass1_plan(int64_t N, int64_t& chunk, int& nsplit) {
-  int64_t k = (N + 511) / 512;
+  int64_t k = (N + 63) / 64;
   if (k < 1) k = 1;
   if (k > 256) k = 256;
   chunk = (N + k - 1) / k;
