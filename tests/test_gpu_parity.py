@@ -109,6 +109,44 @@ def test_selection_index_tie_break():
         check_round_slice(bufs, K, V, n, Qw, 0, 0, 512, 0, 0, M, 1 / math.sqrt(128), label=f"ties M={M}")
 
 
+def test_selection_large_ties_multiworkgroup():
+    """Selection over more than 65536 pairs per head (many 4096-pair workgroups, more than 1024
+    chunks) with long runs of bit-identical cosines at the threshold: the flags and the chunk
+    offsets in the selection state equal a brute-force top-M with the lower index winning ties."""
+    from long_context_kv_kvslimmer_amd import kvslim as L
+    H, P = 3, 150001
+    N = 2 * P + 1                                            # an odd leftover slot
+    K = torch.empty(1, H, N, 64, dtype=torch.bfloat16, device=DEV)   # layout only; select reads cos
+    rng = np.random.default_rng(7)
+    cos = np.empty((H, P), np.float32)
+    cos[0] = 0.875                                           # a single tie group
+    cos[1] = rng.choice(np.float32([0.5, 0.625, 0.75, 0.8125, 0.875, 0.9375, 0.96875]), size=P)
+    cos[2] = rng.uniform(0.6, 0.99, size=P).astype(np.float32)
+    cos_t = torch.from_numpy(cos)[None].contiguous().to(DEV)
+    cache = L.cache_desc(K, H)
+    nch = (P + 63) // 64
+    for M in (1, 4097, 65537, P // 2, P - 1):
+        print(f"\n[select] P={P} M={M}", flush=True)
+        rnd = L.round_desc(4, 0, 0, M, 0.125)
+        st = torch.zeros(L.workspace_bytes(L.KVS_OP_SEL_STATE, cache, rnd), dtype=torch.uint8, device=DEV)
+        selected = torch.empty(1, H, P, dtype=torch.uint8, device=DEV)
+        L.kvs_merge_weights(cache, rnd, None, None, cos_t, None, selected, st)
+        torch.cuda.synchronize()
+        sel = host(selected)[0].astype(bool)
+        sti = st.view(torch.int32).cpu().numpy()
+        stride = sti.size // H
+        for h in range(H):
+            order = np.lexsort((np.arange(P), -cos[h].astype(np.float64)))
+            ref = np.zeros(P, bool)
+            ref[order[:M]] = True
+            assert np.array_equal(sel[h], ref), f"flags h{h} M={M}"
+            per_chunk = np.zeros(nch * 64, np.int64)
+            per_chunk[:P] = ref
+            excl = np.concatenate([[0], np.cumsum(per_chunk.reshape(nch, 64).sum(1))])
+            offs = sti[h * stride + 4: h * stride + 4 + nch + 1]
+            assert np.array_equal(offs, excl), f"offsets h{h} M={M}"
+
+
 DECODE_CASES = [
     ("bf16-g4", 1, 8, 32, 128, 5000, 5100, torch.bfloat16, True),
     ("f32-g1-d64", 2, 1, 1, 64, 700, 700, torch.float32, False),
