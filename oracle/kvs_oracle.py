@@ -24,7 +24,7 @@ except the figure-2 caption's "Eq. 8"):
         are compressed losslessly.
 
 Readings of points the pages leave open are listed next to the function that
-takes them; the same list sits in the design doc.
+takes them, each with its label (O1, O2, ...).
 
 Pinned functions (tests/test_oracle_pins.py): every public function below is
 checked against something other than itself: finite differences, brute-force
