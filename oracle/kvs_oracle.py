@@ -381,6 +381,55 @@ def compose_src(prev_src: np.ndarray, src: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# 实验设置: chunked prefill under a fixed cache budget
+# ---------------------------------------------------------------------------
+@dataclass
+class StreamResult:
+    K: np.ndarray          # [T, D] final cache keys
+    V: np.ndarray          # [T, D] final slot mean values
+    n: np.ndarray          # [T] counts
+    start: np.ndarray      # [T] first original token position each slot covers
+    rounds: list           # (chunk index, N before the round, M, RoundResult)
+
+
+def stream_prefill(K, V, Qw_chunks, scale, n_sink, budget, chunk) -> StreamResult:
+    """The evaluation regime of [DD] 实验设置 (a fixed cache budget, the prompt
+    prefilled in fixed-size chunks, the first tokens kept): reading O21.
+
+    The raw tokens K, V [total, D] arrive in chunks of ``chunk`` (the last one
+    may be shorter).  After a chunk is appended the cache holds N slots; while
+    N > budget one merge round runs with M = min(N − budget, P) pairs,
+    P = num_pairs(N, n_sink, 0): the first n_sink slots never merge and no
+    recent window is protected (the pages name none in this setting).  The
+    round's observation window is Qw_chunks[c] ([GW, D]), the last queries of
+    chunk c.  Requires budget > n_sink, so that every round has a pair to merge.
+    """
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    total, D = K.shape
+    if chunk < 1 or n_sink < 0 or budget <= n_sink:
+        raise ValueError("need chunk >= 1 and budget > n_sink >= 0")
+    cK, cV = np.empty((0, D)), np.empty((0, D))
+    cn = np.empty(0, dtype=np.int64)
+    start = np.empty(0, dtype=np.int64)
+    rounds = []
+    for c, c0 in enumerate(range(0, total, chunk)):
+        c1 = min(total, c0 + chunk)
+        cK = np.vstack([cK, K[c0:c1]])
+        cV = np.vstack([cV, V[c0:c1]])
+        cn = np.concatenate([cn, np.ones(c1 - c0, dtype=np.int64)])
+        start = np.concatenate([start, np.arange(c0, c1, dtype=np.int64)])
+        while len(cn) > budget:
+            N = len(cn)
+            M = min(N - budget, num_pairs(N, n_sink, 0))
+            r = merge_round(cK, cV, cn, Qw_chunks[c], scale, n_sink, 0, M)
+            rounds.append((c, N, M, r))
+            cK, cV, cn = r.K, r.V, r.n
+            start = start[r.src]
+    return StreamResult(K=cK, V=cV, n=cn, start=start, rounds=rounds)
+
+
+# ---------------------------------------------------------------------------
 # 算一遍: KV bytes
 # ---------------------------------------------------------------------------
 def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, dtype_bytes: int) -> int:

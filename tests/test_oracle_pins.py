@@ -401,3 +401,85 @@ def test_kv_bytes_golden():
     for ctx, gib in g["per_request_gib_approx"].items():
         assert round(bpt * int(ctx) / 2**30) == gib
     assert round(8 * 32768 * bpt / 2**30) == g["batch8_32k_gib_approx"]
+
+
+# ------------------------------------------------------ chunked budget loop --
+def _stream_inputs(seed, total, D, GW, chunk, rho=0.9):
+    """AR(1) keys (similar neighbours), iid values, one window per chunk."""
+    rng = _rng(seed)
+    K = np.empty((total, D))
+    K[0] = rng.standard_normal(D)
+    for t in range(1, total):
+        K[t] = rho * K[t - 1] + math.sqrt(1 - rho * rho) * rng.standard_normal(D)
+    V = rng.standard_normal((total, D))
+    Qs = [rng.standard_normal((GW, D)) for _ in range(-(-total // chunk))]
+    return K, V, Qs
+
+
+def test_stream_under_budget_copies_the_tokens():
+    K, V, Qs = _stream_inputs(30, 90, 5, 3, 32)
+    s = O.stream_prefill(K, V, Qs, 0.4, 4, 90, 32)
+    assert s.rounds == []
+    assert np.array_equal(s.K, K) and np.array_equal(s.V, V)
+    assert np.array_equal(s.n, np.ones(90)) and np.array_equal(s.start, np.arange(90))
+
+
+def test_stream_single_chunk_is_one_merge_round():
+    K, V, Qs = _stream_inputs(31, 100, 5, 3, 100)
+    s = O.stream_prefill(K, V, Qs, 0.4, 4, 60, 100)
+    r = O.merge_round(K, V, None, Qs[0], 0.4, 4, 0, 40)
+    assert len(s.rounds) == 1 and s.rounds[0][1:3] == (100, 40)
+    assert np.allclose(s.K, r.K, atol=1e-14) and np.allclose(s.V, r.V, atol=1e-14)
+    assert np.array_equal(s.n, r.n) and np.array_equal(s.start, r.src)
+
+
+def test_stream_round_window_is_its_chunks_queries():
+    """The first round runs on raw tokens only: its lse must be the log-sum-exp of the
+    logits of the queries of the chunk that triggered it, over every slot held."""
+    from scipy.special import logsumexp
+    K, V, Qs = _stream_inputs(33, 160, 6, 3, 40)
+    s = O.stream_prefill(K, V, Qs, 0.35, 2, 100, 40)
+    c, N, M, r = s.rounds[0]
+    assert (c, N, M) == (2, 120, 20)
+    for w in range(3):
+        assert abs(r.lse[w] - logsumexp(0.35 * K[:N] @ Qs[c][w])) < 1e-12
+
+
+@pytest.mark.parametrize("total,budget,chunk,S", [(300, 64, 32, 4), (301, 64, 50, 0), (257, 40, 100, 8),
+                                                  (200, 17, 16, 16)])
+def test_stream_invariants(total, budget, chunk, S):
+    D = 12
+    K, V, Qs = _stream_inputs(32 + total, total, D, 4, chunk)
+    s = O.stream_prefill(K, V, Qs, 0.3, S, budget, chunk)
+    assert len(s.n) == min(total, budget)
+    # rounds merge at most the excess over the budget, and the last round of a chunk
+    # lands exactly on the budget; the cache never holds more than budget + chunk slots
+    last = {}
+    for c, N, M, r in s.rounds:
+        assert 1 <= M <= min(N - budget, O.num_pairs(N, S, 0))
+        assert len(r.n) == N - M and N <= budget + chunk
+        last[c] = N - M
+    assert all(v == budget for v in last.values())
+    assert s.n.sum() == total
+    # slots tile the token sequence in order
+    assert np.array_equal(s.start, np.concatenate([[0], np.cumsum(s.n)[:-1]]))
+    # the first tokens are kept verbatim
+    assert np.array_equal(s.K[:S], K[:S]) and np.array_equal(s.V[:S], V[:S]) and np.all(s.n[:S] == 1)
+    for j in range(len(s.n)):
+        a, m = s.start[j], s.n[j]
+        # lossless values: every slot holds the mean of the raw values it covers
+        assert np.allclose(s.V[j], V[a:a + m].mean(axis=0), atol=1e-12)
+        # merged keys are affine combinations of the raw keys they cover
+        if m == 1:
+            assert np.array_equal(s.K[j], K[a])
+        elif m <= D - 1:
+            X = (K[a + 1:a + m] - K[a]).T
+            y = s.K[j] - K[a]
+            coef = np.linalg.lstsq(X, y, rcond=None)[0]
+            assert np.linalg.norm(X @ coef - y) < 1e-9 * (1 + np.linalg.norm(s.K[j]))
+
+
+def test_stream_rejects_budget_not_above_sinks():
+    K, V, Qs = _stream_inputs(34, 20, 4, 2, 8)
+    with pytest.raises(ValueError):
+        O.stream_prefill(K, V, Qs, 0.3, 8, 8, 8)
