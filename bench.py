@@ -211,7 +211,9 @@ def summarize_mfma(sq_csv, stats_csv, cmd):
 
 def summarize_per_config(jsonl, cmd):
     """Markdown table of the JSON lines printed by `bench.py --per-config`."""
-    rows = [json.loads(line) for line in open(jsonl) if line.startswith("{")]
+    allrows = [json.loads(line) for line in open(jsonl) if line.startswith("{")]
+    rows = [r for r in allrows if "merge_ms_per_layer" in r]
+    streams = [r for r in allrows if "chunk_sweep" in r]
     out = ["# Per-config GPU timings (one layer of each seeded workload)", "", "Made by:", "", "```", cmd, "```", "",
            "Merge rounds use kvs_score_merge for full rounds and kvs_score -> kvs_merge_weights -> kvs_merge_compact "
            "for partial ones; median of 5 repetitions after a warm-up, events around the layer's rounds.  All layers "
@@ -241,6 +243,26 @@ def summarize_per_config(jsonl, cmd):
                     f"{r['decode_kernel_GBps']} GB/s |",
                     f"| combine (library event marks) | {r['decode_combine_us']} us |",
                     f"| per step, all {r['layers']} layers | {r['decode_ms_per_step_all_layers']} ms |"]
+    for r in streams:
+        ks = ", ".join(f"{k} {v}" for k, v in r["kernel_us_per_round"].items())
+        out += ["", f"Chunked prefill under a cache budget ({r['config']}): {r['tokens']} tokens x "
+                    f"{r['layers_folded_into_batch']} layers (folded into the batch) x {r['kv_heads']} KV heads, chunks "
+                    f"of {r['chunk']}, budget {r['budget']} slots, {r['n_sink']} kept first tokens; "
+                    f"{r['merge_rounds']} partial merge rounds.", "",
+                "| measure | value |", "|---|---:|",
+                f"| whole loop (appends + rounds, median of 5) | {r['loop_ms']} ms, "
+                f"{r['prefill_tokens_per_s']:.3g} tokens/s |",
+                f"| per round | {r['ms_per_round']} ms |",
+                f"| kernels per round (library event marks) | {ks} |",
+                f"| kernel time, whole loop | {r['kernel_us_total']} us |",
+                f"| merge algorithmic MB, whole loop | {r['merge_algorithmic_MB']} ({r['merge_kernel_GBps']} GB/s "
+                f"over kernel time) |",
+                f"| peak device memory the loop allocates | {r['peak_alloc_MB']} MB (uncompressed cache "
+                f"{r['full_cache_MB']} MB) |", "",
+                "Peak memory and loop time against chunk size:", "",
+                "| chunk | merge rounds | loop ms | peak alloc MB | two caches MB |", "|---:|---:|---:|---:|---:|"]
+        for c in r["chunk_sweep"]:
+            out.append(f"| {c['chunk']} | {c['rounds']} | {c['loop_ms']} | {c['peak_alloc_MB']} | {c['cache_MB']} |")
     return "\n".join(out) + "\n"
 
 
@@ -292,6 +314,12 @@ def per_config(dev, which, reps=5):
     lines = []
     for idx in which:
         cfg = configs.CONFIGS[idx]
+        if cfg.budget:
+            res = stream_timing(cfg, dev, reps)
+            lines.append(res)
+            print(json.dumps(res), flush=True)
+            torch.cuda.empty_cache()
+            continue
         layer = 0
         K0, V0, last = pipeline.config_cache(cfg, layer, dev)
         elt = K0.element_size()
@@ -401,6 +429,89 @@ def per_config(dev, which, reps=5):
         del plan, K0, V0
         torch.cuda.empty_cache()
     return lines
+
+
+def stream_timing(cfg, dev, reps=5, chunks=(256, 512, 1024, 2016)):
+    """Chunked prefill under a cache budget, all layers folded into the batch: the whole loop
+    (chunk appends + one partial merge round per chunk past the budget) timed with events on
+    the current stream, the library's kernels split by name with event marks, and the peak
+    device memory the loop allocates (two ping-pong caches, round statistics, workspaces)
+    measured for several chunk sizes against the uncompressed cache."""
+    import statistics
+    import torch
+    from long_context_kv_kvslimmer_amd import pipeline
+    from long_context_kv_kvslimmer_amd import kvslim as L
+    K_src, V_src, wq = pipeline.stream_inputs(cfg, dev)
+    B, H, total, D = K_src.shape
+    row = 2 * D * K_src.element_size()
+    full_mb = B * H * total * row / 1e6
+
+    def setup(chunk):
+        plan = pipeline.stream_schedule(total, cfg.budget, chunk, cfg.n_sink)
+        qws = [wq(c) if s.rounds else None for c, s in enumerate(plan)]
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        st = pipeline.alloc_stream(B, H, cfg.q_heads, D, K_src.dtype, dev, cfg.window, cfg.n_sink, plan)
+
+        def run():
+            return pipeline.run_stream(K_src, V_src, lambda c: qws[c], cfg.q_heads, cfg.window, cfg.n_sink,
+                                       plan, st)
+        run()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        return plan, st, run, peak
+
+    def timed(run, n):
+        times = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return statistics.median(times)
+
+    sweep = []
+    for chunk in chunks:
+        plan, st, run, peak = setup(chunk)
+        ms = timed(run, 3)
+        sweep.append({"chunk": chunk, "rounds": sum(len(s.rounds) for s in plan), "loop_ms": round(ms, 3),
+                      "peak_alloc_MB": round(peak / 1e6, 1),
+                      "cache_MB": round(2 * st.bufs[0].K.numel() * 2 * K_src.element_size() / 1e6, 1)})
+        del plan, st, run
+        torch.cuda.empty_cache()
+    plan, st, run, peak = setup(cfg.chunk)
+    ms = timed(run, reps)
+    n_rounds = sum(len(s.rounds) for s in plan)
+    marks = L.KernelMarks(max_launches=16 * n_rounds + 64)
+    with marks:
+        run()
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for name, kms in marks.times():
+        per_kernel[name] = per_kernel.get(name, 0.0) + kms * 1e3
+    kern_us = sum(per_kernel.values())
+    # algorithmic bytes of the merge rounds: both scorer passes and the compaction read K, V
+    # and the counts of the N slots; the compaction writes T slots with count and source index
+    alg = 0
+    for s in plan:
+        for N, M in s.rounds:
+            alg += B * H * (3 * N * (row + 4) + (N - M) * (row + 8))
+    return {"config": f"C{cfg.idx} {cfg.name}", "layers_folded_into_batch": B, "kv_heads": H, "tokens": total,
+            "budget": cfg.budget, "chunk": cfg.chunk, "n_sink": cfg.n_sink, "chunks": len(plan),
+            "merge_rounds": n_rounds, "loop_ms": round(ms, 3),
+            "prefill_tokens_per_s": round(total / (ms * 1e-3), 1),
+            "ms_per_round": round(ms / max(n_rounds, 1), 4),
+            "kernel_us_per_round": {k: round(v / n_rounds, 2) for k, v in per_kernel.items()},
+            "kernel_us_total": round(kern_us, 1),
+            "merge_algorithmic_MB": round(alg / 1e6, 1),
+            "merge_kernel_GBps": round(alg / (kern_us * 1e-6) / 1e9, 1),
+            "peak_alloc_MB": round(peak / 1e6, 1), "full_cache_MB": round(full_mb, 1),
+            "chunk_sweep": sweep,
+            "note": "loop_ms includes the chunk appends (torch copies standing in for the prefill's KV "
+                    "writes) and host launch overhead; kernel times from library event marks"}
 
 
 def main():

@@ -1,4 +1,4 @@
-"""The five seeded synthetic workloads the merge path is checked and measured on.
+"""The seeded synthetic workloads the merge path is checked and measured on.
 
 Shapes follow the Llama-3.1-8B KV layout the KVSlimmer deep-dive
 (charles2530.github.io, section 算一遍) uses for its byte count: 32 layers,
@@ -28,6 +28,8 @@ class Config:
     rope_theta: float | None   # None: no rotary embedding on the synthetic keys
     decode_steps: int = 0
     redraw_window: bool = True  # fresh window queries every round
+    budget: int = 0            # > 0: chunked prefill under this cache budget (slots per head)
+    chunk: int = 0             # tokens appended per chunk in that regime
 
     @property
     def group(self) -> int:
@@ -54,4 +56,12 @@ C5 = Config(5, "llama8b-128k-4x-decode", batch=1, layers=32, kv_heads=8, q_heads
             n_slots=131072, dtype="bf16", window=32, n_sink=0, n_recent=0, rounds=(65536, 32768),
             rho=(0.9, 0.9), rope_theta=5.0e5, decode_steps=128)
 
-CONFIGS = {c.idx: c for c in (C1, C2, C3, C4, C5)}
+# The evaluation regime of the deep-dive's 实验设置: the prompt is prefilled in chunks of
+# 512 tokens into a cache of at most 2048 slots per head, the first 32 tokens never merge.
+# All 32 layers of the model are folded into the batch dimension, so one round per chunk
+# covers the whole model.
+C6 = Config(6, "llama8b-32L-stream-32k-budget2048-chunk512", batch=1, layers=32, kv_heads=8, q_heads=32,
+            head_dim=128, n_slots=32768, dtype="bf16", window=32, n_sink=32, n_recent=0, rounds=(),
+            rho=(0.7, 0.95), rope_theta=5.0e5, budget=2048, chunk=512)
+
+CONFIGS = {c.idx: c for c in (C1, C2, C3, C4, C5, C6)}

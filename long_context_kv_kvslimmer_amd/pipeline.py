@@ -149,3 +149,114 @@ def config_rounds(cfg, layer: int, device, K=None, V=None, batches=None, out_dty
         out.append((K, V, n, Qw, M, bufs))
         K, V, n, N = bufs.K, bufs.V, bufs.n, T
     return out
+
+
+# ------------------------------------------------------ chunked budget loop --
+@dataclass
+class StreamStep:
+    c0: int            # first token of the chunk
+    length: int        # tokens in the chunk
+    n_after: int       # slots held once the chunk is appended
+    rounds: list       # [(N, M), ...]: merge rounds that bring the cache back to the budget
+
+
+def stream_schedule(total: int, budget: int, chunk: int, n_sink: int) -> list:
+    """Host plan of chunked prefill under a cache budget (the evaluation regime of the
+    deep-dive's 实验设置): chunk after chunk is appended, and while the cache holds
+    N > budget slots a merge round with M = min(N - budget, P) runs, P the candidate pairs
+    after the n_sink kept first slots (no recent window is protected).  budget > n_sink
+    guarantees every such round has a pair to merge."""
+    if chunk < 1 or n_sink < 0 or budget <= n_sink or total < 0:
+        raise ValueError("need chunk >= 1, total >= 0 and budget > n_sink >= 0")
+    plan, N = [], 0
+    for c0 in range(0, total, chunk):
+        length = min(chunk, total - c0)
+        N += length
+        step = StreamStep(c0, length, N, [])
+        while N > budget:
+            M = min(N - budget, L.num_pairs(N, n_sink, 0))
+            step.rounds.append((N, M))
+            N -= M
+        plan.append(step)
+    return plan
+
+
+@dataclass
+class StreamBuffers:
+    bufs: tuple        # two RoundBuffers whose K/V/n are the ping-pong caches; statistics shared
+    capacity: int      # slots per (b, h) of each cache
+
+
+def alloc_stream(B: int, H: int, n_q_heads: int, D: int, dtype, device, window: int, n_sink: int,
+                 plan: list, want_flags: bool = False) -> StreamBuffers:
+    """Two caches of the largest size the plan reaches, and one set of round statistics and
+    workspaces sized for the largest round; nothing is allocated while the loop runs."""
+    cap = max([s.n_after for s in plan] + [1])
+    f32 = torch.float32
+    P = L.num_pairs(cap, n_sink, 0)
+    ws = ss = 16
+    for s in plan:
+        for N, M in s.rounds:
+            c = L.KvsCache(B, H, n_q_heads, D, N, H * cap * D, cap * D)
+            r = L.round_desc(window, n_sink, 0, M, 1.0 / math.sqrt(D))
+            ws = max(ws, L.workspace_bytes(L.KVS_OP_SCORE, c, r))
+            ss = max(ss, L.workspace_bytes(L.KVS_OP_SEL_STATE, c, r))
+    shared = dict(
+        lse=torch.empty(B, n_q_heads, window, dtype=f32, device=device),
+        O=torch.empty(B, n_q_heads, window, D, dtype=f32, device=device),
+        g_self=torch.empty(B * H * cap, dtype=f32, device=device),
+        g_cross=torch.empty(max(B * H * P, 1), dtype=f32, device=device),
+        cos=torch.empty(max(B * H * P, 1), dtype=f32, device=device),
+        sel_state=torch.empty(ss, dtype=torch.uint8, device=device),
+        score_ws=torch.empty(ws, dtype=torch.uint8, device=device),
+        w=torch.empty(max(B * H * P, 1), 2, dtype=f32, device=device) if want_flags else None,
+        selected=torch.empty(max(B * H * P, 1), dtype=torch.uint8, device=device) if want_flags else None,
+        src=torch.empty(B, H, cap, dtype=torch.int32, device=device))
+    two = tuple(RoundBuffers(K=torch.empty(B, H, cap, D, dtype=dtype, device=device),
+                             V=torch.empty(B, H, cap, D, dtype=dtype, device=device),
+                             n=torch.empty(B, H, cap, dtype=torch.int32, device=device), **shared)
+                for _ in range(2))
+    return StreamBuffers(two, cap)
+
+
+def run_stream(K_src, V_src, window_queries, n_q_heads: int, window: int, n_sink: int, plan: list,
+               st: StreamBuffers, on_round=None):
+    """Run the chunked budget loop on the current stream.  K_src, V_src [B, H_kv, total, D]
+    hold the raw tokens (a prefill would write each chunk in turn); window_queries(c) gives
+    the observation window [B, H_q, W, D] of chunk c (its last W queries).  Each chunk is
+    appended with count 1 to the current cache, then each planned round reads that cache
+    and writes the other one.  on_round(c, K, V, n, Qw, N, M, out) runs after each round is
+    enqueued.  Returns (buffers holding the final cache, its slot count)."""
+    cur, N = 0, 0
+    for c, s in enumerate(plan):
+        b = st.bufs[cur]
+        b.K[:, :, N:N + s.length].copy_(K_src[:, :, s.c0:s.c0 + s.length])
+        b.V[:, :, N:N + s.length].copy_(V_src[:, :, s.c0:s.c0 + s.length])
+        b.n[:, :, N:N + s.length].fill_(1)
+        N += s.length
+        if not s.rounds:
+            continue
+        Qw = window_queries(c)
+        for Nr, M in s.rounds:
+            out = st.bufs[1 - cur]
+            run_round(b.K, b.V, b.n, Qw, n_q_heads, window, n_sink, 0, M, out, n_slots=Nr)
+            if on_round is not None:
+                on_round(c, b.K, b.V, b.n, Qw, Nr, M, out)
+            cur, b, N = 1 - cur, out, Nr - M
+    return st.bufs[cur], N
+
+
+def stream_inputs(cfg, device, layers=None):
+    """Raw tokens of every layer folded into the batch dimension, [layers, H_kv, N, D], and
+    the per-chunk observation windows [layers, H_q, W, D] (drawn per chunk, seeded)."""
+    from . import synth
+    ls = list(range(cfg.layers)) if layers is None else list(layers)
+    K = torch.empty(len(ls), cfg.kv_heads, cfg.n_slots, cfg.head_dim, dtype=synth.TORCH_DTYPE[cfg.dtype],
+                    device=device)
+    V = torch.empty_like(K)
+    for i, layer in enumerate(ls):
+        K[i], V[i], _ = synth.make_cache(cfg, layer, 0, device)
+
+    def window_queries(c):
+        return torch.stack([synth.window_queries(cfg, layer, 0, c, device) for layer in ls])
+    return K, V, window_queries

@@ -1,0 +1,161 @@
+"""GPU parity of chunked prefill under a fixed cache budget: 32 layers of a
+Llama-3.1-8B-shaped cache folded into the batch, 32768 tokens appended in chunks
+of 512, at most 2048 slots per head, the first 32 tokens kept, one partial merge
+round per chunk once the budget is reached (60 rounds).
+
+Checked: after every round, on every (layer, kv-head) slice, the compaction
+invariants (counts conserved, order kept, first tokens verbatim, each slot
+covering a contiguous run of tokens, exactly M merges); sampled rounds against
+the oracle on the very inputs the GPU consumed; on tracked slices, the lossless
+value property end to end (each slot's value is the mean of the raw values it
+covers, within the bf16 rounding the rounds add); decode over the final cache.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvs_oracle as O
+from tests.parity import REL_TOL, check_round_slice, host, maxrel
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BF16_U = 2.0 ** -8          # unit round-off of bf16 (8 significant bits)
+
+
+def _rerun_fp32(cfg, K, V, n, Qw, N, M, out):
+    """The same round with fp32 output and selection flags: the streamed bf16 output must
+    be its round-to-nearest-even image; the fp32 output is what the oracle is compared with."""
+    from long_context_kv_kvslimmer_amd import pipeline
+    b32 = pipeline.merge_round(K, V, n, Qw, cfg.q_heads, cfg.window, cfg.n_sink, 0, M, n_slots=N,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    T = N - M
+    assert torch.equal(b32.K[:, :, :T].to(torch.bfloat16), out.K[:, :, :T])
+    assert torch.equal(b32.V[:, :, :T].to(torch.bfloat16), out.V[:, :, :T])
+    assert torch.equal(b32.n[:, :, :T], out.n[:, :, :T]) and torch.equal(b32.src[:, :, :T], out.src[:, :, :T])
+    return b32
+
+
+def test_c6_stream_budget_2048_chunk_512():
+    from long_context_kv_kvslimmer_amd import configs, pipeline
+    cfg = configs.C6
+    print("\n[C6] raw tokens, 32 layers x 32768", flush=True)
+    plan = pipeline.stream_schedule(cfg.n_slots, cfg.budget, cfg.chunk, cfg.n_sink)
+    assert all(r == (2560, 512) for s in plan for r in s.rounds)
+    stream_check(cfg, DEV, track=[(0, 0), (13, 5), (31, 7)], check_rounds={0: (0, 3), 29: (17, 1), 59: (31, 6)},
+                 decode_heads=((0, 0), (13, 21), (31, 31)), n_rounds=60)
+
+
+def test_stream_ragged_tail_and_several_rounds_per_chunk():
+    """Chunks larger than the budget less the kept slots need several rounds each (every
+    round merges at most every candidate pair), and the last chunk is short."""
+    import dataclasses
+    from long_context_kv_kvslimmer_amd import configs, pipeline
+    cfg = dataclasses.replace(configs.C6, idx=7, layers=3, kv_heads=2, q_heads=8, head_dim=64, n_slots=3001,
+                              window=16, n_sink=4, budget=256, chunk=384)
+    plan = pipeline.stream_schedule(cfg.n_slots, cfg.budget, cfg.chunk, cfg.n_sink)
+    assert plan[-1].length == 3001 % 384 and max(len(s.rounds) for s in plan) == 2
+    print("\n[stream] ragged, 3 layers x 3001, budget 256, chunk 384", flush=True)
+    stream_check(cfg, DEV, track=[(0, 0), (2, 1)], check_rounds={0: (0, 1), 1: (2, 0), 12: (1, 1), 13: (2, 1), 14: (0, 0)},
+                 decode_heads=((0, 3), (2, 6)), n_rounds=sum(len(s.rounds) for s in plan))
+
+
+def stream_check(cfg, dev, track, check_rounds, decode_heads, n_rounds):
+    """track: (layer, kv head) slices followed end to end; check_rounds: round -> slice
+    checked against the oracle; decode_heads: (layer, query head) checked after the loop."""
+    from long_context_kv_kvslimmer_amd import pipeline, synth
+    S, budget = cfg.n_sink, cfg.budget
+    scale = 1 / math.sqrt(cfg.head_dim)
+    K_src, V_src, window_queries = pipeline.stream_inputs(cfg, dev)
+    B, H = K_src.shape[:2]
+    plan = pipeline.stream_schedule(cfg.n_slots, budget, cfg.chunk, S)
+    assert sum(len(s.rounds) for s in plan) == n_rounds
+    st = pipeline.alloc_stream(B, H, cfg.q_heads, cfg.head_dim, K_src.dtype, dev, cfg.window, S, plan)
+    assert st.capacity == max(s.n_after for s in plan)
+    state = {"round": 0, "chunk": -1, "start": torch.empty(B, H, 0, dtype=torch.int64, device=dev),
+             "tol": {t: np.zeros((0, cfg.head_dim)) for t in track}}
+
+    def append_positions(upto):
+        for cc in range(state["chunk"] + 1, upto + 1):
+            s = plan[cc]
+            pos = torch.arange(s.c0, s.c0 + s.length, device=dev).expand(B, H, -1)
+            state["start"] = torch.cat([state["start"], pos], dim=2)
+            for t in track:
+                state["tol"][t] = np.vstack([state["tol"][t], np.zeros((s.length, cfg.head_dim))])
+        state["chunk"] = upto
+
+    def on_round(c, K, V, n, Qw, N, M, out):
+        r = state["round"]
+        torch.cuda.synchronize()
+        append_positions(c)
+        T = N - M
+        start = state["start"]
+        assert start.shape[2] == N
+        n_in, n_out = n[:, :, :N].long(), out.n[:, :, :T].long()
+        src = out.src[:, :, :T].long()
+        assert torch.equal(n_out.sum(2), n_in.sum(2)), f"round {r} counts"
+        assert torch.all(src[:, :, 1:] > src[:, :, :-1]), f"round {r} order"
+        assert torch.equal(src[:, :, :S], torch.arange(S, device=dev).expand(B, H, -1)), f"round {r} sinks"
+        assert torch.equal(out.K[:, :, :S], K[:, :, :S]) and torch.equal(out.V[:, :, :S], V[:, :, :S])
+        merged = n_out != n_in.gather(2, src)
+        assert torch.all(merged.sum(2) == M), f"round {r} merges"
+        # a merged slot is the aligned pair (src, src + 1) after the kept first slots
+        assert torch.all(((src - S) % 2 == 0)[merged]) and torch.all((src >= S)[merged])
+        nxt = n_in.gather(2, (src + 1).clamp(max=N - 1))
+        assert torch.equal(n_out[merged], (n_in.gather(2, src) + nxt)[merged])
+        start = start.gather(2, src)
+        excl = torch.cumsum(n_out, dim=2) - n_out
+        assert torch.equal(start, excl), f"round {r} slots do not tile the tokens"
+        state["start"] = start
+        # value tolerance of tracked slices: a merged slot inherits the count-weighted tolerance
+        # of its two inputs plus one bf16 rounding and the fp32 arithmetic of the mean
+        for (b, h) in track:
+            tin = state["tol"][(b, h)]
+            s_ = host(out.src[b, h, :T]).astype(np.int64)
+            ni = host(n[b, h, :N]).astype(np.int64)
+            no = host(out.n[b, h, :T]).astype(np.int64)
+            vi = host(V[b, h, :N])
+            vo = host(out.V[b, h, :T])
+            tout = tin[s_].copy()
+            mj = np.nonzero(no != ni[s_])[0]
+            i0 = s_[mj]
+            n0, n1 = ni[i0][:, None].astype(np.float64), ni[i0 + 1][:, None].astype(np.float64)
+            tout[mj] = ((n0 * tin[i0] + n1 * tin[i0 + 1]) / (n0 + n1) + BF16_U * np.abs(vo[mj])
+                        + 1e-6 * (np.abs(vi[i0]) + np.abs(vi[i0 + 1])))
+            state["tol"][(b, h)] = tout
+        if r in check_rounds:
+            b, h = check_rounds[r]
+            print(f"[stream] round {r} (chunk {c}) oracle layer {b} head {h}", flush=True)
+            b32 = _rerun_fp32(cfg, K, V, n, Qw, N, M, out)
+            check_round_slice(b32, K, V, n, Qw, b, h, N, S, 0, M, scale, label=f"stream r{r} l{b} h{h}")
+        state["round"] += 1
+
+    print(f"[stream] {len(plan)} chunks", flush=True)
+    final, N = pipeline.run_stream(K_src, V_src, window_queries, cfg.q_heads, cfg.window, S, plan, st,
+                                   on_round=on_round)
+    torch.cuda.synchronize()
+    assert state["round"] == n_rounds and N == budget
+    assert torch.all(final.n[:, :, :N].long().sum(2) == cfg.n_slots)
+    # lossless values end to end on the tracked slices
+    for (b, h) in track:
+        start = host(state["start"][b, h]).astype(np.int64)
+        cnt = host(final.n[b, h, :N]).astype(np.int64)
+        raw = host(V_src[b, h])
+        csum = np.concatenate([np.zeros((1, raw.shape[1])), np.cumsum(raw, axis=0)])
+        mean = (csum[start + cnt] - csum[start]) / cnt[:, None]
+        err = np.abs(host(final.V[b, h, :N]) - mean)
+        bound = state["tol"][(b, h)] + 1e-9
+        assert np.all(err <= bound), f"layer {b} head {h}: value drift {np.max(err - bound)}"
+        assert cnt.max() > 1 and np.array_equal(cnt[:S], np.ones(S))
+    # decode over the final 2048-slot cache
+    print("[stream] decode over the final cache", flush=True)
+    q = torch.stack([synth.decode_query(cfg, layer, 0, 0, dev) for layer in range(cfg.layers)])
+    out = pipeline.decode(final.K, final.V, final.n, q, n_slots=N)
+    torch.cuda.synchronize()
+    for (b, hq) in decode_heads:
+        h = hq // cfg.group
+        ref = O.decode(host(final.K[b, h, :N]), host(final.V[b, h, :N]), host(final.n[b, h, :N]),
+                       host(q[b, hq]), scale)
+        assert maxrel(host(out[b, hq]), ref) <= REL_TOL, f"decode layer {b} head {hq}"
