@@ -237,6 +237,101 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   }
 }
 
+// Few splits and many units (many heads, short caches): one wave per unit, four units per
+// workgroup, no barriers.  Lane l reads the maximum and sum of split l; the wave reduces
+// them; lane l then owns output elements l (and l + 64 at D = 128) and sums the splits in
+// order, the weight of split s read from lane s.
+constexpr int kCombineWaveMaxSplit = 16;
+constexpr int kCombineWaveUnits = 4;
+
+template <int D>
+__global__ __launch_bounds__(64 * kCombineWaveUnits) void combine_wave_kernel(const float* __restrict__ part,
+                                                                             int64_t units, int nsplit,
+                                                                             float* __restrict__ lse,
+                                                                             float* __restrict__ out, PackP pk) {
+  constexpr int E = D / 64;
+  constexpr int64_t rs = D + 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t u = (int64_t)blockIdx.x * kCombineWaveUnits + (threadIdx.x >> 6);
+  if (u >= units) return;   // whole waves leave; nothing below synchronises the workgroup
+  const float* r = part + u * nsplit * rs;
+  const float2 ml = lane < nsplit ? *reinterpret_cast<const float2*>(r + lane * rs) : make_float2(-INFINITY, 0.f);
+  float o[8][E];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[k][e] = k < nsplit ? r[k * rs + 4 + lane + 64 * e] : 0.f;
+  const float M = group_max<64>(ml.x);
+  const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+  const float L = group_sum<64>(ml.y * w);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[k][e] = s0 + k < nsplit ? r[(s0 + k) * rs + 4 + lane + 64 * e] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k < nsplit) {
+        const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s0 + k));
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(o[k][e], ws, acc[e]);
+      }
+    }
+  }
+  float ov[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    ov[e] = acc[e] / L;
+    out[u * D + lane + 64 * e] = ov[e];
+  }
+  const float lse_u = (M + __log2f(L)) * kLn2;
+  if (lse && lane == 0) lse[u] = lse_u;
+  if (pk.ops) {
+    // operands of the MFMA pass 2 (as in combine_kernel): lane c < D / 8 packs elements
+    // 8c .. 8c + 7, fetched from the lanes that own them
+    constexpr int nch = D / 8, KS = D / 32;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = (lane * 8 + j) & (D - 1);
+      float v = __shfl(ov[0], d & 63, 64);
+      if constexpr (E == 2) {
+        const float v1 = __shfl(ov[1], d & 63, 64);
+        v = d >= 64 ? v1 : v;
+      }
+      x[j] = v;
+    }
+    const int64_t bh = u / pk.GW, q = u - bh * pk.GW;
+    float on = 0.f;
+    if (lane < nch) {
+      const int64_t b = bh / pk.Hkv, hk = bh - b * pk.Hkv;
+      const bf16* qrow = static_cast<const bf16*>(pk.Qw) + ((b * pk.Hq + hk * pk.G) * (int64_t)pk.W + q) * D;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = x[2 * j], x1 = x[2 * j + 1];
+        on = __builtin_fmaf(x0, x0, __builtin_fmaf(x1, x1, on));
+        const float m0 = -2.f * x0, m1 = -2.f * x1;
+        hi[j] = pack_bf16x2(m0, m1);
+        lo[j] = pack_bf16x2(m0 - bf16_lo(hi[j]), m1 - bf16_hi(hi[j]));
+      }
+      pk.ops[pack_ops_index(bh, pk.nwb, q, 0, lane, KS)] = *reinterpret_cast<const uint4*>(qrow + lane * 8);
+      pk.ops[pack_ops_index(bh, pk.nwb, q, 1, lane, KS)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      pk.ops[pack_ops_index(bh, pk.nwb, q, 2, lane, KS)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    on = group_sum<16>(on);   // lanes past nch contributed zeros
+    if (lane == 0) {
+      pk.qc[(bh * pk.nwb * 32 + q) * 2] = on;
+      pk.qc[(bh * pk.nwb * 32 + q) * 2 + 1] = -lse_u * kLog2e;
+    }
+  }
+}
+
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.f;
@@ -256,6 +351,16 @@ hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, f
   if (D > 128) return hipErrorInvalidValue;
   PackP pk{};
   if (pack) pk = *pack;
+  if (nsplit <= kCombineWaveMaxSplit && (D == 64 || D == 128)) {
+    const dim3 grid((unsigned)((units + kCombineWaveUnits - 1) / kCombineWaveUnits));
+    if (D == 128)
+      KVS_LAUNCH("combine", combine_wave_kernel<128>, grid, dim3(64 * kCombineWaveUnits), 0, st, part, units, nsplit,
+                 lse, out, pk);
+    else
+      KVS_LAUNCH("combine", combine_wave_kernel<64>, grid, dim3(64 * kCombineWaveUnits), 0, st, part, units, nsplit,
+                 lse, out, pk);
+    return hipGetLastError();
+  }
   KVS_LAUNCH("combine", combine_kernel, dim3((unsigned)units), dim3(kCombineThreads), 0, st, part, nsplit, D, lse, out,
              pk);
   return hipGetLastError();

@@ -230,6 +230,131 @@ __global__ __launch_bounds__(kSelThreads) void sel_final_kernel(SelArgs a) {
   }
 }
 
+// Heads with at most kSmallSelPairs candidate pairs (short caches, e.g. a budgeted cache
+// between prefill chunks): the whole selection of one head in one workgroup, keys held in
+// registers, the four digit histograms in LDS, then the same header and chunk offsets as
+// the multi-workgroup path.  Wave w at step j holds the 64 pairs of chunk 16 j + w.
+constexpr int kSmallSelKeys = 4;
+constexpr int kSmallSelPairs = kSelThreads * kSmallSelKeys;   // 4096 pairs, 64 chunks
+
+__global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelArgs a) {
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* st = a.st + bh * a.sel_stride;
+  const float* cs = a.cos + bh * a.P;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[2];
+  __shared__ int lds[kSelThreads / 64];
+  __shared__ int eq_c[64], gt_c[64];
+  __shared__ uint64_t eq_m[64];
+  __shared__ int32_t sh_ptau;
+  uint32_t k[kSmallSelKeys];
+#pragma unroll
+  for (int j = 0; j < kSmallSelKeys; ++j) {
+    const int64_t p = (int64_t)j * kSelThreads + tid;
+    k[j] = p < a.P ? order_key(cs[p]) : 0u;
+  }
+  uint32_t prefix = 0, remaining = (uint32_t)a.M;
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t mask = s == 0 ? 0u : 0xffffffffu << (32 - 8 * s);
+    const int shift = 24 - 8 * s;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSmallSelKeys; ++j) {
+      const int64_t p = (int64_t)j * kSelThreads + tid;
+      wave_hist_add(hist, p < a.P && (k[j] & mask) == prefix, (k[j] >> shift) & 255u);
+    }
+    __syncthreads();
+    // digit s: the largest d whose count of keys >= d reaches `remaining`
+    const uint32_t v = tid < 256 ? hist[255 - tid] : 0u;
+    int tot;
+    const uint32_t x = (uint32_t)block_exclusive_scan<kSelThreads>((int)v, &tot, lds) + v;
+    if (tid < 256 && x >= remaining && x - v < remaining) {
+      sh[0] = prefix | ((uint32_t)(255 - tid) << shift);
+      sh[1] = remaining - (x - v);
+    }
+    __syncthreads();
+    prefix = sh[0];
+    remaining = sh[1];
+    __syncthreads();
+  }
+  const uint32_t tau = prefix;
+  // per-chunk counts of keys equal to and above tau
+#pragma unroll
+  for (int j = 0; j < kSmallSelKeys; ++j) {
+    const int64_t p = (int64_t)j * kSelThreads + tid;
+    const uint64_t eq = __ballot(p < a.P && k[j] == tau);
+    const uint64_t gt = __ballot(p < a.P && k[j] > tau);
+    const int c = j * (kSelThreads / 64) + wv;
+    if (lane == 0) {
+      eq_c[c] = __popcll(eq);
+      gt_c[c] = __popcll(gt);
+      eq_m[c] = eq;
+    }
+  }
+  __syncthreads();
+  if (wv == 0) {
+    // chunk `lane`: the tie cut-off (the remaining-th key equal to tau), then the
+    // exclusive offsets of the selected pairs of every chunk
+    const int c = lane;
+    const int e = c < a.nchunks ? eq_c[c] : 0;
+    int incl = e;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int before = incl - e;
+    const bool hit = e > 0 && (uint32_t)before < remaining && remaining <= (uint32_t)incl;
+    const uint64_t hm = __ballot(hit);
+    const int ct = hm ? __ffsll((unsigned long long)hm) - 1 : -1;
+    const int rank = ct >= 0 ? (int)remaining - __shfl(before, ct, 64) : 0;   // 1-based
+    int32_t ptau = -1;
+    if (ct >= 0) {
+      const uint64_t m = eq_m[ct];
+      const bool bit = (m >> lane) & 1ull;
+      const uint64_t at = __ballot(bit && __popcll(m & ((1ull << lane) - 1ull)) + 1 == rank);
+      if (at) ptau = (int32_t)(ct * kChunkPairs + __ffsll((unsigned long long)at) - 1);
+    }
+    const int v = c < a.nchunks ? gt_c[c] + (c < ct ? e : c == ct ? rank : 0) : 0;
+    int vin = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(vin, off, 64);
+      if (lane >= off) vin += y;
+    }
+    if (c < a.nchunks) st[kSelHeaderInts + c] = vin - v;
+    const int total = __shfl(vin, 63, 64);
+    if (lane == 0) {
+      st[0] = (int32_t)tau;
+      st[1] = ptau;
+      st[2] = (int32_t)a.M;
+      st[3] = (int32_t)a.nchunks;
+      st[kSelHeaderInts + a.nchunks] = total;
+      sh_ptau = ptau;
+    }
+  }
+  if (a.selected || a.w) {
+    __syncthreads();
+    SelHeader hd;
+    hd.tau_key = tau;
+    hd.p_tau = sh_ptau;
+    hd.n_merge = (int32_t)a.M;
+    hd.n_chunks = (int32_t)a.nchunks;
+    for (int64_t p = tid; p < a.P; p += kSelThreads) {
+      if (a.selected) a.selected[bh * a.P + p] = is_selected(order_key(cs[p]), p, hd) ? 1 : 0;
+      if (a.w) {
+        const int64_t m = a.S + 2 * p;
+        float w0, w1;
+        closed_form_weights(a.g_self[bh * a.N + m], a.g_cross[bh * a.P + p], a.g_self[bh * a.N + m + 1], w0, w1);
+        a.w[(bh * a.P + p) * 2] = w0;
+        a.w[(bh * a.P + p) * 2 + 1] = w1;
+      }
+    }
+  }
+}
+
 // M == P / M == 0 without a cosine array: thresholds are fixed, so the cosine is never read.
 __global__ __launch_bounds__(kSelThreads) void select_fixed_kernel(SelArgs a) {
   const int64_t bh = blockIdx.x;
@@ -278,6 +403,10 @@ hipError_t launch_select(const Shape& s, const RoundP& r, const float* g_self, c
   if (heads == 0) return hipSuccess;
   if (cos == nullptr || r.M == 0 || r.M == r.P) {
     KVS_LAUNCH("select", select_fixed_kernel, dim3(heads), dim3(kSelThreads), 0, st, a);
+    return hipGetLastError();
+  }
+  if (r.P <= kSmallSelPairs) {
+    KVS_LAUNCH("select", select_small_kernel, dim3(heads), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((r.P + kHistBlock - 1) / kHistBlock), (unsigned)heads);

@@ -109,12 +109,14 @@ def test_selection_index_tie_break():
         check_round_slice(bufs, K, V, n, Qw, 0, 0, 512, 0, 0, M, 1 / math.sqrt(128), label=f"ties M={M}")
 
 
-def test_selection_large_ties_multiworkgroup():
-    """Selection over more than 65536 pairs per head (many 4096-pair workgroups, more than 1024
-    chunks) with long runs of bit-identical cosines at the threshold: the flags and the chunk
-    offsets in the selection state equal a brute-force top-M with the lower index winning ties."""
+@pytest.mark.parametrize("P", [150001, 4097, 4096, 1264, 65])
+def test_selection_ties_against_brute_force(P):
+    """Selection with long runs of bit-identical cosines at the threshold: the flags and the
+    chunk offsets in the selection state equal a brute-force top-M with the lower index
+    winning ties.  P = 150001: many 4096-pair histogram workgroups, more than 1024 chunks;
+    4097: the smallest head that takes that path; 4096 and below: one workgroup per head."""
     from long_context_kv_kvslimmer_amd import kvslim as L
-    H, P = 3, 150001
+    H = 3
     N = 2 * P + 1                                            # an odd leftover slot
     K = torch.empty(1, H, N, 64, dtype=torch.bfloat16, device=DEV)   # layout only; select reads cos
     rng = np.random.default_rng(7)
@@ -125,7 +127,7 @@ def test_selection_large_ties_multiworkgroup():
     cos_t = torch.from_numpy(cos)[None].contiguous().to(DEV)
     cache = L.cache_desc(K, H)
     nch = (P + 63) // 64
-    for M in (1, 4097, 65537, P // 2, P - 1):
+    for M in sorted({m for m in (1, 512, 4097, 65537, P // 2, P - 1) if 1 <= m < P}):
         print(f"\n[select] P={P} M={M}", flush=True)
         rnd = L.round_desc(4, 0, 0, M, 0.125)
         st = torch.zeros(L.workspace_bytes(L.KVS_OP_SEL_STATE, cache, rnd), dtype=torch.uint8, device=DEV)
