@@ -215,11 +215,10 @@ def summarize_per_config(jsonl, cmd):
     rows = [r for r in allrows if "merge_ms_per_layer" in r]
     streams = [r for r in allrows if "chunk_sweep" in r]
     out = ["# Per-config GPU timings (one layer of each seeded workload)", "", "Made by:", "", "```", cmd, "```", "",
-           "Merge rounds use kvs_score_merge for full rounds and kvs_score -> kvs_merge_weights -> kvs_merge_compact "
-           "for partial ones; median of 5 repetitions after a warm-up, events around the layer's rounds.  All layers "
-           "of a config have one shape, so the model-wide time is the per-layer time x layers.  Algorithmic MB: K "
-           "and V read by each pass that reads them (2 for a fused round, 3 for a partial round), merged rows "
-           "written once.", "",
+           "Every merge round is one kvs_score_merge call (for partial rounds the selection runs between the "
+           "scorer's passes and the merge inside the second); median of 5 repetitions after a warm-up, events around "
+           "the layer's rounds.  All layers of a config have one shape, so the model-wide time is the per-layer time "
+           "x layers.  Algorithmic MB: K and V read by both scorer passes, merged rows written once.", "",
            "| config | batch x layers | rounds (pairs merged) | merge ms / layer | merge ms, all layers | tokens/s | "
            "algorithmic MB / layer | GB/s |",
            "|---|---|---|---:|---:|---:|---:|---:|"]
@@ -302,8 +301,7 @@ def cpu_baseline(cfg, K, V, Qw, heads=2):
 
 def per_config(dev, which, reps=5):
     """Per-config GPU timings (not the bench line): every merge round of one layer of each
-    seeded workload, on the fastest entry points the library offers (kvs_score_merge for full
-    rounds, kvs_score -> kvs_merge_weights -> kvs_merge_compact for partial ones), timed with
+    seeded workload through kvs_score_merge (one call per round), timed with
     events on the library's stream over `reps` repetitions after one warm-up; all layers of a
     config have the same shape, so the whole-model time is the per-layer time x layers.  The
     decode workload (C5) appends one token per step and times each kvs_decode_attn."""
@@ -334,21 +332,17 @@ def per_config(dev, which, reps=5):
                                         out_capacity=cap, want_flags=False)
             P = L.num_pairs(N, cfg.n_sink, cfg.n_recent)
             full = M == P
-            # K and V are read by both scorer passes (and once more by a separate merge), the
+            # K and V are read by both scorer passes (the merge runs inside the second), the
             # merged rows are written once
-            reads = (2 if full else 3) * N * row + (N * 4 if n is not None else 0)
+            reads = 2 * N * row + (N * 4 if n is not None else 0)
             alg += cfg.batch * cfg.kv_heads * (reads + (N - M) * (row + 8))
             plan.append((K, V, n, Qw, M, N, full, bufs))
             K, V, n, N = bufs.K, bufs.V, bufs.n, N - M
 
         def rounds():
             for (Ki, Vi, ni, Qw, M, Ni, full, bufs) in plan:
-                if full:
-                    pipeline.run_full_round_fused(Ki, Vi, ni, Qw, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent,
-                                                  bufs, n_slots=Ni)
-                else:
-                    pipeline.run_round(Ki, Vi, ni, Qw, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, bufs,
-                                       n_slots=Ni)
+                pipeline.run_round_fused(Ki, Vi, ni, Qw, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, bufs,
+                                         n_slots=Ni)
 
         rounds()
         torch.cuda.synchronize()
@@ -493,12 +487,13 @@ def stream_timing(cfg, dev, reps=5, chunks=(256, 512, 1024, 2016)):
     for name, kms in marks.times():
         per_kernel[name] = per_kernel.get(name, 0.0) + kms * 1e3
     kern_us = sum(per_kernel.values())
-    # algorithmic bytes of the merge rounds: both scorer passes and the compaction read K, V
-    # and the counts of the N slots; the compaction writes T slots with count and source index
+    # algorithmic bytes of the merge rounds: both scorer passes read K, V and the counts of
+    # the N slots (the merge runs inside the second); T slots are written with count and
+    # source index
     alg = 0
     for s in plan:
         for N, M in s.rounds:
-            alg += B * H * (3 * N * (row + 4) + (N - M) * (row + 8))
+            alg += B * H * (2 * N * (row + 4) + (N - M) * (row + 8))
     return {"config": f"C{cfg.idx} {cfg.name}", "layers_folded_into_batch": B, "kv_heads": H, "tokens": total,
             "budget": cfg.budget, "chunk": cfg.chunk, "n_sink": cfg.n_sink, "chunks": len(plan),
             "merge_rounds": n_rounds, "loop_ms": round(ms, 3),

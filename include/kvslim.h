@@ -6,7 +6,7 @@
  *
  *   kvs_score          window attention statistics (lse, o) and the forward-only
  *                      Hessian-norm sums g_self / g_cross, plus adjacent-key cosine
- *   kvs_score_merge    kvs_score + kvs_merge_compact of a full round in one call
+ *   kvs_score_merge    kvs_score + kvs_merge_weights + kvs_merge_compact in one call
  *   kvs_merge_weights  pair selection (top-M adjacent pairs by cosine) and the
  *                      closed-form key-merge weights
  *   kvs_merge_compact  key merge, lossless value-slot merge, stream compaction
@@ -88,7 +88,8 @@ typedef enum {
   KVS_OP_SCORE = 0,      /* workspace of kvs_score */
   KVS_OP_SELECT = 1,     /* workspace of kvs_merge_weights */
   KVS_OP_SEL_STATE = 2,  /* size of the selection-state buffer (kvs_merge_weights -> kvs_merge_compact) */
-  KVS_OP_DECODE = 3      /* workspace of kvs_decode_attn */
+  KVS_OP_DECODE = 3,     /* workspace of kvs_decode_attn */
+  KVS_OP_SCORE_MERGE = 4 /* workspace of kvs_score_merge (equals KVS_OP_SCORE when n_merge is 0 or P) */
 } kvs_op;
 
 /* Number of candidate pairs P = floor((N - S - R) / 2) (0 if negative).  Pair p is the
@@ -127,16 +128,18 @@ kvs_status kvs_score(const kvs_cache* cache, kvs_dtype dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * kvs_score_merge — one full merge round (n_merge == P: every candidate pair merges) in
- * one call: the statistics of kvs_score (lse, O, g_self, g_cross; no cosine, nothing is
- * chosen) and the outputs of kvs_merge_compact (K_out, V_out, n_out, src_out), computed
- * with the same arithmetic, so every output equals that of kvs_score followed by
- * kvs_merge_compact bit for bit.  For bf16 caches with head_dim 64 or 128 and at most 128
- * window queries per kv head (G * window <= 128), the merge runs inside the scorer's
- * second pass on the K/V tiles it has already loaded, which saves one read of the cache;
- * other shapes run the two passes one after the other.  Arguments as in kvs_score and
- * kvs_merge_compact; workspace: kvs_workspace_bytes(KVS_OP_SCORE).  Errors as theirs, and
- * KVS_ERR_SHAPE if n_merge != P.
+ * kvs_score_merge — one whole merge round in one call: the statistics of kvs_score (lse,
+ * O, g_self, g_cross), the selection of kvs_merge_weights and the outputs of
+ * kvs_merge_compact (K_out, V_out, n_out, src_out), computed with the same arithmetic, so
+ * every output equals that of kvs_score -> kvs_merge_weights -> kvs_merge_compact bit for
+ * bit.  0 <= n_merge <= P.  For 0 < n_merge < P the cosine and the selection state live in
+ * the workspace (they are not outputs); for n_merge == P every pair merges and for
+ * n_merge == 0 none does, and no cosine is computed.  For bf16 caches with head_dim 64 or
+ * 128 and at most 128 window queries per kv head (G * window <= 128), the selection runs
+ * between the scorer's two passes and the merge runs inside the second pass on the K/V
+ * tiles it has already loaded, which saves one read of the cache; other shapes run the
+ * passes one after the other.  Arguments as in kvs_score and kvs_merge_compact;
+ * workspace: kvs_workspace_bytes(KVS_OP_SCORE_MERGE).  Errors as theirs.
  */
 kvs_status kvs_score_merge(const kvs_cache* cache, kvs_dtype dtype,
                            const void* K, const void* V, const int32_t* n, const void* Qw,

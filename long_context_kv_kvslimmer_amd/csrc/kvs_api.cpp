@@ -160,6 +160,17 @@ int64_t kvs_num_pairs(int64_t n_slots, int64_t n_sink, int64_t n_recent) {
   return pairs_of(n_slots, n_sink, n_recent);
 }
 
+// kvs_score_merge workspace: the scorer's, then for a partial round (0 < M < P) the
+// cosine [B*Hkv, P] and the selection state, each 256-byte aligned.
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+static bool partial_round(const kvs::RoundP& r) { return r.M > 0 && r.M < r.P; }
+static size_t score_merge_bytes(const kvs::Shape& s, const kvs::RoundP& r) {
+  const size_t b = kvs::score_workspace_bytes(s, r);
+  if (!partial_round(r)) return b;
+  return align256(b) + align256((size_t)s.B * s.Hkv * r.P * sizeof(float)) +
+         (size_t)s.B * s.Hkv * kvs::sel_stride_ints(r.P) * sizeof(int32_t);
+}
+
 size_t kvs_workspace_bytes(kvs_op op, const kvs_cache* cache, const kvs_round* round) {
   kvs::Shape s;
   if (check_cache(cache, KVS_BF16, s) != KVS_OK) return 0;
@@ -171,6 +182,13 @@ size_t kvs_workspace_bytes(kvs_op op, const kvs_cache* cache, const kvs_round* r
       const size_t bf = kvs::score_workspace_bytes(s, r);
       s.bf16 = false;
       const size_t f32 = kvs::score_workspace_bytes(s, r);
+      return bf > f32 ? bf : f32;
+    }
+    case KVS_OP_SCORE_MERGE: {
+      if (!round || check_round(round, s, r, true) != KVS_OK) return 0;
+      const size_t bf = score_merge_bytes(s, r);
+      s.bf16 = false;
+      const size_t f32 = score_merge_bytes(s, r);
       return bf > f32 ? bf : f32;
     }
     case KVS_OP_SELECT:
@@ -214,9 +232,6 @@ kvs_status kvs_score_merge(const kvs_cache* cache, kvs_dtype dtype, const void* 
   kvs_status st = check_cache(cache, dtype, s);
   if (st) return st;
   if ((st = check_round(round, s, r, true))) return st;
-  if (r.M != r.P)
-    return fail(KVS_ERR_SHAPE, "kvs_score_merge merges every candidate pair: n_merge %lld must equal P = %lld",
-                (long long)r.M, (long long)r.P);
   if (s.N < 1) return fail(KVS_ERR_SHAPE, "kvs_score_merge needs n_slots >= 1");
   if (!K || !V || !Qw || !lse || !O || !g_self || (r.P > 0 && !g_cross))
     return fail(KVS_ERR_NULL, "kvs_score_merge: K, V, Qw, lse, O, g_self and g_cross are required");
@@ -230,18 +245,26 @@ kvs_status kvs_score_merge(const kvs_cache* cache, kvs_dtype dtype, const void* 
     return fail(KVS_ERR_NULL, "kvs_score_merge: K_out, V_out, n_out, src_out are required");
   if (!aligned16(K) || !aligned16(V) || !aligned16(Qw) || !aligned16(K_out) || !aligned16(V_out))
     return fail(KVS_ERR_ALIGN, "K, V, Qw, K_out, V_out must be 16-byte aligned");
-  const size_t need = kvs::score_workspace_bytes(s, r);
+  const size_t need = score_merge_bytes(s, r);
   if (workspace_bytes < need || (need && !workspace))
     return fail(KVS_ERR_WORKSPACE, "kvs_score_merge needs %zu workspace bytes, got %zu", need, workspace_bytes);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   kvs::OutP op{so.sb, so.sh, so.bf16};
+  // workspace: scorer | cosine | selection state (the last two for partial rounds only)
+  uint8_t* wb = static_cast<uint8_t*>(workspace);
+  const bool part = partial_round(r);
+  float* cos = part ? reinterpret_cast<float*>(wb + align256(kvs::score_workspace_bytes(s, r))) : nullptr;
+  int32_t* sel = part ? reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(cos) +
+                                                    align256((size_t)s.B * s.Hkv * r.P * sizeof(float)))
+                      : nullptr;
   if (kvs::fused_round_ok(s, r))
-    return hip_status(kvs::launch_score_merge_mfma(s, r, K, V, n, Qw, lse, O, g_self, g_cross, workspace, op, K_out,
-                                                   V_out, n_out, src_out, hs),
+    return hip_status(kvs::launch_score_merge_mfma(s, r, K, V, n, Qw, lse, O, g_self, g_cross, workspace, cos, sel,
+                                                   op, K_out, V_out, n_out, src_out, hs),
                       "kvs_score_merge");
-  // the same round as two passes on the GPU (scorer, then the merge pass)
-  hipError_t e = kvs::launch_score(s, r, K, V, n, Qw, lse, O, g_self, g_cross, nullptr, workspace, hs);
-  if (e == hipSuccess) e = kvs::launch_merge(s, r, K, V, n, g_self, g_cross, nullptr, op, K_out, V_out, n_out, src_out, hs);
+  // the same round as separate passes on the GPU (scorer, selection, merge pass)
+  hipError_t e = kvs::launch_score(s, r, K, V, n, Qw, lse, O, g_self, g_cross, cos, workspace, hs);
+  if (e == hipSuccess && part) e = kvs::launch_select(s, r, g_self, g_cross, cos, nullptr, nullptr, sel, hs);
+  if (e == hipSuccess) e = kvs::launch_merge(s, r, K, V, n, g_self, g_cross, sel, op, K_out, V_out, n_out, src_out, hs);
   return hip_status(e, "kvs_score_merge");
 }
 

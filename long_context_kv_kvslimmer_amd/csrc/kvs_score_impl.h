@@ -31,12 +31,17 @@ struct P2Args {
   int64_t N, S, P, sb, sh, GW;
   int Hkv, Hq, G, W;
   float scale;
-  // merge outputs of a full round fused into pass 2 (kvs_score_merge); unused otherwise
+  // merge outputs of a round fused into pass 2 (kvs_score_merge); unused otherwise
   void* Ko;
   void* Vo;
   int32_t* no;
   int32_t* so;
   int64_t osb, osh;
+  int64_t M;           // pairs merged (P for a full round)
+  // partial rounds: the pass-1 cosine and the selection state of kvs_merge_weights
+  const float* cos;
+  const int32_t* sel;
+  int64_t sel_stride;
 };
 
 struct CosArgs {
@@ -60,13 +65,15 @@ inline void valu_pass1_plan(int64_t N, int64_t& chunk, int& nsplit) {
 
 bool use_mfma_scorer(const Shape& s);
 size_t mfma_score_workspace_bytes(const Shape& s, const RoundP& r);
-// Whole full round (n_merge == P) fused: pass 1, combine, pass 2 with the merge and
-// compaction folded in.  Requires use_mfma_scorer and at most 128 window queries per kv head.
+// Whole round fused: pass 1, combine, (for 0 < n_merge < P: the selection over the pass-1
+// cosine), pass 2 with the merge and compaction folded in.  Requires use_mfma_scorer and
+// at most 128 window queries per kv head.  cos ([B*Hkv, P]) and sel_state (selection
+// state) are needed only for 0 < n_merge < P.
 bool fused_round_ok(const Shape& s, const RoundP& r);
 hipError_t launch_score_merge_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
                                    const void* Qw, float* lse, float* O, float* g_self, float* g_cross, void* ws,
-                                   const OutP& o, void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
-                                   hipStream_t st);
+                                   float* cos, int32_t* sel_state, const OutP& o, void* K_out, void* V_out,
+                                   int32_t* n_out, int32_t* src_out, hipStream_t st);
 hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
                              const void* Qw, float* lse, float* O, float* g_self, float* g_cross, float* cos,
                              void* ws, hipStream_t st);

@@ -478,9 +478,11 @@ __device__ __forceinline__ int row_slot(int R) { return 2 * (R & 15) + (R >> 4);
 
 // grid: one workgroup per (bh, slot chunk, query block), bh fastest so that the blocks of
 // one head land on one XCD.
-// MERGE: also merge every candidate pair of the chunk (a full round) and write the
-// compacted K/V rows (type TO), counts and sources, reusing the tiles already in LDS.
-template <int D, bool HAS_N, bool MERGE, typename TO>
+// MERGE: also merge the chunk's candidate pairs and write the compacted K/V rows (type
+// TO), counts and sources, reusing the tiles already in LDS.  Without PARTIAL every pair
+// merges (a full round); with PARTIAL the pairs chosen by the selection state merge and
+// the others are copied, each at its compacted row.
+template <int D, bool HAS_N, bool MERGE, bool PARTIAL, typename TO>
 __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t base, int64_t chunk, int nsplit,
                                                              int BH) {
   using M = Dma<D>;
@@ -490,6 +492,11 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
   __shared__ int32_t nr[kRing2 * kT2];            // slot counts as loaded (LDS-row order)
   __shared__ float red_s[kW2 * kChunk2Max];       // per-wave sums over its queries, per slot
   __shared__ float red_x[kW2 * (kChunk2Max / 2)]; // and per candidate pair
+  // partial rounds: selection flags of the 64-pair compaction chunks the workgroup's pairs
+  // fall in, and the selected pairs before each of those chunks
+  constexpr int kSelChunks = kChunk2Max / 2 / kChunkPairs + 1;
+  __shared__ uint64_t selm[kSelChunks];
+  __shared__ int32_t selo[kSelChunks];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g4 = lane >> 4;
@@ -588,6 +595,33 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       }
     }
   }
+  // partial rounds: wave w takes compaction chunks sel_c0 + w, sel_c0 + w + kW2, ... of the
+  // pairs whose first slot lies in the workgroup's slots, reads their cosines and
+  // evaluates the selection
+  int64_t sel_c0 = 0;
+  if constexpr (PARTIAL) {
+    const int64_t pend = a.S + 2 * a.P;
+    const int64_t mlo = lo > a.S ? lo : a.S, mhi = hi < pend ? hi : pend;
+    const int64_t pa = (mlo - a.S + 1) / 2, pb = (mhi - a.S) / 2;   // pairs [pa, pb)
+    sel_c0 = pa / kChunkPairs;
+    const int nck = pb > pa ? (int)((pb - 1) / kChunkPairs - sel_c0 + 1) : 0;
+    for (int k = wv; k < nck; k += kW2) {
+      const int64_t cc = sel_c0 + k;
+      uint64_t m = 0;
+      int32_t before = 0;
+      if (a.M > 0) {
+        const int32_t* st = a.sel + bh * a.sel_stride;
+        const SelHeader hd{(uint32_t)st[0], st[1], st[2], st[3]};
+        const int64_t p = cc * kChunkPairs + lane;
+        m = __ballot(p < a.P && is_selected(order_key(p < a.P ? a.cos[bh * a.P + p] : 0.f), p, hd));
+        before = st[kSelHeaderInts + cc];
+      }
+      if (lane == 0) {
+        selm[k] = m;
+        selo[k] = before;
+      }
+    }
+  }
   // tile 0 and the operands travel together; later tiles are issued once they are in
   asm volatile("" ::"v"(olo[1][KS - 1]), "v"(nbq[1][3]));
   if (ntiles > 1) issue(1);
@@ -670,10 +704,12 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     }
   };
 
-  // Merge of tile tt (its g sums complete, its rows still in the ring): every candidate
-  // pair becomes one slot k* = w_0 k_m + w_1 k_{m+1}, v* = count-weighted mean, n* = n_m +
-  // n_{m+1} at output row S + p; protected slots are copied to row i (sinks) or i - P.
-  // Thread = (pair n, 16-byte chunk ch) of the tile; the arithmetic is the merge pass's.
+  // Merge of tile tt (its g sums complete, its rows still in the ring): a merging pair
+  // becomes one slot k* = w_0 k_m + w_1 k_{m+1}, v* = count-weighted mean, n* = n_m +
+  // n_{m+1} at output row S + 2p - (merging pairs before p) (S + p in a full round); a pair
+  // that does not merge is copied to that row and the next; protected slots are copied to
+  // row i (sinks) or i - M.  Thread = (pair n, 16-byte chunk ch) of the tile; the
+  // arithmetic is the merge pass's.
   auto merge_tile = [&](int tt) {
     constexpr int CPR = M::CPR, E = 8;
     if (tid >= (kT2 / 2) * CPR) return;
@@ -693,10 +729,21 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     const uint4 k1 = *reinterpret_cast<const uint4*>(K_ + chunk_off<D>(16 + pn, ch));
     const uint4 v0 = *reinterpret_cast<const uint4*>(V_ + chunk_off<D>(pn, ch));
     const uint4 v1 = *reinterpret_cast<const uint4*>(V_ + chunk_off<D>(16 + pn, ch));
-    // tile start: its pairs go to rows pos0 + pn (c0 - S is even, so is the tile start - S)
-    const int64_t t0m = c0 + (int64_t)tt * kT2;
-    const int64_t pos0 = a.S + (t0m - a.S) / 2;
-    if (m0 >= a.S && m0 + 1 < pend && m0 >= lo && m0 + 1 < hi) {
+    // c0 - S is even, so is the tile start - S: slot m0 starts pair (m0 - S) / 2
+    const bool cand = m0 >= a.S && m0 + 1 < pend && m0 >= lo && m0 + 1 < hi;
+    bool mrg = cand;
+    int64_t pos0;   // output row of the pair (merged) or of slot m0 (copied)
+    if constexpr (PARTIAL) {
+      const int64_t p = (m0 - a.S) / 2;
+      const int64_t rel = p - sel_c0 * kChunkPairs;
+      const int k = cand ? (int)(rel >> 6) : 0, bit = (int)(rel & 63);
+      const uint64_t mk = selm[k];
+      mrg = cand && ((mk >> bit) & 1ull);
+      pos0 = a.S + 2 * p - (selo[k] + __popcll(mk & ((1ull << bit) - 1ull)));
+    } else {
+      pos0 = a.S + (m0 - a.S) / 2;
+    }
+    if (mrg) {
       const int ls = tt * kT2 + 2 * pn;
       float g0 = 0.f, g1 = 0.f, gx = 0.f;
 #pragma unroll
@@ -707,33 +754,32 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       }
       float w0, w1;
       closed_form_weights(g0, gx, g1, w0, w1);
-      const int lofs = pn * D + ch * E;
       {   // keys, then values: half the live temporaries
         float f0[E], f1[E], o[E];
         unpack<bf16>(k0, f0);
         unpack<bf16>(k1, f1);
         merge_keys<E>(f0, f1, w0, w1, o);
-        store_elems<TO, E>(Ko + pos0 * D + lofs, o);
+        store_elems<TO, E>(Ko + pos0 * D + ch * E, o);
       }
       {
         float f0[E], f1[E], o[E];
         unpack<bf16>(v0, f0);
         unpack<bf16>(v1, f1);
         merge_values<E>(f0, f1, n0, n1, o);
-        store_elems<TO, E>(Vo + pos0 * D + lofs, o);
+        store_elems<TO, E>(Vo + pos0 * D + ch * E, o);
       }
       const int nt = n0 + n1;
       if (ch == 0) {
-        no[pos0 + pn] = nt;
-        so[pos0 + pn] = (int32_t)m0;
+        no[pos0] = nt;
+        so[pos0] = (int32_t)m0;
       }
     } else {
-      // slots outside the candidate pairs (or a pair cut by the chunk edge) are copied
+      // pairs that do not merge, and slots outside the candidate pairs, are copied
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int64_t i = m0 + r;
-        if (i < lo || i >= hi || (i >= a.S && i < pend)) continue;
-        const int64_t pos = i < a.S ? i : i - a.P;
+        if (i < lo || i >= hi || (!cand && i >= a.S && i < pend)) continue;
+        const int64_t pos = cand ? pos0 + r : i < a.S ? i : i - a.M;
         const uint4 kc = r ? k1 : k0, vc = r ? v1 : v0;
         float f[E];
         unpack<bf16>(kc, f);
@@ -869,39 +915,48 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
     if (e == hipSuccess) e = launch_fill_zero(p2.g_cross, BH * r.P, st);
     if (e != hipSuccess) return e;
   }
+  if (merge && r.M > 0 && r.M < r.P) {
+    // partial round: choose the pairs from the pass-1 cosine before pass 2 merges them
+    e = launch_select(s, r, nullptr, nullptr, p2.cos, nullptr, nullptr, const_cast<int32_t*>(p2.sel), st);
+    if (e != hipSuccess) return e;
+  }
   int64_t chunk2;
   int nsplit2;
   p2_plan(s, r, chunk2, nsplit2);
   const dim3 grid2((unsigned)(BH * nsplit2 * nqb));
   const dim3 blk(kW2 * 64);
   const int bhi = (int)BH;
+  const bool part = merge && r.M < r.P;
+#define KVS_P2(NAME, HN, MG, PT, TO)                                                                        \
+  KVS_LAUNCH(NAME, (p2_mfma_kernel<D, HN, MG, PT, TO>), grid2, blk, 0, st, p2, base, chunk2, nsplit2, bhi)
   if (merge == 0) {
-    if (p2.n)
-      KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, true, false, bf16>), grid2, blk, 0, st, p2, base, chunk2, nsplit2, bhi);
-    else
-      KVS_LAUNCH("score_pass2", (p2_mfma_kernel<D, false, false, bf16>), grid2, blk, 0, st, p2, base, chunk2, nsplit2, bhi);
-  } else if (merge == 1) {
-    if (p2.n)
-      KVS_LAUNCH("score_pass2_merge", (p2_mfma_kernel<D, true, true, bf16>), grid2, blk, 0, st, p2, base, chunk2, nsplit2,
-                 bhi);
-    else
-      KVS_LAUNCH("score_pass2_merge", (p2_mfma_kernel<D, false, true, bf16>), grid2, blk, 0, st, p2, base, chunk2,
-                 nsplit2, bhi);
+    if (p2.n) KVS_P2("score_pass2", true, false, false, bf16);
+    else KVS_P2("score_pass2", false, false, false, bf16);
+  } else if (!part) {
+    if (merge == 1) {
+      if (p2.n) KVS_P2("score_pass2_merge", true, true, false, bf16);
+      else KVS_P2("score_pass2_merge", false, true, false, bf16);
+    } else {
+      if (p2.n) KVS_P2("score_pass2_merge", true, true, false, float);
+      else KVS_P2("score_pass2_merge", false, true, false, float);
+    }
   } else {
-    if (p2.n)
-      KVS_LAUNCH("score_pass2_merge", (p2_mfma_kernel<D, true, true, float>), grid2, blk, 0, st, p2, base, chunk2,
-                 nsplit2, bhi);
-    else
-      KVS_LAUNCH("score_pass2_merge", (p2_mfma_kernel<D, false, true, float>), grid2, blk, 0, st, p2, base, chunk2,
-                 nsplit2, bhi);
+    if (merge == 1) {
+      if (p2.n) KVS_P2("score_pass2_merge", true, true, true, bf16);
+      else KVS_P2("score_pass2_merge", false, true, true, bf16);
+    } else {
+      if (p2.n) KVS_P2("score_pass2_merge", true, true, true, float);
+      else KVS_P2("score_pass2_merge", false, true, true, float);
+    }
   }
+#undef KVS_P2
   return hipGetLastError();
 }
 
 static hipError_t launch_score_any(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
                                    const void* Qw, float* lse, float* O, float* g_self, float* g_cross, float* cos,
-                                   void* ws, const OutP* o, void* K_out, void* V_out, int32_t* n_out,
-                                   int32_t* src_out, hipStream_t st) {
+                                   void* ws, const OutP* o, int32_t* sel_state, void* K_out, void* V_out,
+                                   int32_t* n_out, int32_t* src_out, hipStream_t st) {
   int64_t base;
   P1Args p1;
   p1.K = K;
@@ -943,6 +998,7 @@ static hipError_t launch_score_any(const Shape& s, const RoundP& r, const void* 
   p2.GW = p1.GW;
   p2.scale = r.scale;
   int merge = 0;
+  p2.M = r.M;
   if (o) {
     p2.Ko = K_out;
     p2.Vo = V_out;
@@ -950,6 +1006,9 @@ static hipError_t launch_score_any(const Shape& s, const RoundP& r, const void* 
     p2.so = src_out;
     p2.osb = o->sb;
     p2.osh = o->sh;
+    p2.cos = cos;
+    p2.sel = sel_state;
+    p2.sel_stride = sel_stride_ints(r.P);
     merge = o->bf16 ? 1 : 2;
   }
   CosArgs ca;
@@ -968,19 +1027,20 @@ hipError_t launch_score_mfma(const Shape& s, const RoundP& r, const void* K, con
                              const void* Qw, float* lse, float* O, float* g_self, float* g_cross, float* cos,
                              void* ws, hipStream_t st) {
   return launch_score_any(s, r, K, V, n, Qw, lse, O, g_self, g_cross, cos, ws, nullptr, nullptr, nullptr, nullptr,
-                          nullptr, st);
+                          nullptr, nullptr, st);
 }
 
 bool fused_round_ok(const Shape& s, const RoundP& r) {
-  return use_mfma_scorer(s) && r.M == r.P && (int64_t)s.G * r.W <= kQB;
+  return use_mfma_scorer(s) && (int64_t)s.G * r.W <= kQB;
 }
 
 hipError_t launch_score_merge_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
                                    const void* Qw, float* lse, float* O, float* g_self, float* g_cross, void* ws,
-                                   const OutP& o, void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
-                                   hipStream_t st) {
-  return launch_score_any(s, r, K, V, n, Qw, lse, O, g_self, g_cross, nullptr, ws, &o, K_out, V_out, n_out, src_out,
-                          st);
+                                   float* cos, int32_t* sel_state, const OutP& o, void* K_out, void* V_out,
+                                   int32_t* n_out, int32_t* src_out, hipStream_t st) {
+  const bool part = r.M > 0 && r.M < r.P;
+  return launch_score_any(s, r, K, V, n, Qw, lse, O, g_self, g_cross, part ? cos : nullptr, ws, &o,
+                          part ? sel_state : nullptr, K_out, V_out, n_out, src_out, st);
 }
 
 }  // namespace kvs

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libkvslim.so")
 KVS_OK, KVS_ERR_NULL, KVS_ERR_SHAPE, KVS_ERR_DTYPE, KVS_ERR_STRIDE, KVS_ERR_ALIGN, \
     KVS_ERR_INFEASIBLE, KVS_ERR_WORKSPACE, KVS_ERR_HIP = range(9)
 KVS_BF16, KVS_F32 = 0, 1
-KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE = range(4)
+KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE, KVS_OP_SCORE_MERGE = range(5)
 
 EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_score_merge", "kvs_merge_weights", "kvs_merge_compact",
            "kvs_decode_attn", "kvs_marks_begin", "kvs_marks_end", "kvs_mark_name", "kvs_mark_ms", "kvs_status_str",

@@ -38,7 +38,7 @@ def alloc_round(K: torch.Tensor, n_q_heads: int, window: int, n_sink: int, n_rec
     f32 = torch.float32
     cache = L.cache_desc(K, n_q_heads, N)
     rnd = L.round_desc(window, n_sink, n_recent, n_merge, 1.0 / math.sqrt(D))
-    ws = L.workspace_bytes(L.KVS_OP_SCORE, cache, rnd)
+    ws = max(L.workspace_bytes(L.KVS_OP_SCORE, cache, rnd), L.workspace_bytes(L.KVS_OP_SCORE_MERGE, cache, rnd))
     ss = L.workspace_bytes(L.KVS_OP_SEL_STATE, cache, rnd)
     ocap = T if out_capacity is None else out_capacity
     odt = K.dtype if out_dtype is None else out_dtype
@@ -77,18 +77,26 @@ def run_round(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: i
     return bufs
 
 
-def run_full_round_fused(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: int,
-                         bufs: RoundBuffers, n_slots: int | None = None):
-    """A full round (every candidate pair merges) through kvs_score_merge."""
+def run_round_fused(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: int, n_merge: int,
+                    bufs: RoundBuffers, n_slots: int | None = None):
+    """A whole round (any 0 <= n_merge <= P) through kvs_score_merge; selection flags and
+    weights are not produced."""
     B, H, cap, D = K.shape
     N = cap if n_slots is None else n_slots
-    P = L.num_pairs(N, n_sink, n_recent)
     cache = L.cache_desc(K, n_q_heads, N)
-    rnd = L.round_desc(window, n_sink, n_recent, P, 1.0 / math.sqrt(D))
-    out = L.cache_desc(bufs.K, n_q_heads, N - P)
+    rnd = L.round_desc(window, n_sink, n_recent, n_merge, 1.0 / math.sqrt(D))
+    out = L.cache_desc(bufs.K, n_q_heads, N - n_merge)
     L.kvs_score_merge(cache, K, V, n, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, out,
                       bufs.K, bufs.V, bufs.n, bufs.src, bufs.score_ws)
     return bufs
+
+
+def run_full_round_fused(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: int,
+                         bufs: RoundBuffers, n_slots: int | None = None):
+    """A full round (every candidate pair merges) through kvs_score_merge."""
+    N = K.shape[2] if n_slots is None else n_slots
+    P = L.num_pairs(N, n_sink, n_recent)
+    return run_round_fused(K, V, n, Qw, n_q_heads, window, n_sink, n_recent, P, bufs, n_slots)
 
 
 def merge_round(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: int, n_merge: int,
@@ -199,7 +207,7 @@ def alloc_stream(B: int, H: int, n_q_heads: int, D: int, dtype, device, window: 
         for N, M in s.rounds:
             c = L.KvsCache(B, H, n_q_heads, D, N, H * cap * D, cap * D)
             r = L.round_desc(window, n_sink, 0, M, 1.0 / math.sqrt(D))
-            ws = max(ws, L.workspace_bytes(L.KVS_OP_SCORE, c, r))
+            ws = max(ws, L.workspace_bytes(L.KVS_OP_SCORE, c, r), L.workspace_bytes(L.KVS_OP_SCORE_MERGE, c, r))
             ss = max(ss, L.workspace_bytes(L.KVS_OP_SEL_STATE, c, r))
     shared = dict(
         lse=torch.empty(B, n_q_heads, window, dtype=f32, device=device),
@@ -220,13 +228,14 @@ def alloc_stream(B: int, H: int, n_q_heads: int, D: int, dtype, device, window: 
 
 
 def run_stream(K_src, V_src, window_queries, n_q_heads: int, window: int, n_sink: int, plan: list,
-               st: StreamBuffers, on_round=None):
+               st: StreamBuffers, on_round=None, fused: bool = True):
     """Run the chunked budget loop on the current stream.  K_src, V_src [B, H_kv, total, D]
     hold the raw tokens (a prefill would write each chunk in turn); window_queries(c) gives
     the observation window [B, H_q, W, D] of chunk c (its last W queries).  Each chunk is
     appended with count 1 to the current cache, then each planned round reads that cache
-    and writes the other one.  on_round(c, K, V, n, Qw, N, M, out) runs after each round is
-    enqueued.  Returns (buffers holding the final cache, its slot count)."""
+    and writes the other one, through kvs_score_merge (fused) or the three separate calls.
+    on_round(c, K, V, n, Qw, N, M, out) runs after each round is enqueued.  Returns
+    (buffers holding the final cache, its slot count)."""
     cur, N = 0, 0
     for c, s in enumerate(plan):
         b = st.bufs[cur]
@@ -239,7 +248,8 @@ def run_stream(K_src, V_src, window_queries, n_q_heads: int, window: int, n_sink
         Qw = window_queries(c)
         for Nr, M in s.rounds:
             out = st.bufs[1 - cur]
-            run_round(b.K, b.V, b.n, Qw, n_q_heads, window, n_sink, 0, M, out, n_slots=Nr)
+            step = run_round_fused if fused else run_round
+            step(b.K, b.V, b.n, Qw, n_q_heads, window, n_sink, 0, M, out, n_slots=Nr)
             if on_round is not None:
                 on_round(c, b.K, b.V, b.n, Qw, Nr, M, out)
             cur, b, N = 1 - cur, out, Nr - M

@@ -1,7 +1,8 @@
-"""GPU: kvs_score_merge (a full round in one call; the merge runs inside the scorer's
-second pass when the shape allows) against kvs_score followed by kvs_merge_compact,
-bit for bit, and against the oracle.  Shapes that the fused kernel does not take (fp32,
-more than 128 window queries per kv head) exercise the two-pass path of the same call."""
+"""GPU: kvs_score_merge (a whole round in one call; for partial rounds the selection runs
+between the scorer's passes, and the merge runs inside the second pass when the shape
+allows) against kvs_score -> kvs_merge_weights -> kvs_merge_compact, bit for bit, and
+against the oracle.  Shapes that the fused kernel does not take (fp32, more than 128
+window queries per kv head) exercise the separate-pass path of the same call."""
 import math
 import zlib
 
@@ -32,17 +33,16 @@ def _same(a, b, what):
     assert torch.equal(a, b), f"{what}: {(a != b).sum().item()} elements differ"
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_fused_round_matches_two_calls(case):
+def _compare(K, V, n, Qw, Hq, W, S, R, M, N, odt):
     from long_context_kv_kvslimmer_amd import pipeline
-    name, B, Hkv, Hq, D, N, cap, W, S, R, dtype, counts, odt = case
-    print(f"\n[fused] {name}", flush=True)
-    K, V, n, Qw = make_inputs(zlib.crc32(name.encode()) % 10000, B, Hkv, Hq, D, N, cap, W, dtype, counts)
     P = O.num_pairs(N, S, R)
-    T = N - P
-    ref = pipeline.merge_round(K, V, n, Qw, Hq, W, S, R, P, n_slots=N, out_dtype=odt, want_flags=False)
-    fused = pipeline.alloc_round(K, Hq, W, S, R, P, n_slots=N, out_dtype=odt)
-    pipeline.run_full_round_fused(K, V, n, Qw, Hq, W, S, R, fused, n_slots=N)
+    T = N - M
+    ref = pipeline.merge_round(K, V, n, Qw, Hq, W, S, R, M, n_slots=N, out_dtype=odt, want_flags=False)
+    fused = pipeline.alloc_round(K, Hq, W, S, R, M, n_slots=N, out_dtype=odt)
+    if M == P:
+        pipeline.run_full_round_fused(K, V, n, Qw, Hq, W, S, R, fused, n_slots=N)
+    else:
+        pipeline.run_round_fused(K, V, n, Qw, Hq, W, S, R, M, fused, n_slots=N)
     torch.cuda.synchronize()
     _same(fused.lse, ref.lse, "lse")
     _same(fused.O, ref.O, "O")
@@ -52,6 +52,27 @@ def test_fused_round_matches_two_calls(case):
     _same(fused.V[:, :, :T], ref.V[:, :, :T], "V_out")
     _same(fused.n[:, :, :T], ref.n[:, :, :T], "n_out")
     _same(fused.src[:, :, :T], ref.src[:, :, :T], "src_out")
+
+
+@pytest.mark.parametrize("frac", [1.0, 0.29, 0.0])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fused_round_matches_separate_calls(case, frac):
+    name, B, Hkv, Hq, D, N, cap, W, S, R, dtype, counts, odt = case
+    print(f"\n[fused] {name} frac {frac}", flush=True)
+    K, V, n, Qw = make_inputs(zlib.crc32(name.encode()) % 10000, B, Hkv, Hq, D, N, cap, W, dtype, counts)
+    M = int(round(frac * O.num_pairs(N, S, R)))
+    _compare(K, V, n, Qw, Hq, W, S, R, M, N, odt)
+
+
+def test_fused_partial_round_with_tie_runs():
+    """Bit-identical pairs tie at the selection threshold; the cut falls inside a tie run."""
+    K, V, n, Qw = make_inputs(11, 1, 2, 8, 128, 1024, 1024, 8, torch.bfloat16, True)
+    for h in range(2):
+        for p in range(0, 512, 3):          # every third pair: identical rows
+            K[0, h, 2 * p + 1] = K[0, h, 2 * p]
+    for M in (1, 100, 171, 172, 300):       # 171 pairs tie at cosine 1
+        print(f"\n[fused ties] M={M}", flush=True)
+        _compare(K, V, n, Qw, 8, 8, 0, 0, M, 1024, torch.bfloat16)
 
 
 def test_fused_round_against_oracle():
@@ -64,3 +85,11 @@ def test_fused_round_against_oracle():
     torch.cuda.synchronize()
     for h in range(Hkv):
         check_round_slice(bufs, K, V, n, Qw, 0, h, N, S, R, P, 1 / math.sqrt(D), label=f"fused h{h}", with_cos=False)
+    # a partial round: the oracle's own selection decides the compaction it is compared with
+    M = 173
+    bufs = pipeline.alloc_round(K, Hq, W, S, R, M, n_slots=N, out_dtype=torch.float32, want_flags=False)
+    pipeline.run_round_fused(K, V, n, Qw, Hq, W, S, R, M, bufs, n_slots=N)
+    torch.cuda.synchronize()
+    for h in range(Hkv):
+        check_round_slice(bufs, K, V, n, Qw, 0, h, N, S, R, M, 1 / math.sqrt(D), label=f"fused partial h{h}",
+                          with_cos=False)

@@ -164,8 +164,20 @@ def test_score_merge_validation(L):
     o = L.KvsCache(1, 2, 8, 128, 500, 2 * 500 * 128, 500 * 128)
     r_partial = L.round_desc(8, 0, 0, 100, 0.1)
     args = [FAKE, FAKE, None, FAKE]
+    # out must hold N - M slots
     assert f(ctypes.byref(c), L.KVS_BF16, *args, ctypes.byref(r_partial), FAKE, FAKE, FAKE, FAKE, ctypes.byref(o),
              L.KVS_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == L.KVS_ERR_SHAPE
+    # a partial round needs room for the cosine and the selection state as well
+    o900 = L.KvsCache(1, 2, 8, 128, 900, 2 * 900 * 128, 900 * 128)
+    ws_score = L.workspace_bytes(L.KVS_OP_SCORE, c, r_partial)
+    ws_part = L.workspace_bytes(L.KVS_OP_SCORE_MERGE, c, r_partial)
+    assert ws_part >= ws_score + 2 * 500 * 4
+    assert f(ctypes.byref(c), L.KVS_BF16, *args, ctypes.byref(r_partial), FAKE, FAKE, FAKE, FAKE, ctypes.byref(o900),
+             L.KVS_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == L.KVS_ERR_WORKSPACE
+    r_all = L.round_desc(8, 0, 0, 500, 0.1)
+    r_none = L.round_desc(8, 0, 0, 0, 0.1)
+    assert L.workspace_bytes(L.KVS_OP_SCORE_MERGE, c, r_all) == L.workspace_bytes(L.KVS_OP_SCORE, c, r_all)
+    assert L.workspace_bytes(L.KVS_OP_SCORE_MERGE, c, r_none) == L.workspace_bytes(L.KVS_OP_SCORE, c, r_none)
     r_full = L.round_desc(8, 0, 0, 500, 0.1)
     bad_out = L.KvsCache(1, 2, 8, 128, 499, 2 * 500 * 128, 500 * 128)
     assert f(ctypes.byref(c), L.KVS_BF16, *args, ctypes.byref(r_full), FAKE, FAKE, FAKE, FAKE, ctypes.byref(bad_out),
