@@ -11,6 +11,7 @@
  *                      closed-form key-merge weights
  *   kvs_merge_compact  key merge, lossless value-slot merge, stream compaction
  *   kvs_decode_attn    GQA decode attention over a (merged) cache
+ *   kvs_append         write raw tokens (count 1) into a cache: a prefill chunk or a decode step
  *
  * Sources.  The operations follow the KVSlimmer deep-dive "论文专题讲解：KVSlimmer：
  * 非对称 KV 合并的数学与工程" (charles2530.github.io), sections 数学主线二 (merging an adjacent
@@ -203,6 +204,22 @@ kvs_status kvs_merge_compact(const kvs_cache* cache, kvs_dtype in_dtype,
                              const kvs_cache* out, kvs_dtype out_dtype,
                              void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
                              void* stream);
+
+/*
+ * kvs_append — the cache write of new raw tokens (a prefill chunk in the chunked regime of
+ * the deep-dive's section 实验设置, or a decode step): for every (b, h), rows
+ * [from, from + count) of the source (K_new, V_new; layout `src`, its n_slots = the rows
+ * it holds) are copied to rows [at, at + count) of the cache (K, V; layout `cache`, its
+ * n_slots = the rows allocated), and n[b, h, at .. at + count) = 1 (a raw token is a slot
+ * of count 1, as in kvs_score); n is nullable.  Both layouts share batch, n_kv_heads,
+ * head_dim and `dtype`; the source and destination rows must not overlap.  Errors:
+ * KVS_ERR_SHAPE if at + count exceeds the cache rows, from + count the source rows, or the
+ * layouts differ; KVS_ERR_ALIGN unless K, V, K_new, V_new are 16-byte aligned;
+ * KVS_ERR_NULL for missing pointers when count > 0.  Enqueued on `stream`.
+ */
+kvs_status kvs_append(const kvs_cache* cache, kvs_dtype dtype, void* K, void* V, int32_t* n, int64_t at,
+                      const kvs_cache* src, const void* K_new, const void* V_new, int64_t from, int64_t count,
+                      void* stream);
 
 /*
  * kvs_decode_attn — decode attention over a (merged) cache (deep-dive 数学主线三

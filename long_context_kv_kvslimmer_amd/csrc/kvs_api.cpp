@@ -268,6 +268,31 @@ kvs_status kvs_score_merge(const kvs_cache* cache, kvs_dtype dtype, const void* 
   return hip_status(e, "kvs_score_merge");
 }
 
+kvs_status kvs_append(const kvs_cache* cache, kvs_dtype dtype, void* K, void* V, int32_t* n, int64_t at,
+                      const kvs_cache* src, const void* K_new, const void* V_new, int64_t from, int64_t count,
+                      void* stream) {
+  kvs::Shape s, ss;
+  kvs_status st = check_cache(cache, dtype, s);
+  if (st) return st;
+  if ((st = check_cache(src, dtype, ss))) return st;
+  if (ss.B != s.B || ss.Hkv != s.Hkv || ss.D != s.D)
+    return fail(KVS_ERR_SHAPE, "kvs_append: source and cache must share batch, n_kv_heads and head_dim");
+  if (at < 0 || from < 0 || count < 0) return fail(KVS_ERR_SHAPE, "kvs_append: at, from and count must be >= 0");
+  if (at + count > s.N)
+    return fail(KVS_ERR_SHAPE, "kvs_append: rows [%lld, %lld) exceed the cache's %lld rows", (long long)at,
+                (long long)(at + count), (long long)s.N);
+  if (from + count > ss.N)
+    return fail(KVS_ERR_SHAPE, "kvs_append: source rows [%lld, %lld) exceed its %lld rows", (long long)from,
+                (long long)(from + count), (long long)ss.N);
+  if (count == 0) return KVS_OK;
+  if (!K || !V || !K_new || !V_new) return fail(KVS_ERR_NULL, "kvs_append: K, V, K_new and V_new are required");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(K_new) || !aligned16(V_new))
+    return fail(KVS_ERR_ALIGN, "kvs_append: K, V, K_new, V_new must be 16-byte aligned");
+  return hip_status(kvs::launch_append(s, ss, K, V, n, at, K_new, V_new, from, count,
+                                       static_cast<hipStream_t>(stream)),
+                    "kvs_append");
+}
+
 kvs_status kvs_merge_weights(const kvs_cache* cache, const kvs_round* round, const float* g_self,
                              const float* g_cross, const float* cos, float* w, uint8_t* selected, void* sel_state,
                              size_t sel_state_bytes, void* workspace, size_t workspace_bytes, void* stream) {

@@ -64,6 +64,10 @@ hipError_t launch_merge(const Shape& s, const RoundP& r, const void* K, const vo
                         const float* g_self, const float* g_cross, const int32_t* sel_state, const OutP& o,
                         void* K_out, void* V_out, int32_t* n_out, int32_t* src_out, hipStream_t st);
 
+// ---- append raw tokens (count 1) into a cache ----
+hipError_t launch_append(const Shape& dst, const Shape& src, void* K, void* V, int32_t* n, int64_t at,
+                         const void* K_new, const void* V_new, int64_t from, int64_t count, hipStream_t st);
+
 // ---- log-sum-exp combine of split partial records {m (log2 units), l, -, -, o[D]} ----
 // Optional operand pack for the bf16 MFMA pass 2 (written by the combine, read by pass 2):
 // per kv head, the window queries in blocks of 32 (one wave each), two 16-query halves;

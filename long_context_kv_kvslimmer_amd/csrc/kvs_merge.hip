@@ -253,3 +253,62 @@ hipError_t launch_merge(const Shape& s, const RoundP& r, const void* K, const vo
 }
 
 }  // namespace kvs
+
+namespace kvs {
+
+// ------------------------------------------------------------------ append --
+// Rows [from, from + count) of every (b, h) of the source go to rows [at, at + count) of
+// the cache; their counts become 1.  One thread per 16-byte piece of a row, grid-stride.
+struct AppendArgs {
+  const uint8_t* Ks;
+  const uint8_t* Vs;
+  uint8_t* Kd;
+  uint8_t* Vd;
+  int32_t* n;
+  int64_t at, from, count, total;
+  int64_t sb, sh, dsb, dsh;   // element strides of the source and of the cache
+  int Hkv, D, esz, cpr;       // element bytes, 16-byte pieces per row
+};
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.total; i += (int64_t)gridDim.x * 256) {
+    const int64_t c = i % a.cpr, rest = i / a.cpr;
+    const int64_t r = rest % a.count, bh = rest / a.count;
+    const int64_t b = bh / a.Hkv, h = bh - b * a.Hkv;
+    const int64_t so = ((b * a.sb + h * a.sh) + (a.from + r) * a.D) * a.esz + c * 16;
+    const int64_t dro = (b * a.dsb + h * a.dsh) / a.D + a.at + r;   // cache row
+    const int64_t dof = dro * a.D * a.esz + c * 16;
+    *reinterpret_cast<uint4*>(a.Kd + dof) = *reinterpret_cast<const uint4*>(a.Ks + so);
+    *reinterpret_cast<uint4*>(a.Vd + dof) = *reinterpret_cast<const uint4*>(a.Vs + so);
+    if (a.n && c == 0) a.n[dro] = 1;
+  }
+}
+
+hipError_t launch_append(const Shape& dst, const Shape& src, void* K, void* V, int32_t* n, int64_t at,
+                         const void* K_new, const void* V_new, int64_t from, int64_t count, hipStream_t st) {
+  AppendArgs a;
+  a.Ks = static_cast<const uint8_t*>(K_new);
+  a.Vs = static_cast<const uint8_t*>(V_new);
+  a.Kd = static_cast<uint8_t*>(K);
+  a.Vd = static_cast<uint8_t*>(V);
+  a.n = n;
+  a.at = at;
+  a.from = from;
+  a.count = count;
+  a.sb = src.sb;
+  a.sh = src.sh;
+  a.dsb = dst.sb;
+  a.dsh = dst.sh;
+  a.Hkv = dst.Hkv;
+  a.D = dst.D;
+  a.esz = dst.bf16 ? 2 : 4;
+  a.cpr = dst.D * a.esz / 16;
+  a.total = (int64_t)dst.B * dst.Hkv * count * a.cpr;
+  if (a.total == 0) return hipSuccess;
+  int64_t blocks = (a.total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  KVS_LAUNCH("append", append_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

@@ -21,6 +21,7 @@ KVS_BF16, KVS_F32 = 0, 1
 KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE, KVS_OP_SCORE_MERGE = range(5)
 
 EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_score_merge", "kvs_merge_weights", "kvs_merge_compact",
+           "kvs_append",
            "kvs_decode_attn", "kvs_marks_begin", "kvs_marks_end", "kvs_mark_name", "kvs_mark_ms", "kvs_status_str",
            "kvs_last_error", "kvs_version")
 
@@ -57,6 +58,7 @@ def _load():
         "kvs_merge_weights": (ctypes.c_int, [C, R, P, P, P, P, P, P, SZ, P, SZ, P]),
         "kvs_merge_compact": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, P, R, P, C, ctypes.c_int, P, P, P, P, P]),
         "kvs_decode_attn": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, F, P, P, SZ, P]),
+        "kvs_append": (ctypes.c_int, [C, ctypes.c_int, P, P, P, I64, C, P, P, I64, I64, P]),
         "kvs_marks_begin": (ctypes.c_int, [I32, ctypes.c_char_p]),
         "kvs_marks_end": (I32, []),
         "kvs_mark_name": (ctypes.c_char_p, [I32]),
@@ -206,3 +208,13 @@ def kvs_decode_attn(cache: KvsCache, K, V, n, q, sm_scale: float, out, workspace
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.kvs_decode_attn(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(q),
                                 ctypes.c_float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream()))
+
+
+def kvs_append(cache: KvsCache, K, V, n, at: int, src: KvsCache, K_new, V_new, from_: int, count: int):
+    """Copy rows [from_, from_ + count) of K_new/V_new into rows [at, at + count) of K/V, counts 1."""
+    _same_layout(K, V)
+    _same_layout(K_new, V_new)
+    if K.dtype != K_new.dtype:
+        raise ValueError("cache and source must share a dtype")
+    _check(_lib.kvs_append(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), at, ctypes.byref(src),
+                           _ptr(K_new), _ptr(V_new), from_, count, _stream()))

@@ -232,16 +232,15 @@ def run_stream(K_src, V_src, window_queries, n_q_heads: int, window: int, n_sink
     """Run the chunked budget loop on the current stream.  K_src, V_src [B, H_kv, total, D]
     hold the raw tokens (a prefill would write each chunk in turn); window_queries(c) gives
     the observation window [B, H_q, W, D] of chunk c (its last W queries).  Each chunk is
-    appended with count 1 to the current cache, then each planned round reads that cache
+    appended with count 1 to the current cache (kvs_append), then each planned round reads that cache
     and writes the other one, through kvs_score_merge (fused) or the three separate calls.
     on_round(c, K, V, n, Qw, N, M, out) runs after each round is enqueued.  Returns
     (buffers holding the final cache, its slot count)."""
     cur, N = 0, 0
+    src = L.cache_desc(K_src, n_q_heads)
     for c, s in enumerate(plan):
         b = st.bufs[cur]
-        b.K[:, :, N:N + s.length].copy_(K_src[:, :, s.c0:s.c0 + s.length])
-        b.V[:, :, N:N + s.length].copy_(V_src[:, :, s.c0:s.c0 + s.length])
-        b.n[:, :, N:N + s.length].fill_(1)
+        L.kvs_append(L.cache_desc(b.K, n_q_heads), b.K, b.V, b.n, N, src, K_src, V_src, s.c0, s.length)
         N += s.length
         if not s.rounds:
             continue

@@ -186,3 +186,21 @@ def test_score_merge_validation(L):
              L.KVS_BF16, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == L.KVS_ERR_NULL
     assert f(ctypes.byref(c), L.KVS_BF16, *args, ctypes.byref(r_full), FAKE, FAKE, FAKE, FAKE, ctypes.byref(o),
              L.KVS_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == L.KVS_ERR_WORKSPACE
+
+
+def test_append_validation(L):
+    f = L._lib.kvs_append
+    c = L.KvsCache(1, 2, 8, 128, 200, 2 * 200 * 128, 200 * 128)
+    src = L.KvsCache(1, 2, 8, 128, 50, 2 * 50 * 128, 50 * 128)
+    other = L.KvsCache(1, 4, 8, 128, 50, 4 * 50 * 128, 50 * 128)
+
+    def call(at, frm, count, s=src, K=FAKE, dt=L.KVS_BF16):
+        return f(ctypes.byref(c), dt, K, FAKE, None, at, ctypes.byref(s), FAKE, FAKE, frm, count, None)
+    assert call(190, 0, 11) == L.KVS_ERR_SHAPE        # past the cache's rows
+    assert call(0, 45, 6) == L.KVS_ERR_SHAPE          # past the source's rows
+    assert call(0, 0, 5, s=other) == L.KVS_ERR_SHAPE  # different head count
+    assert call(-1, 0, 5) == L.KVS_ERR_SHAPE
+    assert call(0, 0, 5, K=None) == L.KVS_ERR_NULL
+    assert call(0, 0, 5, K=ctypes.c_void_p(4104)) == L.KVS_ERR_ALIGN
+    assert call(0, 0, 5, dt=9) == L.KVS_ERR_DTYPE
+    assert call(200, 50, 0) == L.KVS_OK               # nothing to write: no launch
