@@ -1,10 +1,12 @@
 """Benchmark of the KVSlimmer merge path on one MI355X.
 
 One step = the whole hot path on one Llama-3.1-8B-shaped layer at 32K context
-(8 KV heads x 128, 32 query heads, bf16): kvs_score (window statistics and
-Hessian-norm sums) -> kvs_merge_weights -> kvs_merge_compact (merge to 50%,
-32 most recent tokens kept) -> kvs_decode_attn (one decode query per head over
-the merged cache).  Inputs are resident in HBM before timing starts; steps
+(8 KV heads x 128, 32 query heads, bf16): one merge round to 50% with the 32
+most recent tokens kept, in kvs_score_merge (window statistics, Hessian-norm
+sums, closed-form weights, merge and compaction), then kvs_decode_attn (one
+decode query per head over the merged cache).  The same round through the
+separate calls kvs_score -> kvs_merge_weights -> kvs_merge_compact is timed
+beside it, outside the step.  Inputs are resident in HBM before timing starts; steps
 rotate over several input layers whose total exceeds the 256 MB Infinity
 Cache, so every step reads its K/V from HBM.
 
@@ -51,7 +53,9 @@ def kernel_bytes(N, H, D, P, T, GW, has_n=False, elt=2):
 KERNEL_LABELS = (("p1_mfma_kernel", "score_pass1"), ("pass1_valu_kernel", "score_pass1"),
                  ("p2_mfma_kernel", "score_pass2"), ("pass2_valu_kernel", "score_pass2"),
                  ("combine_kernel", "combine"), ("fill_zero_kernel", "fill_zero"), ("pair_cos_kernel", "pair_cos"),
-                 ("select_kernel", "select"), ("select_fixed_kernel", "select"),
+                 ("combine_wave_kernel", "combine"), ("select_fixed_kernel", "select"),
+                 ("select_small_kernel", "select"), ("sel_clear_kernel", "select"), ("sel_hist_kernel", "select"),
+                 ("sel_count_kernel", "select"), ("sel_final_kernel", "select"), ("append_kernel", "append"),
                  ("merge_compact_kernel", "merge_compact"), ("decode_mfma_kernel", "decode"),
                  ("decode_kernel", "decode"))
 COPY_BYTES = 1 << 30            # calibration copy: reads and writes this many bytes
@@ -165,6 +169,23 @@ def summarize_trace(stats_csv, bench_json, cmd):
                    f"{e.get('algorithmic_MB', 0)} | {e.get('GBps')} |")
     out += ["", f"ms_per_step {line['ms_per_step']}, value {line['value']} {line['unit']}, roofline "
             f"{json.dumps(line['roofline'])}"]
+    return "\n".join(out) + "\n"
+
+
+def summarize_stats(stats_csv, title, cmd):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run: launches, mean and total
+    duration per kernel label."""
+    import csv
+    rows = {}
+    for r in csv.DictReader(open(stats_csv)):
+        lab = kernel_label(r["Name"])
+        if lab:
+            c, t = rows.get(lab, (0, 0.0))
+            rows[lab] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
+    out = [f"# {title}", "", "Made by:", "", "```", cmd, "```", "",
+           "| kernel | launches | rocprofv3 avg us | total ms |", "|---|---:|---:|---:|"]
+    for lab, (c, t) in sorted(rows.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| {lab} | {c} | {t / c / 1e3:.2f} | {t / 1e6:.3f} |")
     return "\n".join(out) + "\n"
 
 
@@ -524,9 +545,13 @@ def main():
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "BENCH_JSON", "CMD"))
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("SQ_CSV", "STATS_CSV", "CMD"))
     ap.add_argument("--summarize-per-config", nargs=2, metavar=("JSONL", "CMD"))
-    ap.add_argument("--per-config", type=str, default=None, metavar="1,2,3,4,5",
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "TITLE", "CMD"))
+    ap.add_argument("--per-config", type=str, default=None, metavar="1,2,3,4,5,6",
                     help="print per-config merge and decode timings (one JSON line per config) instead of the bench line")
     args = ap.parse_args()
+    if args.summarize_stats:
+        sys.stdout.write(summarize_stats(*args.summarize_stats))
+        return
     if args.summarize_per_config:
         sys.stdout.write(summarize_per_config(*args.summarize_per_config))
         return
