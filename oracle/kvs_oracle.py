@@ -314,6 +314,33 @@ def merge_round(K, V, n, Qw, scale, n_sink, n_recent, n_merge) -> RoundResult:
 
     # 1. window attention statistics
     lse, alpha, O = window_statistics(K, V, None if n is None else nn, Qw, scale)
+    return _round_steps_2_to_7(K, V, nn, lse, alpha, O, n_sink, P, n_merge)
+
+
+def merge_round_given_stats(K, V, n, Qw, lse, O, scale, n_sink, n_recent, n_merge) -> RoundResult:
+    """The same round when the window statistics come from elsewhere (the prefill
+    attention that already computed them): lse [GW] and O [GW, D] are taken as given
+    instead of step 1, and the attention weights follow from them by the definition of
+    [DD] 数学主线三, α_{w,i} = exp(e_{w,i} − lse_w) with e = scale·q·k + ln n.  With the
+    lse and O of ``window_statistics`` this is ``merge_round``."""
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    Qw = np.asarray(Qw, F64)
+    N, D = K.shape
+    nn = np.ones(N, dtype=np.int64) if n is None else np.asarray(n, dtype=np.int64)
+    P = num_pairs(N, n_sink, n_recent)
+    if not (0 <= n_merge <= P):
+        raise ValueError("infeasible merge count")
+    lse = np.asarray(lse, F64)
+    O = np.asarray(O, F64)
+    alpha = np.empty((Qw.shape[0], N))
+    for w in range(Qw.shape[0]):
+        e = scale * (K @ Qw[w]) + np.log(nn.astype(F64))
+        alpha[w] = np.exp(e - lse[w])
+    return _round_steps_2_to_7(K, V, nn, lse, alpha, O, n_sink, P, n_merge)
+
+
+def _round_steps_2_to_7(K, V, nn, lse, alpha, O, n_sink, P, n_merge) -> RoundResult:
     # 2. Hessian-norm sums
     g_self, g_cross = hessian_norm_sums(V, alpha, O, n_sink, P)
     # 3. adjacent-key similarity

@@ -483,3 +483,29 @@ def test_stream_rejects_budget_not_above_sinks():
     K, V, Qs = _stream_inputs(34, 20, 4, 2, 8)
     with pytest.raises(ValueError):
         O.stream_prefill(K, V, Qs, 0.3, 8, 8, 8)
+
+
+# ------------------------------------------------- round given the statistics --
+def test_given_stats_equal_computed_stats():
+    """Supplying the statistics the window attention computes reproduces the round."""
+    K, V, n, Q = _random_slice(40, counts=True)
+    for S, R, M in ((0, 0, 20), (2, 3, 7), (1, 0, 0)):
+        ref = O.merge_round(K, V, n, Q, 0.4, S, R, M)
+        r = O.merge_round_given_stats(K, V, n, Q, ref.lse, ref.O, 0.4, S, R, M)
+        assert np.allclose(r.g_self, ref.g_self, rtol=1e-13, atol=0)
+        assert np.allclose(r.g_cross, ref.g_cross, rtol=1e-13, atol=0)
+        assert np.array_equal(r.selected, ref.selected) and np.array_equal(r.src, ref.src)
+        assert np.allclose(r.K, ref.K, atol=1e-13) and np.array_equal(r.n, ref.n)
+
+
+def test_given_stats_handworked():
+    """N = 4 one-dimensional slots, one zero query: alpha = 1/4 for every slot whatever the
+    keys, lse = ln 4.  With a supplied O = 10 (not the attention output 2.5), by hand:
+    g_self[i] = 1/4 |1 - 1/2| |v_i - 10| = (9, 8, 7, 6) / 8 and
+    g_cross[p] = 1/16 |v_m + v_{m+1} - 20| = (17, 13) / 16."""
+    K = np.array([[0.3], [-1.2], [2.0], [0.7]])
+    V = np.array([[1.0], [2.0], [3.0], [4.0]])
+    Q = np.zeros((1, 1))
+    r = O.merge_round_given_stats(K, V, None, Q, [math.log(4.0)], [[10.0]], 0.5, 0, 0, 1)
+    assert np.allclose(r.g_self, [9 / 8, 8 / 8, 7 / 8, 6 / 8], rtol=1e-15)
+    assert np.allclose(r.g_cross, [17 / 16, 13 / 16], rtol=1e-15)
