@@ -56,6 +56,7 @@ KERNEL_LABELS = (("p1_mfma_kernel", "score_pass1"), ("pass1_valu_kernel", "score
                  ("combine_wave_kernel", "combine"), ("select_fixed_kernel", "select"),
                  ("select_small_kernel", "select"), ("sel_clear_kernel", "select"), ("sel_hist_kernel", "select"),
                  ("sel_count_kernel", "select"), ("sel_final_kernel", "select"), ("append_kernel", "append"),
+                 ("pack_kernel", "pack"),
                  ("merge_compact_kernel", "merge_compact"), ("decode_mfma_kernel", "decode"),
                  ("decode_kernel", "decode"))
 COPY_BYTES = 1 << 30            # calibration copy: reads and writes this many bytes
@@ -321,7 +322,7 @@ def cpu_baseline(cfg, K, V, Qw, heads=2):
                       f"one decode query, fp64 NumPy, 1 BLAS thread, {dt:.1f} s"}
 
 
-def per_config(dev, which, reps=5):
+def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016)):
     """Per-config GPU timings (not the bench line): every merge round of one layer of each
     seeded workload through kvs_score_merge (one call per round), timed with
     events on the library's stream over `reps` repetitions after one warm-up; all layers of a
@@ -335,7 +336,7 @@ def per_config(dev, which, reps=5):
     for idx in which:
         cfg = configs.CONFIGS[idx]
         if cfg.budget:
-            res = stream_timing(cfg, dev, reps)
+            res = stream_timing(cfg, dev, reps, chunks=chunk_sweep)
             lines.append(res)
             print(json.dumps(res), flush=True)
             torch.cuda.empty_cache()
@@ -546,6 +547,8 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("SQ_CSV", "STATS_CSV", "CMD"))
     ap.add_argument("--summarize-per-config", nargs=2, metavar=("JSONL", "CMD"))
     ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "TITLE", "CMD"))
+    ap.add_argument("--no-chunk-sweep", action="store_true",
+                    help="with --per-config 6: time only the 512-token-chunk loop (no chunk-size sweep)")
     ap.add_argument("--per-config", type=str, default=None, metavar="1,2,3,4,5,6",
                     help="print per-config merge and decode timings (one JSON line per config) instead of the bench line")
     args = ap.parse_args()
@@ -577,7 +580,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     if args.per_config:
-        per_config(dev, [int(x) for x in args.per_config.split(",")])
+        per_config(dev, [int(x) for x in args.per_config.split(",")],
+                   chunk_sweep=() if args.no_chunk_sweep else (256, 512, 1024, 2016))
         return
     cfg = configs.C2
     if args.copy_calibration:
@@ -710,10 +714,61 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(dominant)},
     }
+    line["given_window_stats"] = given_stats_timing(args, sets, step, bufs, cache, rnd, out_desc, dec_cache, dec_out,
+                                                    dec_ws, D, B * N, kb)
     if not args.no_cpu_baseline:
         K, V, Qw, _ = sets[0]
         line["cpu_baseline"] = cpu_baseline(cfg, K, V, Qw)
     print(json.dumps(line), flush=True)
+
+
+def given_stats_timing(args, sets, step, bufs, cache, rnd, out_desc, dec_cache, dec_out, dec_ws, D, tokens, kb):
+    """The same step when the prefill attention supplies the window statistics: the round
+    through kvs_score_merge_stats (no first scorer pass), then the decode step.  Each input
+    set's statistics are taken from kvs_score_merge once, before timing."""
+    import torch
+    from long_context_kv_kvslimmer_amd import kvslim as L
+    stats = []
+    for i in range(len(sets)):
+        step(i)
+        stats.append((bufs.lse.clone(), bufs.O.clone()))
+    torch.cuda.synchronize()
+
+    def step_stats(i):
+        K, V, Qw, q = sets[i % len(sets)]
+        lse, O = stats[i % len(sets)]
+        L.kvs_score_merge_stats(cache, K, V, None, Qw, rnd, lse, O, bufs.g_self, bufs.g_cross, out_desc,
+                                bufs.K, bufs.V, bufs.n, bufs.src, bufs.score_ws)
+        L.kvs_decode_attn(dec_cache, bufs.K, bufs.V, bufs.n, q, 1.0 / math.sqrt(D), dec_out, dec_ws)
+
+    for i in range(args.warmup):
+        step_stats(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step_stats(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    marks = L.KernelMarks(max_launches=64)
+    with marks:
+        for i in range(4):
+            step_stats(i)
+    torch.cuda.synchronize()
+    per = {}
+    for name, kms in marks.times():
+        tot, cnt = per.get(name, (0.0, 0))
+        per[name] = (tot + kms, cnt + 1)
+    kernels = {}
+    for name, (tot, cnt) in per.items():
+        avg = tot / cnt
+        by = kb.get(name, 0)
+        kernels[name] = {"avg_ms": round(avg, 4), "GBps": round(by / (avg * 1e-3) / 1e9, 1) if by else None}
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1), "kernels": kernels,
+            "note": "kvs_score_merge_stats + kvs_decode_attn per step (GPU events); the window statistics "
+                    "are an input here (a prefill attention computes them), so the first scorer pass and its "
+                    "combine are not run; not the headline value"}
 
 
 if __name__ == "__main__":

@@ -7,6 +7,8 @@
  *   kvs_score          window attention statistics (lse, o) and the forward-only
  *                      Hessian-norm sums g_self / g_cross, plus adjacent-key cosine
  *   kvs_score_merge    kvs_score + kvs_merge_weights + kvs_merge_compact in one call
+ *   kvs_score_merge_stats  the same round given the window statistics (lse, O) from the
+ *                      prefill attention that already computed them: no first scorer pass
  *   kvs_merge_weights  pair selection (top-M adjacent pairs by cosine) and the
  *                      closed-form key-merge weights
  *   kvs_merge_compact  key merge, lossless value-slot merge, stream compaction
@@ -90,7 +92,8 @@ typedef enum {
   KVS_OP_SELECT = 1,     /* workspace of kvs_merge_weights */
   KVS_OP_SEL_STATE = 2,  /* size of the selection-state buffer (kvs_merge_weights -> kvs_merge_compact) */
   KVS_OP_DECODE = 3,     /* workspace of kvs_decode_attn */
-  KVS_OP_SCORE_MERGE = 4 /* workspace of kvs_score_merge (equals KVS_OP_SCORE when n_merge is 0 or P) */
+  KVS_OP_SCORE_MERGE = 4, /* workspace of kvs_score_merge (equals KVS_OP_SCORE when n_merge is 0 or P) */
+  KVS_OP_STATS_MERGE = 5  /* workspace of kvs_score_merge_stats */
 } kvs_op;
 
 /* Number of candidate pairs P = floor((N - S - R) / 2) (0 if negative).  Pair p is the
@@ -148,6 +151,27 @@ kvs_status kvs_score_merge(const kvs_cache* cache, kvs_dtype dtype,
                            const kvs_cache* out, kvs_dtype out_dtype,
                            void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_score_merge_stats — kvs_score_merge for a caller that already holds the window
+ * statistics: lse [B, H_q, W] (natural log) and O [B, H_q, W, D] (fp32), the attention of
+ * the window queries Qw over the cache's N slots with the + ln n slot bias (deep-dive
+ * 数学主线三, as kvs_score defines them).  The prefill attention of the chunk that ends
+ * with the window computes exactly these (with the slot bias over a merged cache), so the
+ * round skips the scorer's first pass and reads the cache once for the statistics plus,
+ * for 0 < n_merge < P, the keys once for the cosine.  g_self, g_cross and the merged cache
+ * are as in kvs_score_merge; given the lse and O that kvs_score writes, every output equals
+ * kvs_score_merge's bit for bit.  lse and O are read only.  Workspace:
+ * kvs_workspace_bytes(KVS_OP_STATS_MERGE).  Errors as kvs_score_merge's; O must be 16-byte
+ * aligned.
+ */
+kvs_status kvs_score_merge_stats(const kvs_cache* cache, kvs_dtype dtype,
+                                 const void* K, const void* V, const int32_t* n, const void* Qw,
+                                 const kvs_round* round, const float* lse, const float* O,
+                                 float* g_self, float* g_cross,
+                                 const kvs_cache* out, kvs_dtype out_dtype,
+                                 void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kvs_merge_weights — pair selection and closed-form weights.

@@ -171,6 +171,16 @@ static size_t score_merge_bytes(const kvs::Shape& s, const kvs::RoundP& r) {
          (size_t)s.B * s.Hkv * kvs::sel_stride_ints(r.P) * sizeof(int32_t);
 }
 
+// kvs_score_merge_stats workspace: the pass-2 operand pack when the fused pass takes the
+// shape, then for a partial round the cosine and the selection state, 256-byte aligned.
+static size_t stats_merge_bytes(const kvs::Shape& s, const kvs::RoundP& r) {
+  size_t b = kvs::use_mfma_scorer(s) ? align256(kvs::stats_pack_bytes(s, r)) : 0;
+  if (partial_round(r))
+    b += align256((size_t)s.B * s.Hkv * r.P * sizeof(float)) +
+         (size_t)s.B * s.Hkv * kvs::sel_stride_ints(r.P) * sizeof(int32_t);
+  return b;
+}
+
 size_t kvs_workspace_bytes(kvs_op op, const kvs_cache* cache, const kvs_round* round) {
   kvs::Shape s;
   if (check_cache(cache, KVS_BF16, s) != KVS_OK) return 0;
@@ -189,6 +199,13 @@ size_t kvs_workspace_bytes(kvs_op op, const kvs_cache* cache, const kvs_round* r
       const size_t bf = score_merge_bytes(s, r);
       s.bf16 = false;
       const size_t f32 = score_merge_bytes(s, r);
+      return bf > f32 ? bf : f32;
+    }
+    case KVS_OP_STATS_MERGE: {
+      if (!round || check_round(round, s, r, true) != KVS_OK) return 0;
+      const size_t bf = stats_merge_bytes(s, r);
+      s.bf16 = false;
+      const size_t f32 = stats_merge_bytes(s, r);
       return bf > f32 ? bf : f32;
     }
     case KVS_OP_SELECT:
@@ -266,6 +283,67 @@ kvs_status kvs_score_merge(const kvs_cache* cache, kvs_dtype dtype, const void* 
   if (e == hipSuccess && part) e = kvs::launch_select(s, r, g_self, g_cross, cos, nullptr, nullptr, sel, hs);
   if (e == hipSuccess) e = kvs::launch_merge(s, r, K, V, n, g_self, g_cross, sel, op, K_out, V_out, n_out, src_out, hs);
   return hip_status(e, "kvs_score_merge");
+}
+
+kvs_status kvs_score_merge_stats(const kvs_cache* cache, kvs_dtype dtype, const void* K, const void* V,
+                                 const int32_t* n, const void* Qw, const kvs_round* round, const float* lse,
+                                 const float* O, float* g_self, float* g_cross, const kvs_cache* out,
+                                 kvs_dtype out_dtype, void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  kvs::Shape s, so;
+  kvs::RoundP r;
+  kvs_status st = check_cache(cache, dtype, s);
+  if (st) return st;
+  if ((st = check_round(round, s, r, true))) return st;
+  if (s.N < 1) return fail(KVS_ERR_SHAPE, "kvs_score_merge_stats needs n_slots >= 1");
+  if (!K || !V || !Qw || !lse || !O || !g_self || (r.P > 0 && !g_cross))
+    return fail(KVS_ERR_NULL, "kvs_score_merge_stats: K, V, Qw, lse, O, g_self and g_cross are required");
+  if (!out) return fail(KVS_ERR_NULL, "kvs_score_merge_stats: out layout is NULL");
+  if ((st = check_cache(out, out_dtype, so))) return st;
+  if (so.B != s.B || so.Hkv != s.Hkv || so.D != s.D)
+    return fail(KVS_ERR_SHAPE, "out layout must match batch, n_kv_heads and head_dim of the input");
+  if (so.N != s.N - r.M)
+    return fail(KVS_ERR_SHAPE, "out n_slots %lld != N - M = %lld", (long long)so.N, (long long)(s.N - r.M));
+  if (!K_out || !V_out || !n_out || !src_out)
+    return fail(KVS_ERR_NULL, "kvs_score_merge_stats: K_out, V_out, n_out, src_out are required");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(Qw) || !aligned16(K_out) || !aligned16(V_out) ||
+      !aligned16(O))
+    return fail(KVS_ERR_ALIGN, "K, V, Qw, O, K_out, V_out must be 16-byte aligned");
+  const size_t need = stats_merge_bytes(s, r);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(KVS_ERR_WORKSPACE, "kvs_score_merge_stats needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  kvs::OutP op{so.sb, so.sh, so.bf16};
+  const bool mfma = kvs::use_mfma_scorer(s);
+  // workspace: [operand pack] | cosine | selection state (the last two for partial rounds)
+  uint8_t* wb = static_cast<uint8_t*>(workspace);
+  const bool part = partial_round(r);
+  float* cos = part ? reinterpret_cast<float*>(wb + (mfma ? align256(kvs::stats_pack_bytes(s, r)) : 0)) : nullptr;
+  int32_t* sel = part ? reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(cos) +
+                                                    align256((size_t)s.B * s.Hkv * r.P * sizeof(float)))
+                      : nullptr;
+  if (mfma)
+    return hip_status(kvs::launch_stats_merge_mfma(s, r, K, V, n, Qw, lse, O, g_self, g_cross, workspace, cos, sel,
+                                                   op, K_out, V_out, n_out, src_out, hs),
+                      "kvs_score_merge_stats");
+  // fp32 caches: the cosine and the selection, the VALU pass 2, the merge pass
+  hipError_t e = hipSuccess;
+  if (part) {
+    kvs::CosArgs ca;
+    ca.K = K;
+    ca.cos = cos;
+    ca.S = r.S;
+    ca.P = r.P;
+    ca.sb = s.sb;
+    ca.sh = s.sh;
+    ca.Hkv = s.Hkv;
+    e = kvs::launch_pair_cos(s, ca, r.P, hs);
+    if (e == hipSuccess) e = kvs::launch_select(s, r, g_self, g_cross, cos, nullptr, nullptr, sel, hs);
+  }
+  if (e == hipSuccess) e = kvs::launch_pass2_valu(s, r, K, V, n, Qw, lse, O, g_self, g_cross, hs);
+  if (e == hipSuccess) e = kvs::launch_merge(s, r, K, V, n, g_self, g_cross, sel, op, K_out, V_out, n_out, src_out, hs);
+  return hip_status(e, "kvs_score_merge_stats");
 }
 
 kvs_status kvs_append(const kvs_cache* cache, kvs_dtype dtype, void* K, void* V, int32_t* n, int64_t at,

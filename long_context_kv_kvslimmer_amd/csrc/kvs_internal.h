@@ -88,6 +88,9 @@ __host__ __device__ inline int64_t pack_ops_index(int64_t bh, int64_t nwb, int64
 // units: rows of `out` ([units, D]); lse (natural log) is nullable; pack nullable.
 hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, float* lse, float* out,
                           hipStream_t st, const PackP* pack = nullptr);
+// The same operand pack from window statistics the caller supplies (lse natural log
+// [units], O [units, D]).
+hipError_t launch_pack(const float* lse, const float* O, int64_t units, int D, const PackP& pk, hipStream_t st);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 

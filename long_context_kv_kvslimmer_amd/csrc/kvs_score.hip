@@ -237,6 +237,50 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   }
 }
 
+// The MFMA pass-2 operands of row u (as combine_kernel writes them): lane c < D / 8 of the
+// calling wave packs elements 8c .. 8c + 7 of the row, fetched from the lanes that hold
+// them (lane l holds elements l + 64 e in ov[e]); lane 0 writes ||o||^2 and -lse log2 e.
+// All 64 lanes call it.
+template <int D>
+__device__ __forceinline__ void pack_row_wave(const PackP& pk, int64_t u, const float (&ov)[D / 64], float lse_u,
+                                              int lane) {
+  constexpr int nch = D / 8, KS = D / 32;
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int d = (lane * 8 + j) & (D - 1);
+    float v = __shfl(ov[0], d & 63, 64);
+    if constexpr (D == 128) {
+      const float v1 = __shfl(ov[1], d & 63, 64);
+      v = d >= 64 ? v1 : v;
+    }
+    x[j] = v;
+  }
+  const int64_t bh = u / pk.GW, q = u - bh * pk.GW;
+  float on = 0.f;
+  if (lane < nch) {
+    const int64_t b = bh / pk.Hkv, hk = bh - b * pk.Hkv;
+    const bf16* qrow = static_cast<const bf16*>(pk.Qw) + ((b * pk.Hq + hk * pk.G) * (int64_t)pk.W + q) * D;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x0 = x[2 * j], x1 = x[2 * j + 1];
+      on = __builtin_fmaf(x0, x0, __builtin_fmaf(x1, x1, on));
+      const float m0 = -2.f * x0, m1 = -2.f * x1;
+      hi[j] = pack_bf16x2(m0, m1);
+      lo[j] = pack_bf16x2(m0 - bf16_lo(hi[j]), m1 - bf16_hi(hi[j]));
+    }
+    pk.ops[pack_ops_index(bh, pk.nwb, q, 0, lane, KS)] = *reinterpret_cast<const uint4*>(qrow + lane * 8);
+    pk.ops[pack_ops_index(bh, pk.nwb, q, 1, lane, KS)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    pk.ops[pack_ops_index(bh, pk.nwb, q, 2, lane, KS)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+  on = group_sum<16>(on);   // lanes past nch contributed zeros
+  if (lane == 0) {
+    pk.qc[(bh * pk.nwb * 32 + q) * 2] = on;
+    pk.qc[(bh * pk.nwb * 32 + q) * 2 + 1] = -lse_u * kLog2e;
+  }
+}
+
 // Few splits and many units (many heads, short caches): one wave per unit, four units per
 // workgroup, no barriers.  Lane l reads the maximum and sum of split l; the wave reduces
 // them; lane l then owns output elements l (and l + 64 at D = 128) and sums the splits in
@@ -291,45 +335,35 @@ __global__ __launch_bounds__(64 * kCombineWaveUnits) void combine_wave_kernel(co
   }
   const float lse_u = (M + __log2f(L)) * kLn2;
   if (lse && lane == 0) lse[u] = lse_u;
-  if (pk.ops) {
-    // operands of the MFMA pass 2 (as in combine_kernel): lane c < D / 8 packs elements
-    // 8c .. 8c + 7, fetched from the lanes that own them
-    constexpr int nch = D / 8, KS = D / 32;
-    float x[8];
+  if (pk.ops) pack_row_wave<D>(pk, u, ov, lse_u, lane);
+}
+
+// One wave per row: the MFMA pass-2 operands of window statistics the caller supplies
+// (lse natural log [units], O [units, D]), packed exactly as the combine packs them.
+template <int D>
+__global__ __launch_bounds__(64 * kCombineWaveUnits) void pack_kernel(const float* __restrict__ lse,
+                                                                     const float* __restrict__ O, int64_t units,
+                                                                     PackP pk) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t u = (int64_t)blockIdx.x * kCombineWaveUnits + (threadIdx.x >> 6);
+  if (u >= units) return;
+  float ov[E];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = (lane * 8 + j) & (D - 1);
-      float v = __shfl(ov[0], d & 63, 64);
-      if constexpr (E == 2) {
-        const float v1 = __shfl(ov[1], d & 63, 64);
-        v = d >= 64 ? v1 : v;
-      }
-      x[j] = v;
-    }
-    const int64_t bh = u / pk.GW, q = u - bh * pk.GW;
-    float on = 0.f;
-    if (lane < nch) {
-      const int64_t b = bh / pk.Hkv, hk = bh - b * pk.Hkv;
-      const bf16* qrow = static_cast<const bf16*>(pk.Qw) + ((b * pk.Hq + hk * pk.G) * (int64_t)pk.W + q) * D;
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = x[2 * j], x1 = x[2 * j + 1];
-        on = __builtin_fmaf(x0, x0, __builtin_fmaf(x1, x1, on));
-        const float m0 = -2.f * x0, m1 = -2.f * x1;
-        hi[j] = pack_bf16x2(m0, m1);
-        lo[j] = pack_bf16x2(m0 - bf16_lo(hi[j]), m1 - bf16_hi(hi[j]));
-      }
-      pk.ops[pack_ops_index(bh, pk.nwb, q, 0, lane, KS)] = *reinterpret_cast<const uint4*>(qrow + lane * 8);
-      pk.ops[pack_ops_index(bh, pk.nwb, q, 1, lane, KS)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      pk.ops[pack_ops_index(bh, pk.nwb, q, 2, lane, KS)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    }
-    on = group_sum<16>(on);   // lanes past nch contributed zeros
-    if (lane == 0) {
-      pk.qc[(bh * pk.nwb * 32 + q) * 2] = on;
-      pk.qc[(bh * pk.nwb * 32 + q) * 2 + 1] = -lse_u * kLog2e;
-    }
-  }
+  for (int e = 0; e < E; ++e) ov[e] = O[u * D + lane + 64 * e];
+  pack_row_wave<D>(pk, u, ov, lse[u], lane);
+}
+
+hipError_t launch_pack(const float* lse, const float* O, int64_t units, int D, const PackP& pk, hipStream_t st) {
+  if (units == 0) return hipSuccess;
+  const dim3 grid((unsigned)((units + kCombineWaveUnits - 1) / kCombineWaveUnits));
+  if (D == 128)
+    KVS_LAUNCH("pack", pack_kernel<128>, grid, dim3(64 * kCombineWaveUnits), 0, st, lse, O, units, pk);
+  else if (D == 64)
+    KVS_LAUNCH("pack", pack_kernel<64>, grid, dim3(64 * kCombineWaveUnits), 0, st, lse, O, units, pk);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -483,6 +517,25 @@ __global__ __launch_bounds__(256) void pair_cos_kernel(CosArgs a) {
 }
 
 // ------------------------------------------------------------------- launchers --
+hipError_t launch_pair_cos(const Shape& s, const CosArgs& ca, int64_t P, hipStream_t st) {
+  if (P <= 0) return hipSuccess;
+  const int64_t BH = (int64_t)s.B * s.Hkv;
+  if (s.bf16) {
+    constexpr int GPB128 = 256 / (128 / Elt<bf16>::kPerChunk), GPB64 = 256 / (64 / Elt<bf16>::kPerChunk);
+    if (s.D == 128)
+      KVS_LAUNCH("pair_cos", (pair_cos_kernel<bf16, 128>), dim3((P + GPB128 - 1) / GPB128, BH), dim3(256), 0, st, ca);
+    else
+      KVS_LAUNCH("pair_cos", (pair_cos_kernel<bf16, 64>), dim3((P + GPB64 - 1) / GPB64, BH), dim3(256), 0, st, ca);
+  } else {
+    constexpr int GPB128 = 256 / (128 / Elt<float>::kPerChunk), GPB64 = 256 / (64 / Elt<float>::kPerChunk);
+    if (s.D == 128)
+      KVS_LAUNCH("pair_cos", (pair_cos_kernel<float, 128>), dim3((P + GPB128 - 1) / GPB128, BH), dim3(256), 0, st, ca);
+    else
+      KVS_LAUNCH("pair_cos", (pair_cos_kernel<float, 64>), dim3((P + GPB64 - 1) / GPB64, BH), dim3(256), 0, st, ca);
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_score_valu(const Shape& s, const RoundP& r, const P1Args& p1, const P2Args& p2,
                                     const CosArgs& ca, float* lse, float* O, hipStream_t st) {
@@ -507,8 +560,47 @@ size_t score_workspace_bytes(const Shape& s, const RoundP& r) {
   const int64_t GW = (int64_t)s.G * r.W;
   int64_t chunk;
   int nsplit;
-  valu_pass1_plan(s.N, chunk, nsplit);
+  valu_pass1_plan(s.N, (int64_t)s.B * s.Hkv * ((GW + 127) / 128), chunk, nsplit);
   return (size_t)s.B * s.Hkv * GW * nsplit * (s.D + 4) * sizeof(float);
+}
+
+// Pass 2 alone on the VALU kernels, from window statistics the caller supplies.
+hipError_t launch_pass2_valu(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                             const void* Qw, const float* lse, const float* O, float* g_self, float* g_cross,
+                             hipStream_t st) {
+  P2Args p2{};
+  p2.K = K;
+  p2.V = V;
+  p2.n = n;
+  p2.Qw = Qw;
+  p2.lse = lse;
+  p2.O = O;
+  p2.g_self = g_self;
+  p2.g_cross = g_cross;
+  p2.N = s.N;
+  p2.S = r.S;
+  p2.P = r.P;
+  p2.sb = s.sb;
+  p2.sh = s.sh;
+  p2.Hkv = s.Hkv;
+  p2.Hq = s.Hq;
+  p2.G = s.G;
+  p2.W = r.W;
+  p2.GW = (int64_t)s.G * r.W;
+  p2.scale = r.scale;
+  const int64_t BH = (int64_t)s.B * s.Hkv;
+  const int64_t units = r.S + r.P + (s.N - r.S - 2 * r.P);
+  const dim3 grid((unsigned)((units + 63) / 64), (unsigned)BH);
+#define KVS_P2V(T, D)                                                                        \
+  if (p2.n) KVS_LAUNCH("score_pass2", (pass2_valu_kernel<T, D, true>), grid, dim3(256), 0, st, p2); \
+  else KVS_LAUNCH("score_pass2", (pass2_valu_kernel<T, D, false>), grid, dim3(256), 0, st, p2);
+  if (s.bf16) {
+    if (s.D == 64) { KVS_P2V(bf16, 64) } else { KVS_P2V(bf16, 128) }
+  } else {
+    if (s.D == 64) { KVS_P2V(float, 64) } else { KVS_P2V(float, 128) }
+  }
+#undef KVS_P2V
+  return hipGetLastError();
 }
 
 hipError_t launch_score(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
@@ -530,7 +622,7 @@ hipError_t launch_score(const Shape& s, const RoundP& r, const void* K, const vo
   p1.W = r.W;
   p1.GW = (int64_t)s.G * r.W;
   p1.scale = r.scale;
-  valu_pass1_plan(s.N, p1.chunk, p1.nsplit);
+  valu_pass1_plan(s.N, (int64_t)s.B * s.Hkv * ((p1.GW + 127) / 128), p1.chunk, p1.nsplit);
   P2Args p2;
   p2.K = K;
   p2.V = V;

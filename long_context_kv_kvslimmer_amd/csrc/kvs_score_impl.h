@@ -51,10 +51,13 @@ struct CosArgs {
   int Hkv;
 };
 
-// Slot splits of the VALU pass 1: at least 64 slots per workgroup, at most 256 splits,
-// every split non-empty.
-inline void valu_pass1_plan(int64_t N, int64_t& chunk, int& nsplit) {
+// Slot splits of the VALU pass 1 over `units` (kv head, query block) pairs: about 1024
+// workgroups in all, at least 64 slots per workgroup, at most 256 splits, every split
+// non-empty (many heads need few splits, which keeps the partial records small).
+inline void valu_pass1_plan(int64_t N, int64_t units, int64_t& chunk, int& nsplit) {
   int64_t k = (N + 63) / 64;
+  const int64_t want = (1024 + units - 1) / (units > 0 ? units : 1);
+  if (k > want) k = want;
   if (k < 1) k = 1;
   if (k > 256) k = 256;
   chunk = (N + k - 1) / k;
@@ -63,6 +66,21 @@ inline void valu_pass1_plan(int64_t N, int64_t& chunk, int& nsplit) {
   if (nsplit < 1) nsplit = 1;
 }
 
+// Pass 2 alone on the VALU kernels from caller-supplied window statistics.
+hipError_t launch_pass2_valu(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                             const void* Qw, const float* lse, const float* O, float* g_self, float* g_cross,
+                             hipStream_t st);
+// Adjacent-key cosine of every candidate pair on its own (the routine pass 1 uses).
+hipError_t launch_pair_cos(const Shape& s, const CosArgs& ca, int64_t P, hipStream_t st);
+// A whole round given the window statistics (lse, O) instead of pass 1: operand pack,
+// [cosine and selection for 0 < M < P], pass 2 with the merge and compaction folded in
+// (fused_round_ok), or pass 2 then the merge pass (more than 128 window queries per kv
+// head).  Requires use_mfma_scorer.
+hipError_t launch_stats_merge_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                                   const void* Qw, const float* lse, const float* O, float* g_self, float* g_cross,
+                                   void* ws, float* cos, int32_t* sel_state, const OutP& o, void* K_out, void* V_out,
+                                   int32_t* n_out, int32_t* src_out, hipStream_t st);
+size_t stats_pack_bytes(const Shape& s, const RoundP& r);
 bool use_mfma_scorer(const Shape& s);
 size_t mfma_score_workspace_bytes(const Shape& s, const RoundP& r);
 // Whole round fused: pass 1, combine, (for 0 < n_merge < P: the selection over the pass-1

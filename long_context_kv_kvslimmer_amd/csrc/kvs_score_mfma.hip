@@ -885,6 +885,10 @@ size_t mfma_score_workspace_bytes(const Shape& s, const RoundP& r) {
 
 // merge: 0 = plain pass 2; 1 = fused merge with bf16 output; 2 = fused merge with fp32 output
 template <int D>
+static hipError_t launch_p2_d(const Shape& s, const RoundP& r, const P2Args& p2, int64_t base, int merge,
+                              hipStream_t st);
+
+template <int D>
 static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p1, const P2Args& p2,
                                 const CosArgs& ca, int64_t base, float* lse, float* O, int merge, hipStream_t st) {
   const int64_t BH = (int64_t)s.B * s.Hkv;
@@ -908,6 +912,17 @@ static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p
   pk.W = r.W;
   e = launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st, &pk);
   if (e != hipSuccess) return e;
+  return launch_p2_d<D>(s, r, p2, base, merge, st);
+}
+
+// Pass 2 once the operand pack exists: zero the sums when several query blocks accumulate
+// into them, choose the pairs of a partial fused round, then the pass itself.
+template <int D>
+static hipError_t launch_p2_d(const Shape& s, const RoundP& r, const P2Args& p2, int64_t base, int merge,
+                              hipStream_t st) {
+  const int64_t BH = (int64_t)s.B * s.Hkv;
+  const int nqb = (int)((p2.GW + kQB - 1) / kQB);
+  hipError_t e = hipSuccess;
   if (nqb > 1) {
     if (merge) return hipErrorInvalidValue;   // the fused merge needs every query in one workgroup
     // several query blocks accumulate into the same sums
@@ -1041,6 +1056,93 @@ hipError_t launch_score_merge_mfma(const Shape& s, const RoundP& r, const void* 
   const bool part = r.M > 0 && r.M < r.P;
   return launch_score_any(s, r, K, V, n, Qw, lse, O, g_self, g_cross, part ? cos : nullptr, ws, &o,
                           part ? sel_state : nullptr, K_out, V_out, n_out, src_out, st);
+}
+
+}  // namespace kvs
+
+namespace kvs {
+
+// Workspace of a round given the window statistics: the pass-2 operand pack and the
+// per-query constants (the cosine and the selection state follow, in the API layer).
+size_t stats_pack_bytes(const Shape& s, const RoundP& r) {
+  return pack_ops_bytes(s, r) + (size_t)s.B * s.Hkv * pack_blocks(s, r) * 32 * 2 * sizeof(float);
+}
+
+hipError_t launch_stats_merge_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                                   const void* Qw, const float* lse, const float* O, float* g_self, float* g_cross,
+                                   void* ws, float* cos, int32_t* sel_state, const OutP& o, void* K_out, void* V_out,
+                                   int32_t* n_out, int32_t* src_out, hipStream_t st) {
+  const bool part = r.M > 0 && r.M < r.P;
+  P2Args p2{};
+  p2.nwb = pack_blocks(s, r);
+  p2.ops = static_cast<const uint4*>(ws);
+  p2.qc = reinterpret_cast<const float*>(static_cast<uint8_t*>(ws) + pack_ops_bytes(s, r));
+  p2.K = K;
+  p2.V = V;
+  p2.n = n;
+  p2.Qw = Qw;
+  p2.lse = lse;
+  p2.O = O;
+  p2.g_self = g_self;
+  p2.g_cross = g_cross;
+  p2.N = s.N;
+  p2.S = r.S;
+  p2.P = r.P;
+  p2.sb = s.sb;
+  p2.sh = s.sh;
+  p2.Hkv = s.Hkv;
+  p2.Hq = s.Hq;
+  p2.G = s.G;
+  p2.W = r.W;
+  p2.GW = (int64_t)s.G * r.W;
+  p2.scale = r.scale;
+  p2.M = r.M;
+  p2.Ko = K_out;
+  p2.Vo = V_out;
+  p2.no = n_out;
+  p2.so = src_out;
+  p2.osb = o.sb;
+  p2.osh = o.sh;
+  p2.cos = part ? cos : nullptr;
+  p2.sel = part ? sel_state : nullptr;
+  p2.sel_stride = sel_stride_ints(r.P);
+  PackP pk;
+  pk.ops = const_cast<uint4*>(p2.ops);
+  pk.qc = const_cast<float*>(p2.qc);
+  pk.Qw = Qw;
+  pk.nwb = p2.nwb;
+  pk.GW = p2.GW;
+  pk.Hkv = s.Hkv;
+  pk.Hq = s.Hq;
+  pk.G = s.G;
+  pk.W = r.W;
+  hipError_t e = launch_pack(lse, O, (int64_t)s.B * s.Hkv * p2.GW, s.D, pk, st);
+  if (e != hipSuccess) return e;
+  if (part) {
+    CosArgs ca;
+    ca.K = K;
+    ca.cos = cos;
+    ca.S = r.S;
+    ca.P = r.P;
+    ca.sb = s.sb;
+    ca.sh = s.sh;
+    ca.Hkv = s.Hkv;
+    e = launch_pair_cos(s, ca, r.P, st);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t base = -(r.S & 1);
+  if (fused_round_ok(s, r)) {
+    const int merge = o.bf16 ? 1 : 2;
+    return s.D == 64 ? launch_p2_d<64>(s, r, p2, base, merge, st) : launch_p2_d<128>(s, r, p2, base, merge, st);
+  }
+  // more than 128 window queries per kv head: pass 2 alone (query blocks accumulate), the
+  // selection, then the merge pass
+  e = s.D == 64 ? launch_p2_d<64>(s, r, p2, base, 0, st) : launch_p2_d<128>(s, r, p2, base, 0, st);
+  if (e == hipSuccess && part)
+    e = launch_select(s, r, g_self, g_cross, cos, nullptr, nullptr, sel_state, st);
+  if (e == hipSuccess)
+    e = launch_merge(s, r, K, V, n, g_self, g_cross, part ? sel_state : nullptr, o, K_out, V_out, n_out, src_out, st);
+  return e;
 }
 
 }  // namespace kvs

@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(_PKG, "libkvslim.so")
 KVS_OK, KVS_ERR_NULL, KVS_ERR_SHAPE, KVS_ERR_DTYPE, KVS_ERR_STRIDE, KVS_ERR_ALIGN, \
     KVS_ERR_INFEASIBLE, KVS_ERR_WORKSPACE, KVS_ERR_HIP = range(9)
 KVS_BF16, KVS_F32 = 0, 1
-KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE, KVS_OP_SCORE_MERGE = range(5)
+KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE, KVS_OP_SCORE_MERGE, KVS_OP_STATS_MERGE = range(6)
 
 EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_score_merge", "kvs_merge_weights", "kvs_merge_compact",
-           "kvs_append",
+           "kvs_append", "kvs_score_merge_stats",
            "kvs_decode_attn", "kvs_marks_begin", "kvs_marks_end", "kvs_mark_name", "kvs_mark_ms", "kvs_status_str",
            "kvs_last_error", "kvs_version")
 
@@ -59,6 +59,8 @@ def _load():
         "kvs_merge_compact": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, P, R, P, C, ctypes.c_int, P, P, P, P, P]),
         "kvs_decode_attn": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, F, P, P, SZ, P]),
         "kvs_append": (ctypes.c_int, [C, ctypes.c_int, P, P, P, I64, C, P, P, I64, I64, P]),
+        "kvs_score_merge_stats": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, R, P, P, P, P, C, ctypes.c_int, P, P,
+                                                  P, P, P, SZ, P]),
         "kvs_marks_begin": (ctypes.c_int, [I32, ctypes.c_char_p]),
         "kvs_marks_end": (I32, []),
         "kvs_mark_name": (ctypes.c_char_p, [I32]),
@@ -184,6 +186,18 @@ def kvs_score_merge(cache: KvsCache, K, V, n, Qw, rnd: KvsRound, lse, O, g_self,
                                 ctypes.byref(rnd), _ptr(lse), _ptr(O), _ptr(g_self), _ptr(g_cross),
                                 ctypes.byref(out), dtype_code(K_out), _ptr(K_out), _ptr(V_out), _ptr(n_out),
                                 _ptr(src_out), _ptr(workspace), ws_bytes, _stream()))
+
+
+def kvs_score_merge_stats(cache: KvsCache, K, V, n, Qw, rnd: KvsRound, lse, O, g_self, g_cross,
+                          out: KvsCache, K_out, V_out, n_out, src_out, workspace):
+    _same_layout(K, V)
+    if K_out.dtype != V_out.dtype:
+        raise ValueError("K_out and V_out must share a dtype")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.kvs_score_merge_stats(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(Qw),
+                                      ctypes.byref(rnd), _ptr(lse), _ptr(O), _ptr(g_self), _ptr(g_cross),
+                                      ctypes.byref(out), dtype_code(K_out), _ptr(K_out), _ptr(V_out), _ptr(n_out),
+                                      _ptr(src_out), _ptr(workspace), ws_bytes, _stream()))
 
 
 def kvs_merge_weights(cache: KvsCache, rnd: KvsRound, g_self, g_cross, cos, w, selected, sel_state):

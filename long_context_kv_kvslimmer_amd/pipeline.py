@@ -38,7 +38,7 @@ def alloc_round(K: torch.Tensor, n_q_heads: int, window: int, n_sink: int, n_rec
     f32 = torch.float32
     cache = L.cache_desc(K, n_q_heads, N)
     rnd = L.round_desc(window, n_sink, n_recent, n_merge, 1.0 / math.sqrt(D))
-    ws = max(L.workspace_bytes(L.KVS_OP_SCORE, cache, rnd), L.workspace_bytes(L.KVS_OP_SCORE_MERGE, cache, rnd))
+    ws = max(L.workspace_bytes(op, cache, rnd) for op in (L.KVS_OP_SCORE, L.KVS_OP_SCORE_MERGE, L.KVS_OP_STATS_MERGE))
     ss = L.workspace_bytes(L.KVS_OP_SEL_STATE, cache, rnd)
     ocap = T if out_capacity is None else out_capacity
     odt = K.dtype if out_dtype is None else out_dtype
@@ -88,6 +88,20 @@ def run_round_fused(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_rec
     out = L.cache_desc(bufs.K, n_q_heads, N - n_merge)
     L.kvs_score_merge(cache, K, V, n, Qw, rnd, bufs.lse, bufs.O, bufs.g_self, bufs.g_cross, out,
                       bufs.K, bufs.V, bufs.n, bufs.src, bufs.score_ws)
+    return bufs
+
+
+def run_round_given_stats(K, V, n, Qw, lse, O, n_q_heads: int, window: int, n_sink: int, n_recent: int,
+                          n_merge: int, bufs: RoundBuffers, n_slots: int | None = None):
+    """A whole round through kvs_score_merge_stats: the window statistics lse [B, H_q, W] and
+    O [B, H_q, W, D] come from the caller (the prefill attention); bufs.lse / bufs.O unused."""
+    B, H, cap, D = K.shape
+    N = cap if n_slots is None else n_slots
+    cache = L.cache_desc(K, n_q_heads, N)
+    rnd = L.round_desc(window, n_sink, n_recent, n_merge, 1.0 / math.sqrt(D))
+    out = L.cache_desc(bufs.K, n_q_heads, N - n_merge)
+    L.kvs_score_merge_stats(cache, K, V, n, Qw, rnd, lse, O, bufs.g_self, bufs.g_cross, out,
+                            bufs.K, bufs.V, bufs.n, bufs.src, bufs.score_ws)
     return bufs
 
 
