@@ -408,6 +408,82 @@ def compose_src(prev_src: np.ndarray, src: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# 数学主线三/四: exact-gradient scalars against the forward-only substitution
+# ---------------------------------------------------------------------------
+def exact_weights(g11: float, g12: float, g22: float):
+    """``hessian_weights`` with the degenerate case handled (reading O22, pages
+    silent): when g11 + 2 g12 + g22 is not finite or its magnitude is at most
+    1e-6 (|g11| + 2|g12| + |g22|), the plain average (½, ½).  An indefinite
+    model keeps its stationary point (no clamping).  Returns (w_m, w_{m+1})."""
+    den = g11 + 2.0 * g12 + g22
+    scale = abs(g11) + 2.0 * abs(g12) + abs(g22)
+    if not math.isfinite(den) or abs(den) <= DEGENERATE_REL * scale:
+        return 0.5, 0.5
+    return hessian_weights(g11, g12, g22)
+
+
+def pair_loss(w0: float, w1: float, k_m, k_m1, g11: float, g12: float, g22: float) -> float:
+    """``merge_objective`` at k = w0 k_m + w1 k_{m+1}."""
+    k = w0 * np.asarray(k_m, F64) + w1 * np.asarray(k_m1, F64)
+    return merge_objective(k, k_m, k_m1, g11, g12, g22)
+
+
+def exact_e_diagnostics(K, V, n, Qw, E, lse, O, scale, n_sink, n_recent) -> dict:
+    """Given an upstream gradient E_w = ∂L/∂o_w per window query, the exact
+    scalars g_ij = E_wᵀ c_ij^{(w)} of [DD] 数学主线三 (the Hessian blocks are
+    g_ij q qᵀ / d_k), summed over the window as the norms are (reading O2);
+    their exact-weight k* (``exact_weights``, the stationary point of
+    数学主线二); the forward-only k* of 数学主线四 from the norms; and the
+    quantities that compare the two: Σ_w ‖E_w‖‖c^{(w)}‖ (so that g / that sum is
+    a norm-weighted cos(E, c), whose pattern cos11 ≈ cos22 ≈ −cos12 is what the
+    forward-only weights assume) and the exact second-order loss of each k*.
+
+    Window statistics lse [GW], O [GW, D] as in ``merge_round_given_stats``.
+    Per slot i (any slot: c_ii = α_i (1 − 2α_i)(v_i − o_w)): g_self_e, n_self_e,
+    g_self (the forward-only norm sum).  Per candidate pair p: g_cross_e, n_cross_e,
+    g_cross, w_exact [P, 2], w_fwd [P, 2], loss_exact, loss_fwd."""
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    Qw = np.asarray(Qw, F64)
+    E = np.asarray(E, F64)
+    lse = np.asarray(lse, F64)
+    O = np.asarray(O, F64)
+    N, D = K.shape
+    nn = np.ones(N, dtype=np.int64) if n is None else np.asarray(n, dtype=np.int64)
+    P = num_pairs(N, n_sink, n_recent)
+    g_self_e, n_self_e, g_self = np.zeros(N), np.zeros(N), np.zeros(N)
+    g_cross_e, n_cross_e, g_cross = np.zeros(P), np.zeros(P), np.zeros(P)
+    for w in range(Qw.shape[0]):
+        e = scale * (K @ Qw[w]) + np.log(nn.astype(F64))
+        alpha = np.exp(e - lse[w])
+        en = math.sqrt(float(E[w] @ E[w]))
+        for i in range(N):
+            c = alpha[i] * (1.0 - 2.0 * alpha[i]) * (V[i] - O[w])
+            g_self_e[i] += float(E[w] @ c)
+            g_self[i] += math.sqrt(float(c @ c))
+            n_self_e[i] += en * math.sqrt(float(c @ c))
+        for p in range(P):
+            _, _, c12 = c_vectors(alpha, V, O[w], n_sink + 2 * p)
+            g_cross_e[p] += float(E[w] @ c12)
+            g_cross[p] += math.sqrt(float(c12 @ c12))
+            n_cross_e[p] += en * math.sqrt(float(c12 @ c12))
+    w_exact = np.empty((P, 2))
+    w_fwd = np.empty((P, 2))
+    loss_exact = np.empty(P)
+    loss_fwd = np.empty(P)
+    for p in range(P):
+        m = n_sink + 2 * p
+        g11, g12, g22 = g_self_e[m], g_cross_e[p], g_self_e[m + 1]
+        w_exact[p] = exact_weights(g11, g12, g22)
+        w_fwd[p] = forward_only_weights(g_self[m], g_cross[p], g_self[m + 1])[:2]
+        loss_exact[p] = pair_loss(w_exact[p, 0], w_exact[p, 1], K[m], K[m + 1], g11, g12, g22)
+        loss_fwd[p] = pair_loss(w_fwd[p, 0], w_fwd[p, 1], K[m], K[m + 1], g11, g12, g22)
+    return {"g_self_e": g_self_e, "n_self_e": n_self_e, "g_self": g_self, "g_cross_e": g_cross_e,
+            "n_cross_e": n_cross_e, "g_cross": g_cross, "w_exact": w_exact, "w_fwd": w_fwd,
+            "loss_exact": loss_exact, "loss_fwd": loss_fwd}
+
+
+# ---------------------------------------------------------------------------
 # 实验设置: chunked prefill under a fixed cache budget
 # ---------------------------------------------------------------------------
 @dataclass

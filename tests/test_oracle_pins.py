@@ -509,3 +509,59 @@ def test_given_stats_handworked():
     r = O.merge_round_given_stats(K, V, None, Q, [math.log(4.0)], [[10.0]], 0.5, 0, 0, 1)
     assert np.allclose(r.g_self, [9 / 8, 8 / 8, 7 / 8, 6 / 8], rtol=1e-15)
     assert np.allclose(r.g_cross, [17 / 16, 13 / 16], rtol=1e-15)
+
+
+# --------------------------------------------------- exact-gradient diagnostics --
+def test_exact_scalars_are_the_hessian_blocks():
+    """One window query: g_ij q qᵀ / d_k is the exact Hessian block (pinned by finite
+    differences above), for the diagonal blocks and the cross block of every pair."""
+    rng = _rng(50)
+    N, D = 8, 5
+    K, V = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    q, E = rng.standard_normal(D), rng.standard_normal(D)
+    s = 0.45
+    _, alpha, o = O.attention_forward(K, V, q, s)
+    lse = np.log(np.sum(np.exp(s * (K @ q))))
+    d = O.exact_e_diagnostics(K, V, None, q[None], E[None], [lse], o[None], s, 0, 0)
+    for p in range(N // 2):
+        m = 2 * p
+        for (i, j, g) in ((m, m, d["g_self_e"][m]), (m + 1, m + 1, d["g_self_e"][m + 1]), (m, m + 1, d["g_cross_e"][p])):
+            H = O.hessian_block(alpha, V, o, q, E, i, j, s)
+            assert np.allclose(g * s * s * np.outer(q, q), H, atol=1e-14, rtol=1e-12)
+
+
+def test_exact_weights_equal_forward_only_when_angles_agree():
+    """One dimension, one query, both values above the output and both attention weights
+    below 1/2: cos(E, c11) = cos(E, c22) = -cos(E, c12) = sign(E), the pattern the
+    forward-only weights assume, so the two closed forms give the same k*."""
+    K = np.array([[0.2], [0.5], [-0.3], [0.1], [0.4], [-0.2]])
+    V = np.array([[2.0], [3.0], [-1.0], [-2.0], [0.5], [0.4]])
+    q = np.array([0.7])
+    s = 1.0
+    _, alpha, o = O.attention_forward(K, V, q, s)
+    lse = np.log(np.sum(np.exp(s * (K @ q))))
+    assert np.all(alpha < 0.5) and V[0, 0] > o[0] and V[1, 0] > o[0]
+    for E in (1.7, -0.4):
+        d = O.exact_e_diagnostics(K, V, None, q[None], np.array([[E]]), [lse], o[None], s, 0, 0)
+        assert np.allclose(d["w_exact"][0], d["w_fwd"][0], atol=1e-12)
+        assert abs(d["g_self_e"][0] / d["n_self_e"][0] - np.sign(E)) < 1e-12
+        assert abs(d["g_cross_e"][0] / d["n_cross_e"][0] + np.sign(E)) < 1e-12
+        assert d["loss_fwd"][0] == pytest.approx(d["loss_exact"][0], abs=1e-12)
+
+
+def test_exact_diagnostics_invariants():
+    """Effective cosines lie in [-1, 1]; the forward-only norm sums equal the round's;
+    the exact k* is stationary for the exact model, so when it is convex it has the
+    smaller loss."""
+    K, V, n, Q = _random_slice(51, N=24, D=6, GW=4, counts=True)
+    E = _rng(52).standard_normal((4, 6))
+    ref = O.merge_round(K, V, n, Q, 0.4, 2, 2, 0)
+    d = O.exact_e_diagnostics(K, V, n, Q, E, ref.lse, ref.O, 0.4, 2, 2)
+    assert np.all(np.abs(d["g_self_e"]) <= d["n_self_e"] * (1 + 1e-12))
+    assert np.all(np.abs(d["g_cross_e"]) <= d["n_cross_e"] * (1 + 1e-12))
+    assert np.allclose(d["g_self"], ref.g_self, rtol=1e-12) and np.allclose(d["g_cross"], ref.g_cross, rtol=1e-12)
+    for p in range(len(d["loss_exact"])):
+        m = 2 + 2 * p
+        g11, g12, g22 = d["g_self_e"][m], d["g_cross_e"][p], d["g_self_e"][m + 1]
+        if g11 + 2 * g12 + g22 > 0 and g11 * g22 - g12 * g12 > 0:
+            assert d["loss_exact"][p] <= d["loss_fwd"][p] + 1e-12
