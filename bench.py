@@ -56,7 +56,7 @@ KERNEL_LABELS = (("p1_mfma_kernel", "score_pass1"), ("pass1_valu_kernel", "score
                  ("combine_wave_kernel", "combine"), ("select_fixed_kernel", "select"),
                  ("select_small_kernel", "select"), ("sel_clear_kernel", "select"), ("sel_hist_kernel", "select"),
                  ("sel_count_kernel", "select"), ("sel_final_kernel", "select"), ("append_kernel", "append"),
-                 ("pack_kernel", "pack"),
+                 ("pack_kernel", "pack"), ("exact_e_kernel", "exact_e"),
                  ("merge_compact_kernel", "merge_compact"), ("decode_mfma_kernel", "decode"),
                  ("decode_kernel", "decode"))
 COPY_BYTES = 1 << 30            # calibration copy: reads and writes this many bytes
@@ -533,6 +533,58 @@ def stream_timing(cfg, dev, reps=5, chunks=(256, 512, 1024, 2016)):
                     "launch overhead; kernel times from library event marks"}
 
 
+def diag_timing(dev, reps=5):
+    """The exact-gradient diagnostics on one C2 layer (32K slots, 8 KV heads, 128 window
+    queries per head) with an upstream gradient E ~ N(0, 1) per window query: kernel time,
+    and what it reports - the norm-weighted cosines cos(E, c11), cos(E, c22), cos(E, c12)
+    and how far the forward-only weights land from the exact-Hessian ones."""
+    import statistics
+    import torch
+    from long_context_kv_kvslimmer_amd import configs, pipeline, synth
+    from long_context_kv_kvslimmer_amd import kvslim as L
+    cfg = configs.C2
+    K, V, _ = synth.make_cache(cfg, 0, 0, dev)
+    K, V = K[None].contiguous(), V[None].contiguous()
+    Qw = synth.window_queries(cfg, 0, 0, 0, dev)[None].contiguous()
+    g = torch.Generator(device=dev)
+    g.manual_seed(17)
+    E = torch.randn(Qw.shape, generator=g, device=dev, dtype=torch.float32)
+    S, R, Hq, W = cfg.n_sink, cfg.n_recent, cfg.q_heads, cfg.window
+    bufs = pipeline.alloc_round(K, Hq, W, S, R, cfg.rounds[0], want_flags=False)
+    pipeline.run_round_fused(K, V, None, Qw, Hq, W, S, R, cfg.rounds[0], bufs)
+    lse, O = bufs.lse.clone(), bufs.O.clone()
+    pipeline.exact_e_diag(K, V, None, Qw, E, lse, O, Hq, W, S, R)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        marks = L.KernelMarks(max_launches=4)
+        with marks:
+            slot, pair = pipeline.exact_e_diag(K, V, None, Qw, E, lse, O, Hq, W, S, R)
+        torch.cuda.synchronize()
+        times.append(sum(ms for _, ms in marks.times()))
+    P = pair.shape[2]
+    m = S + 2 * torch.arange(P, device=dev)
+    so = slot[0]
+    c11 = (so[:, m, 0].sum() / so[:, m, 1].sum()).item()
+    c22 = (so[:, m + 1, 0].sum() / so[:, m + 1, 1].sum()).item()
+    c12 = (pair[0, :, :, 0].sum() / pair[0, :, :, 1].sum()).item()
+    dw = (pair[0, :, :, 3] - pair[0, :, :, 5]).abs()
+    ms = statistics.median(times)
+    # per window query and unit (pair or single slot), per head-dim element: 9 fma + 3 add
+    units = cfg.n_sink + P + (cfg.n_slots - cfg.n_sink - 2 * P)
+    flop = cfg.kv_heads * units * cfg.group * W * cfg.head_dim * 21
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"config": "exact-gradient diagnostics, C2 layer (32K slots x 8 KV heads, 128 window queries per head), "
+                      "E ~ N(0, 1)", "kernel_ms": round(ms, 4),
+            "roofline": {"bound": "alu", "achieved": round(tf, 1), "peak": 157.3, "unit": "TFLOP/s",
+                         "frac": round(tf / 157.3, 3), "flop_per_launch": flop},
+            "cos_E_c11": round(c11, 4), "cos_E_c22": round(c22, 4), "cos_E_c12": round(c12, 4),
+            "median_abs_w_exact_minus_w_fwd": round(dw.median().item(), 4),
+            "note": "a random E is no trained model's gradient: the angle relation the forward-only weights "
+                    "assume (cos11 = cos22 = -cos12) does not hold for it, so these figures show the diagnostic "
+                    "working, not KVSlimmer's accuracy"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -547,6 +599,8 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("SQ_CSV", "STATS_CSV", "CMD"))
     ap.add_argument("--summarize-per-config", nargs=2, metavar=("JSONL", "CMD"))
     ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "TITLE", "CMD"))
+    ap.add_argument("--diag", action="store_true",
+                    help="time the exact-gradient diagnostics on a C2 layer instead of the bench line")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="with --per-config 6: time only the 512-token-chunk loop (no chunk-size sweep)")
     ap.add_argument("--per-config", type=str, default=None, metavar="1,2,3,4,5,6",
@@ -579,6 +633,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.diag:
+        print(json.dumps(diag_timing(dev)), flush=True)
+        return
     if args.per_config:
         per_config(dev, [int(x) for x in args.per_config.split(",")],
                    chunk_sweep=() if args.no_chunk_sweep else (256, 512, 1024, 2016))

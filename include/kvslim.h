@@ -14,6 +14,7 @@
  *   kvs_merge_compact  key merge, lossless value-slot merge, stream compaction
  *   kvs_decode_attn    GQA decode attention over a (merged) cache
  *   kvs_append         write raw tokens (count 1) into a cache: a prefill chunk or a decode step
+ *   kvs_exact_e_diag   diagnostics: exact-gradient scalars and weights against the forward-only ones
  *
  * Sources.  The operations follow the KVSlimmer deep-dive "论文专题讲解：KVSlimmer：
  * 非对称 KV 合并的数学与工程" (charles2530.github.io), sections 数学主线二 (merging an adjacent
@@ -228,6 +229,31 @@ kvs_status kvs_merge_compact(const kvs_cache* cache, kvs_dtype in_dtype,
                              const kvs_cache* out, kvs_dtype out_dtype,
                              void* K_out, void* V_out, int32_t* n_out, int32_t* src_out,
                              void* stream);
+
+/*
+ * kvs_exact_e_diag — measures the one approximation of the forward-only weights.  Given
+ * an upstream gradient E [B, H_q, W, D] (fp32, dL/do of each window query) and the window
+ * statistics lse [B, H_q, W], O [B, H_q, W, D] (fp32, as kvs_score writes them), with
+ * alpha = exp(sm_scale q.k + ln n - lse) and, per window query w,
+ *   c_ii = alpha_i (1 - 2 alpha_i)(v_i - o_w),  c12 = -alpha_m alpha_{m+1}(v_m + v_{m+1} - 2 o_w)
+ * (deep-dive 数学主线四; the exact Hessian block of 数学主线三 is (E_w . c) q q^T / d_k):
+ *   slot_out[b, h, i, :] = ( sum_w E_w . c_ii,  sum_w |E_w| |c_ii|,  sum_w |c_ii| )      [B, H_kv, N, 3]
+ *   pair_out[b, h, p, :] = ( sum_w E_w . c12,   sum_w |E_w| |c12|,   sum_w |c12|,
+ *                            exact w_m, w_{m+1}  (stationary point of 数学主线二 in the exact
+ *                            scalars; (1/2, 1/2) when g11 + 2 g12 + g22 is not finite or at
+ *                            most 1e-6 (|g11| + 2|g12| + |g22|) in magnitude),
+ *                            forward-only w_m, w_{m+1}  (as kvs_merge_weights),
+ *                            loss at each k*: |k_m - k_{m+1}|^2 (g11 w_{m+1}^2 - 2 g12 w_m w_{m+1}
+ *                            + g22 w_m^2) in the exact scalars )                       [B, H_kv, P, 9]
+ * Column 0 over column 1 is a norm-weighted cos(E, c); the forward-only weights assume
+ * cos(E, c11) = cos(E, c22) = -cos(E, c12).  round: window, n_sink, n_recent, sm_scale
+ * (n_merge is not used but must be feasible).  fp32 arithmetic on the vector units; a
+ * diagnostic, not part of a merge round.  Errors as kvs_score's.
+ */
+kvs_status kvs_exact_e_diag(const kvs_cache* cache, kvs_dtype dtype,
+                            const void* K, const void* V, const int32_t* n, const void* Qw,
+                            const kvs_round* round, const float* E, const float* lse, const float* O,
+                            float* slot_out, float* pair_out, void* stream);
 
 /*
  * kvs_append — the cache write of new raw tokens (a prefill chunk in the chunked regime of

@@ -346,6 +346,24 @@ kvs_status kvs_score_merge_stats(const kvs_cache* cache, kvs_dtype dtype, const 
   return hip_status(e, "kvs_score_merge_stats");
 }
 
+kvs_status kvs_exact_e_diag(const kvs_cache* cache, kvs_dtype dtype, const void* K, const void* V, const int32_t* n,
+                            const void* Qw, const kvs_round* round, const float* E, const float* lse, const float* O,
+                            float* slot_out, float* pair_out, void* stream) {
+  kvs::Shape s;
+  kvs::RoundP r;
+  kvs_status st = check_cache(cache, dtype, s);
+  if (st) return st;
+  if ((st = check_round(round, s, r, true))) return st;
+  if (s.N < 1) return fail(KVS_ERR_SHAPE, "kvs_exact_e_diag needs n_slots >= 1");
+  if (!K || !V || !Qw || !E || !lse || !O || !slot_out || (r.P > 0 && !pair_out))
+    return fail(KVS_ERR_NULL, "kvs_exact_e_diag: K, V, Qw, E, lse, O, slot_out and pair_out are required");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(Qw))
+    return fail(KVS_ERR_ALIGN, "K, V, Qw must be 16-byte aligned");
+  return hip_status(kvs::launch_exact_e(s, r, K, V, n, Qw, E, lse, O, slot_out, pair_out,
+                                        static_cast<hipStream_t>(stream)),
+                    "kvs_exact_e_diag");
+}
+
 kvs_status kvs_append(const kvs_cache* cache, kvs_dtype dtype, void* K, void* V, int32_t* n, int64_t at,
                       const kvs_cache* src, const void* K_new, const void* V_new, int64_t from, int64_t count,
                       void* stream) {

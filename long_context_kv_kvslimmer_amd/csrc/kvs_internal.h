@@ -64,6 +64,11 @@ hipError_t launch_merge(const Shape& s, const RoundP& r, const void* K, const vo
                         const float* g_self, const float* g_cross, const int32_t* sel_state, const OutP& o,
                         void* K_out, void* V_out, int32_t* n_out, int32_t* src_out, hipStream_t st);
 
+// ---- exact-gradient diagnostics ----
+hipError_t launch_exact_e(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
+                          const void* Qw, const float* E, const float* lse, const float* O, float* slot_out,
+                          float* pair_out, hipStream_t st);
+
 // ---- append raw tokens (count 1) into a cache ----
 hipError_t launch_append(const Shape& dst, const Shape& src, void* K, void* V, int32_t* n, int64_t at,
                          const void* K_new, const void* V_new, int64_t from, int64_t count, hipStream_t st);

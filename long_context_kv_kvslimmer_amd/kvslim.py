@@ -21,7 +21,7 @@ KVS_BF16, KVS_F32 = 0, 1
 KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE, KVS_OP_SCORE_MERGE, KVS_OP_STATS_MERGE = range(6)
 
 EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_score_merge", "kvs_merge_weights", "kvs_merge_compact",
-           "kvs_append", "kvs_score_merge_stats",
+           "kvs_append", "kvs_score_merge_stats", "kvs_exact_e_diag",
            "kvs_decode_attn", "kvs_marks_begin", "kvs_marks_end", "kvs_mark_name", "kvs_mark_ms", "kvs_status_str",
            "kvs_last_error", "kvs_version")
 
@@ -59,6 +59,7 @@ def _load():
         "kvs_merge_compact": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, P, R, P, C, ctypes.c_int, P, P, P, P, P]),
         "kvs_decode_attn": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, F, P, P, SZ, P]),
         "kvs_append": (ctypes.c_int, [C, ctypes.c_int, P, P, P, I64, C, P, P, I64, I64, P]),
+        "kvs_exact_e_diag": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, R, P, P, P, P, P, P]),
         "kvs_score_merge_stats": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, R, P, P, P, P, C, ctypes.c_int, P, P,
                                                   P, P, P, SZ, P]),
         "kvs_marks_begin": (ctypes.c_int, [I32, ctypes.c_char_p]),
@@ -232,3 +233,10 @@ def kvs_append(cache: KvsCache, K, V, n, at: int, src: KvsCache, K_new, V_new, f
         raise ValueError("cache and source must share a dtype")
     _check(_lib.kvs_append(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), at, ctypes.byref(src),
                            _ptr(K_new), _ptr(V_new), from_, count, _stream()))
+
+
+def kvs_exact_e_diag(cache: KvsCache, K, V, n, Qw, rnd: KvsRound, E, lse, O, slot_out, pair_out):
+    _same_layout(K, V)
+    _check(_lib.kvs_exact_e_diag(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(Qw),
+                                 ctypes.byref(rnd), _ptr(E), _ptr(lse), _ptr(O), _ptr(slot_out), _ptr(pair_out),
+                                 _stream()))

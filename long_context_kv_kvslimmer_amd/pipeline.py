@@ -105,6 +105,21 @@ def run_round_given_stats(K, V, n, Qw, lse, O, n_q_heads: int, window: int, n_si
     return bufs
 
 
+def exact_e_diag(K, V, n, Qw, E, lse, O, n_q_heads: int, window: int, n_sink: int, n_recent: int,
+                 n_slots: int | None = None):
+    """Exact-gradient diagnostics of one round (kvs_exact_e_diag): returns slot_out
+    [B, H, N, 3] and pair_out [B, H, P, 9]."""
+    B, H, cap, D = K.shape
+    N = cap if n_slots is None else n_slots
+    P = L.num_pairs(N, n_sink, n_recent)
+    cache = L.cache_desc(K, n_q_heads, N)
+    rnd = L.round_desc(window, n_sink, n_recent, 0, 1.0 / math.sqrt(D))
+    slot_out = torch.empty(B, H, N, 3, dtype=torch.float32, device=K.device)
+    pair_out = torch.empty(B, H, max(P, 1), 9, dtype=torch.float32, device=K.device)
+    L.kvs_exact_e_diag(cache, K, V, n, Qw, rnd, E, lse, O, slot_out, pair_out)
+    return slot_out, pair_out[:, :, :P]
+
+
 def run_full_round_fused(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_recent: int,
                          bufs: RoundBuffers, n_slots: int | None = None):
     """A full round (every candidate pair merges) through kvs_score_merge."""
