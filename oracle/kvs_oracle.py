@@ -88,6 +88,29 @@ def spectral_mode_contributions(x_t: np.ndarray, x_t1: np.ndarray, W: np.ndarray
     return lam * p_t * p_t1 / den
 
 
+def spectral_contributions(X: np.ndarray, modes: np.ndarray, lam: np.ndarray):
+    """The per-mode split of [DD] 数学主线一 for a whole token sequence, given the
+    eigen-pairs of M = W Wᵀ: ``modes`` [r, d] holds the eigenvectors u_i as rows,
+    ``lam`` [r] their eigenvalues (the modes with λ_i = 0 contribute nothing, so
+    the r = d_k nonzero ones of a thin SVD W = U Σ Vᵀ, λ = σ², suffice).  For every
+    adjacent pair (t, t+1): p_{t,i} = x_t u_i, and
+    c[t, i] = λ_i p_{t,i} p_{t+1,i} / (sqrt(Σ_i λ_i p_{t,i}²) sqrt(Σ_i λ_i p_{t+1,i}²)),
+    cos[t] = Σ_i c[t, i] = cos(x_t W, x_{t+1} W).  A zero norm gives c = 0 and
+    cos = 0 (reading O23).  Returns (c [T−1, r], cos [T−1])."""
+    X = np.asarray(X, F64)
+    U = np.asarray(modes, F64)
+    lam = np.asarray(lam, F64)
+    Pm = X @ U.T
+    ny = np.sqrt(np.sum(lam * Pm * Pm, axis=1))
+    T = X.shape[0]
+    c = np.zeros((max(T - 1, 0), U.shape[0]))
+    for t in range(T - 1):
+        den = ny[t] * ny[t + 1]
+        if den > 0:
+            c[t] = lam * Pm[t] * Pm[t + 1] / den
+    return c, c.sum(axis=1)
+
+
 # ---------------------------------------------------------------------------
 # 数学主线三: single-query attention, gradient and exact Hessian blocks
 # ---------------------------------------------------------------------------

@@ -565,3 +565,29 @@ def test_exact_diagnostics_invariants():
         g11, g12, g22 = d["g_self_e"][m], d["g_cross_e"][p], d["g_self_e"][m + 1]
         if g11 + 2 * g12 + g22 > 0 and g11 * g22 - g12 * g12 > 0:
             assert d["loss_exact"][p] <= d["loss_fwd"][p] + 1e-12
+
+
+# ------------------------------------------------------- spectral contributions --
+def test_spectral_contributions_match_the_pairwise_split():
+    """Given the eigen-pairs of W Wᵀ from numpy.linalg.eigh, the sequence split equals the
+    pairwise one for every adjacent pair, and its sum is the cosine of the projected keys;
+    the d_k nonzero modes of the thin SVD give the same numbers."""
+    rng = _rng(60)
+    T, d, dk = 9, 12, 4
+    X = rng.standard_normal((T, d))
+    W = rng.standard_normal((d, dk))
+    lam, U = np.linalg.eigh(W @ W.T)
+    c, cs = O.spectral_contributions(X, U.T, lam)
+    for t in range(T - 1):
+        assert np.allclose(c[t], O.spectral_mode_contributions(X[t], X[t + 1], W), atol=1e-12)
+        assert abs(cs[t] - O.cosine(X[t] @ W, X[t + 1] @ W)) < 1e-12
+    Us, sig, _ = np.linalg.svd(W, full_matrices=False)
+    c2, cs2 = O.spectral_contributions(X, Us.T, sig ** 2)
+    assert np.allclose(cs2, cs, atol=1e-12)
+    assert np.allclose(np.sort(c2, axis=1), np.sort(c[:, -dk:], axis=1), atol=1e-12)
+
+
+def test_spectral_contributions_zero_token():
+    X = np.array([[1.0, 0.0], [0.0, 0.0], [0.5, 0.5]])
+    c, cs = O.spectral_contributions(X, np.eye(2), np.array([2.0, 1.0]))
+    assert np.all(c[:2] == 0) and np.all(cs == 0)
