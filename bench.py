@@ -56,7 +56,8 @@ KERNEL_LABELS = (("p1_mfma_kernel", "score_pass1"), ("pass1_valu_kernel", "score
                  ("combine_wave_kernel", "combine"), ("select_fixed_kernel", "select"),
                  ("select_small_kernel", "select"), ("sel_clear_kernel", "select"), ("sel_hist_kernel", "select"),
                  ("sel_count_kernel", "select"), ("sel_final_kernel", "select"), ("append_kernel", "append"),
-                 ("pack_kernel", "pack"), ("exact_e_kernel", "exact_e"),
+                 ("pack_kernel", "pack"), ("exact_e_kernel", "exact_e"), ("spectral_proj_kernel", "spectral_proj"),
+                 ("spectral_pair_kernel", "spectral_pair"),
                  ("merge_compact_kernel", "merge_compact"), ("decode_mfma_kernel", "decode"),
                  ("decode_kernel", "decode"))
 COPY_BYTES = 1 << 30            # calibration copy: reads and writes this many bytes
@@ -585,6 +586,65 @@ def diag_timing(dev, reps=5):
                     "working, not KVSlimmer's accuracy"}
 
 
+def spectral_timing(dev, T=32768, d=4096, r=128, reps=5):
+    """The spectral split on a Llama-3.1-8B-shaped key projection (d_model 4096 -> one KV
+    head of 128): 32K synthetic token states (AR(1) in d_model), W with a decaying
+    spectrum, its thin SVD as the modes; kernel times and what the split shows (the share
+    of the mean adjacent-key cosine carried by the top modes)."""
+    import statistics
+    import torch
+    from long_context_kv_kvslimmer_amd import kvslim as L
+    g = torch.Generator(device=dev)
+    g.manual_seed(23)
+    # AR(1) token states x_t = 0.9 x_{t-1} + eps_t, 256 steps at a time with a
+    # lower-triangular power matrix
+    eps = torch.randn(T, d, generator=g, device=dev) * 0.44
+    coef = torch.tensor(0.9, device=dev)
+    X = torch.empty(T, d, device=dev)
+    carry = torch.randn(d, generator=g, device=dev)
+    blk = 256
+    tt = torch.arange(blk, device=dev, dtype=torch.float32)
+    Lm = torch.where(tt[:, None] >= tt[None, :], coef ** (tt[:, None] - tt[None, :]), torch.zeros((), device=dev))
+    pw = coef ** (tt + 1)
+    for b0 in range(0, T, blk):
+        y = Lm @ eps[b0:b0 + blk] + pw[:, None] * carry[None, :]
+        X[b0:b0 + blk] = y
+        carry = y[-1]
+    W = torch.randn(d, r, generator=g, device=dev) / torch.sqrt(1 + torch.arange(r, device=dev, dtype=torch.float32))
+    U, sig, _ = torch.linalg.svd(W.cpu().double(), full_matrices=False)
+    Xb = X.to(torch.bfloat16).contiguous()
+    Ub = U.T.contiguous().to(torch.bfloat16).to(dev)
+    lam = (sig ** 2).float().to(dev)
+    proj = torch.empty(T, r, device=dev)
+    contrib = torch.empty(T - 1, r, device=dev)
+    cos = torch.empty(T - 1, device=dev)
+    L.kvs_spectral_modes(Xb, Ub, lam, proj, contrib, cos)
+    torch.cuda.synchronize()
+    per = {}
+    for _ in range(reps):
+        marks = L.KernelMarks(max_launches=4)
+        with marks:
+            L.kvs_spectral_modes(Xb, Ub, lam, proj, contrib, cos)
+        torch.cuda.synchronize()
+        for name, ms in marks.times():
+            per.setdefault(name, []).append(ms)
+    med = {k: statistics.median(v) for k, v in per.items()}
+    share = contrib.mean(0) / cos.mean()
+    top = torch.sort(share, descending=True).values.cumsum(0)
+    proj_bytes = T * d * 2 + r * d * 2 + T * r * 4
+    flop = 2 * T * d * r
+    pm = med.get("spectral_proj", float("nan"))
+    return {"config": f"spectral split, T={T} tokens, d_model={d}, {r} modes (bf16)",
+            "kernel_ms": {k: round(v, 4) for k, v in med.items()},
+            "roofline": {"kernel": "spectral_proj", "bound": "hbm", "achieved": round(proj_bytes / (pm * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(proj_bytes / (pm * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                         "mfma_TFLOPs": round(flop / (pm * 1e-3) / 1e12, 1)},
+            "mean_adjacent_cos": round(cos.mean().item(), 4),
+            "share_of_mean_cos_top4_top16_modes": [round(top[3].item(), 3), round(top[15].item(), 3)],
+            "note": "synthetic W (singular values ~ 1/sqrt(i)) and AR(1) token states: the split shows the tool "
+                    "working; the pages' figure needs a trained model's projections"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -599,6 +659,8 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("SQ_CSV", "STATS_CSV", "CMD"))
     ap.add_argument("--summarize-per-config", nargs=2, metavar=("JSONL", "CMD"))
     ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "TITLE", "CMD"))
+    ap.add_argument("--spectral", action="store_true",
+                    help="time the spectral split (32K tokens, d_model 4096, 128 modes) instead of the bench line")
     ap.add_argument("--diag", action="store_true",
                     help="time the exact-gradient diagnostics on a C2 layer instead of the bench line")
     ap.add_argument("--no-chunk-sweep", action="store_true",
@@ -635,6 +697,9 @@ def main():
     torch.cuda.set_device(0)
     if args.diag:
         print(json.dumps(diag_timing(dev)), flush=True)
+        return
+    if args.spectral:
+        print(json.dumps(spectral_timing(dev)), flush=True)
         return
     if args.per_config:
         per_config(dev, [int(x) for x in args.per_config.split(",")],

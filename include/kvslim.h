@@ -15,6 +15,7 @@
  *   kvs_decode_attn    GQA decode attention over a (merged) cache
  *   kvs_append         write raw tokens (count 1) into a cache: a prefill chunk or a decode step
  *   kvs_exact_e_diag   diagnostics: exact-gradient scalars and weights against the forward-only ones
+ *   kvs_spectral_modes analysis: per-eigen-mode split of adjacent-key cosines
  *
  * Sources.  The operations follow the KVSlimmer deep-dive "论文专题讲解：KVSlimmer：
  * 非对称 KV 合并的数学与工程" (charles2530.github.io), sections 数学主线二 (merging an adjacent
@@ -254,6 +255,26 @@ kvs_status kvs_exact_e_diag(const kvs_cache* cache, kvs_dtype dtype,
                             const void* K, const void* V, const int32_t* n, const void* Qw,
                             const kvs_round* round, const float* E, const float* lse, const float* O,
                             float* slot_out, float* pair_out, void* stream);
+
+/*
+ * kvs_spectral_modes — the per-mode split of adjacent-key similarity of the deep-dive's
+ * section 数学主线一.  Keys are y_t = x_t W; with the eigen-pairs (u_i, l_i) of W W^T,
+ * p_{t,i} = x_t . u_i and
+ *   contrib[t, i] = l_i p_{t,i} p_{t+1,i} / (|y_t| |y_{t+1}|),  |y_t|^2 = sum_i l_i p_{t,i}^2,
+ *   cos[t] = sum_i contrib[t, i] = cos(y_t, y_{t+1}),
+ * zero when a norm is zero.  X: [n_tokens, d_model] bf16 token states (rows contiguous);
+ * modes: [n_modes, d_model] bf16, the eigenvectors as rows (the n_modes = d_k modes of
+ * nonzero eigenvalue suffice: the left singular vectors of W), eigvals [n_modes] fp32.
+ * Outputs (fp32, caller-owned): proj [n_tokens, n_modes] = the p_{t,i}; contrib
+ * [n_tokens - 1, n_modes] (nullable); cos [n_tokens - 1].  The projections run on the
+ * matrix cores with fp32 accumulation.  An analysis tool, not part of a merge round.
+ * Errors: KVS_ERR_DTYPE unless bf16; KVS_ERR_SHAPE unless n_tokens >= 1, d_model is a
+ * positive multiple of 64 and 1 <= n_modes <= 4096; KVS_ERR_ALIGN unless X and modes are
+ * 16-byte aligned.
+ */
+kvs_status kvs_spectral_modes(kvs_dtype dtype, const void* X, int64_t n_tokens, int32_t d_model,
+                              const void* modes, const float* eigvals, int32_t n_modes,
+                              float* proj, float* contrib, float* cos, void* stream);
 
 /*
  * kvs_append — the cache write of new raw tokens (a prefill chunk in the chunked regime of

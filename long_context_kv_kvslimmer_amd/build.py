@@ -23,7 +23,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]
 
 SOURCES = ["kvs_api.cpp", "kvs_score.hip", "kvs_score_mfma.hip", "kvs_select.hip", "kvs_merge.hip",
-           "kvs_decode.hip", "kvs_diag.hip"]
+           "kvs_decode.hip", "kvs_diag.hip", "kvs_spectral.hip"]
 
 
 def _compile(src: str) -> str:

@@ -364,6 +364,21 @@ kvs_status kvs_exact_e_diag(const kvs_cache* cache, kvs_dtype dtype, const void*
                     "kvs_exact_e_diag");
 }
 
+kvs_status kvs_spectral_modes(kvs_dtype dtype, const void* X, int64_t n_tokens, int32_t d_model, const void* modes,
+                              const float* eigvals, int32_t n_modes, float* proj, float* contrib, float* cos,
+                              void* stream) {
+  if (dtype != KVS_BF16) return fail(KVS_ERR_DTYPE, "kvs_spectral_modes takes bf16 token states and modes");
+  if (n_tokens < 1 || d_model < 64 || d_model % 64 || n_modes < 1 || n_modes > 4096)
+    return fail(KVS_ERR_SHAPE, "kvs_spectral_modes: n_tokens >= 1, d_model a positive multiple of 64, "
+                               "1 <= n_modes <= 4096");
+  if (!X || !modes || !eigvals || !proj || (n_tokens > 1 && !cos))
+    return fail(KVS_ERR_NULL, "kvs_spectral_modes: X, modes, eigvals, proj and cos are required");
+  if (!aligned16(X) || !aligned16(modes)) return fail(KVS_ERR_ALIGN, "X and modes must be 16-byte aligned");
+  return hip_status(kvs::launch_spectral(X, n_tokens, d_model, modes, eigvals, n_modes, proj, contrib, cos,
+                                         static_cast<hipStream_t>(stream)),
+                    "kvs_spectral_modes");
+}
+
 kvs_status kvs_append(const kvs_cache* cache, kvs_dtype dtype, void* K, void* V, int32_t* n, int64_t at,
                       const kvs_cache* src, const void* K_new, const void* V_new, int64_t from, int64_t count,
                       void* stream) {

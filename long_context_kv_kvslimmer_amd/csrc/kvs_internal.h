@@ -64,6 +64,10 @@ hipError_t launch_merge(const Shape& s, const RoundP& r, const void* K, const vo
                         const float* g_self, const float* g_cross, const int32_t* sel_state, const OutP& o,
                         void* K_out, void* V_out, int32_t* n_out, int32_t* src_out, hipStream_t st);
 
+// ---- spectral split of adjacent-key cosines ----
+hipError_t launch_spectral(const void* X, int64_t T, int d, const void* U, const float* lam, int r, float* P,
+                           float* c, float* cosv, hipStream_t st);
+
 // ---- exact-gradient diagnostics ----
 hipError_t launch_exact_e(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
                           const void* Qw, const float* E, const float* lse, const float* O, float* slot_out,

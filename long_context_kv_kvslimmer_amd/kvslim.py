@@ -21,7 +21,7 @@ KVS_BF16, KVS_F32 = 0, 1
 KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE, KVS_OP_SCORE_MERGE, KVS_OP_STATS_MERGE = range(6)
 
 EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_score_merge", "kvs_merge_weights", "kvs_merge_compact",
-           "kvs_append", "kvs_score_merge_stats", "kvs_exact_e_diag",
+           "kvs_append", "kvs_score_merge_stats", "kvs_exact_e_diag", "kvs_spectral_modes",
            "kvs_decode_attn", "kvs_marks_begin", "kvs_marks_end", "kvs_mark_name", "kvs_mark_ms", "kvs_status_str",
            "kvs_last_error", "kvs_version")
 
@@ -60,6 +60,7 @@ def _load():
         "kvs_decode_attn": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, F, P, P, SZ, P]),
         "kvs_append": (ctypes.c_int, [C, ctypes.c_int, P, P, P, I64, C, P, P, I64, I64, P]),
         "kvs_exact_e_diag": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, R, P, P, P, P, P, P]),
+        "kvs_spectral_modes": (ctypes.c_int, [ctypes.c_int, P, I64, I32, P, P, I32, P, P, P, P]),
         "kvs_score_merge_stats": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, R, P, P, P, P, C, ctypes.c_int, P, P,
                                                   P, P, P, SZ, P]),
         "kvs_marks_begin": (ctypes.c_int, [I32, ctypes.c_char_p]),
@@ -240,3 +241,13 @@ def kvs_exact_e_diag(cache: KvsCache, K, V, n, Qw, rnd: KvsRound, E, lse, O, slo
     _check(_lib.kvs_exact_e_diag(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(Qw),
                                  ctypes.byref(rnd), _ptr(E), _ptr(lse), _ptr(O), _ptr(slot_out), _ptr(pair_out),
                                  _stream()))
+
+
+def kvs_spectral_modes(X, modes, eigvals, proj, contrib, cos):
+    """X [T, d] and modes [r, d] bf16 (rows contiguous), eigvals [r] fp32; writes proj [T, r],
+    contrib [T - 1, r] (may be None) and cos [T - 1]."""
+    if X.dim() != 2 or modes.dim() != 2 or X.stride(1) != 1 or modes.stride(1) != 1 or \
+            X.stride(0) != X.shape[1] or modes.stride(0) != modes.shape[1] or X.shape[1] != modes.shape[1]:
+        raise ValueError("X [T, d] and modes [r, d] must be contiguous with the same d")
+    _check(_lib.kvs_spectral_modes(dtype_code(X), _ptr(X), X.shape[0], X.shape[1], _ptr(modes), _ptr(eigvals),
+                                   modes.shape[0], _ptr(proj), _ptr(contrib), _ptr(cos), _stream()))
