@@ -647,6 +647,9 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     const f32x4_t be = {lge * ics, lge * ics, lge * ics, lge * ics};
     const f32x4_t bo = {lgo * ics, lgo * ics, lgo * ics, lgo * ics};
     f32x4_t se[2], so[2], re[2], ro[2], gee = z, goo = z, geo = z;
+    // the two workgroups that share a CU pair their waves on each SIMD: the one issuing its
+    // matrix block goes first, the other fills the vector slots in between
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch = 4 * ks + g4;
@@ -669,6 +672,7 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       goo = mfma(vo, vo, goo);
       geo = mfma(ve, vo, geo);
     }
+    __builtin_amdgcn_s_setprio(0);
     // diagonal element n of a 16x16 result sits in lane n + 16 (n / 4), register n % 4
     const int rsel = n16 & 3;
     auto pick = [&](const f32x4_t& g) {
@@ -798,7 +802,10 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     wait_tile(ntiles - 1 - t < 2 ? ntiles - 1 - t : 2);   // tile t landed
     __syncthreads();
     if (MERGE && t > 0) {
+      // the merge sits between two barriers of this workgroup: let it finish first
+      __builtin_amdgcn_s_setprio(2);
       merge_tile(t - 1);
+      __builtin_amdgcn_s_setprio(0);
       wait_lds();   // its LDS reads are done before the ring slot is refilled
     }
     if (t + 3 < ntiles) issue(t + 3);
