@@ -839,15 +839,15 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
 // -------------------------------------------------------------------- dispatch --
 bool use_mfma_scorer(const Shape& s) { return s.bf16 && (s.D == 64 || s.D == 128); }
 
-// Chunk plan shared by both passes: slot chunks are multiples of the tile, start at
-// base = -(S mod 2) so that every tile starts on a candidate-pair boundary, and number
-// about 2 chunks per CU over the whole grid.
+// Chunk plan of pass 1: slot chunks are multiples of the tile, start at base = -(S mod 2)
+// so that every tile starts on a candidate-pair boundary, and number about one per CU over
+// the whole grid (pass 1 runs one workgroup per CU).
 static void mfma_plan(const Shape& s, const RoundP& r, int64_t& base, int64_t& chunk, int& nsplit) {
   base = -(r.S & 1);
   const int64_t span = s.N - base;
   const int64_t BH = (int64_t)s.B * s.Hkv;
   const int64_t nqb = ((int64_t)s.G * r.W + kQB - 1) / kQB;
-  int64_t want = (512 + BH * nqb - 1) / (BH * nqb);   // target chunks per (bh, query block)
+  int64_t want = (256 + BH * nqb - 1) / (BH * nqb);   // target chunks per (bh, query block)
   if (want < 1) want = 1;
   int64_t c = (span + want - 1) / want;
   if (c < 512 * kGroups) c = 512 * kGroups;             // keep partial records small
