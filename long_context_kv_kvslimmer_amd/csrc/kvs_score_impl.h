@@ -14,6 +14,12 @@ struct P1Args {
   int64_t N, sb, sh, GW, chunk;
   int Hkv, Hq, G, W, nsplit;
   float scale;
+  // MFMA pass 1 with one split per query: finish the statistics in the pass instead of the
+  // combine (lse, O and the pass-2 operand pack); unused otherwise
+  int fin;
+  float* lse;
+  float* O;
+  PackP pk;
 };
 
 struct P2Args {

@@ -18,6 +18,7 @@
 // row layout), so the merge pass can recompute bit-identical values.
 #include "kvs_common.h"
 #include "kvs_dma.h"
+#include "kvs_pack.h"
 #include "kvs_score_impl.h"
 
 namespace kvs {
@@ -448,6 +449,36 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
   __syncthreads();
   const int64_t qbase = qb * kQB;
   const int nq = (int)(a.GW - qbase < kQB ? a.GW - qbase : kQB);
+  if (a.fin) {
+    // one split per query: what the combine does with a single record, here (o / l, the
+    // log-sum-exp in natural log, the pass-2 operand pack), one wave per query row
+    constexpr int E = D / 64, RPW = kQB / (kThreads / 64);   // rows per wave
+    const int ln = tid & 63, w8 = tid >> 6;
+    // the query chunks of all the wave's rows first, so their loads overlap
+    uint4 qch[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int qq = w8 + i * (kThreads / 64);
+      qch[i] = qq < nq ? pack_query_chunk<D>(a.pk, bh * a.GW + qbase + qq, ln) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int qq = w8 + i * (kThreads / 64);
+      if (qq >= nq) break;   // wave-uniform
+      const float* row = xo + qq * RS;
+      const float mm = row[0], ll = row[1];
+      float ov[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) ov[e] = row[4 + ln + 64 * e] / ll;
+      const int64_t u = bh * a.GW + qbase + qq;
+#pragma unroll
+      for (int e = 0; e < E; ++e) a.O[u * D + ln + 64 * e] = ov[e];
+      const float lse_u = (mm + __log2f(ll)) * kLn2;
+      if (ln == 0) a.lse[u] = lse_u;
+      pack_row_wave_q<D>(a.pk, u, ov, lse_u, ln, qch[i]);
+    }
+    return;
+  }
   for (int idx = tid; idx < nq * (RS / 4); idx += kThreads) {
     const int qq = idx / (RS / 4), c = idx % (RS / 4);
     float* rec = a.part + ((bh * a.GW + qbase + qq) * a.nsplit + split) * (int64_t)RS;
@@ -896,29 +927,37 @@ static hipError_t launch_p2_d(const Shape& s, const RoundP& r, const P2Args& p2,
                               hipStream_t st);
 
 template <int D>
-static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p1, const P2Args& p2,
+static hipError_t launch_mfma_d(const Shape& s, const RoundP& r, const P1Args& p1_in, const P2Args& p2,
                                 const CosArgs& ca, int64_t base, float* lse, float* O, int merge, hipStream_t st) {
   const int64_t BH = (int64_t)s.B * s.Hkv;
-  const int nqb = (int)((p1.GW + kQB - 1) / kQB);
-  const dim3 grid((unsigned)(BH * p1.nsplit * nqb));
+  const int nqb = (int)((p1_in.GW + kQB - 1) / kQB);
+  const dim3 grid((unsigned)(BH * p1_in.nsplit * nqb));
+  PackP pk;
+  pk.ops = const_cast<uint4*>(p2.ops);
+  pk.qc = const_cast<float*>(p2.qc);
+  pk.Qw = p1_in.Qw;
+  pk.nwb = p2.nwb;
+  pk.GW = p1_in.GW;
+  pk.Hkv = s.Hkv;
+  pk.Hq = s.Hq;
+  pk.G = s.G;
+  pk.W = r.W;
+  // one split per query: pass 1 finishes the statistics itself and no combine runs
+  P1Args p1 = p1_in;
+  p1.fin = p1.nsplit == 1;
+  p1.lse = lse;
+  p1.O = O;
+  p1.pk = pk;
   if (p1.n)
     KVS_LAUNCH("score_pass1", (p1_mfma_kernel<D, true>), grid, dim3(kThreads), 0, st, p1, base, ca, (int)BH);
   else
     KVS_LAUNCH("score_pass1", (p1_mfma_kernel<D, false>), grid, dim3(kThreads), 0, st, p1, base, ca, (int)BH);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  PackP pk;
-  pk.ops = const_cast<uint4*>(p2.ops);
-  pk.qc = const_cast<float*>(p2.qc);
-  pk.Qw = p1.Qw;
-  pk.nwb = p2.nwb;
-  pk.GW = p1.GW;
-  pk.Hkv = s.Hkv;
-  pk.Hq = s.Hq;
-  pk.G = s.G;
-  pk.W = r.W;
-  e = launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st, &pk);
-  if (e != hipSuccess) return e;
+  if (!p1.fin) {
+    e = launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st, &pk);
+    if (e != hipSuccess) return e;
+  }
   return launch_p2_d<D>(s, r, p2, base, merge, st);
 }
 
