@@ -31,8 +31,10 @@ checked against something other than itself: finite differences, brute-force
 minimisation, closed forms, textbook/library routines, exact invariants or the
 numbers the pages print.  Parity unpinned (true to the pages only by argument):
 the multi-query aggregation of the Hessian norms (reading O2), the pair
-selection policy (O6/O7) and the degenerate-denominator threshold (O10); each
-is marked "parity unpinned" below.
+selection policy (O6/O7) and the degenerate-denominator thresholds (O10, and
+O22 for the exact-gradient weights); each is marked "parity unpinned" below.
+The chunked budget loop (O21) is pinned by its invariants only: the pages give
+its settings, not its steps.
 """
 from __future__ import annotations
 
@@ -435,9 +437,10 @@ def compose_src(prev_src: np.ndarray, src: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 def exact_weights(g11: float, g12: float, g22: float):
     """``hessian_weights`` with the degenerate case handled (reading O22, pages
-    silent): when g11 + 2 g12 + g22 is not finite or its magnitude is at most
-    1e-6 (|g11| + 2|g12| + |g22|), the plain average (½, ½).  An indefinite
-    model keeps its stationary point (no clamping).  Returns (w_m, w_{m+1})."""
+    silent; the threshold is parity unpinned): when g11 + 2 g12 + g22 is not
+    finite or its magnitude is at most 1e-6 (|g11| + 2|g12| + |g22|), the plain
+    average (½, ½).  An indefinite model keeps its stationary point (no
+    clamping).  Returns (w_m, w_{m+1})."""
     den = g11 + 2.0 * g12 + g22
     scale = abs(g11) + 2.0 * abs(g12) + abs(g22)
     if not math.isfinite(den) or abs(den) <= DEGENERATE_REL * scale:

@@ -204,3 +204,47 @@ def test_append_validation(L):
     assert call(0, 0, 5, K=ctypes.c_void_p(4104)) == L.KVS_ERR_ALIGN
     assert call(0, 0, 5, dt=9) == L.KVS_ERR_DTYPE
     assert call(200, 50, 0) == L.KVS_OK               # nothing to write: no launch
+
+
+def test_score_merge_stats_validation(L):
+    f = L._lib.kvs_score_merge_stats
+    c = L.KvsCache(1, 2, 8, 128, 1000, 2 * 1000 * 128, 1000 * 128)
+    r = L.round_desc(8, 0, 0, 100, 0.1)
+    o900 = L.KvsCache(1, 2, 8, 128, 900, 2 * 900 * 128, 900 * 128)
+    o500 = L.KvsCache(1, 2, 8, 128, 500, 2 * 500 * 128, 500 * 128)
+
+    def call(out, lse=FAKE, O=FAKE, ws=1 << 30):
+        return f(ctypes.byref(c), L.KVS_BF16, FAKE, FAKE, None, FAKE, ctypes.byref(r), lse, O, FAKE, FAKE,
+                 ctypes.byref(out), L.KVS_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert call(o500) == L.KVS_ERR_SHAPE                  # out must hold N - M slots
+    assert call(o900, lse=None) == L.KVS_ERR_NULL
+    assert call(o900, O=ctypes.c_void_p(4100)) == L.KVS_ERR_ALIGN
+    assert call(o900, ws=16) == L.KVS_ERR_WORKSPACE
+    assert L.workspace_bytes(L.KVS_OP_STATS_MERGE, c, r) > 0
+
+
+def test_exact_e_diag_validation(L):
+    f = L._lib.kvs_exact_e_diag
+    r = L.round_desc(8, 0, 0, 0, 0.1)
+
+    def call(c, E=FAKE, pair=FAKE):
+        return f(ctypes.byref(c), L.KVS_BF16, FAKE, FAKE, None, FAKE, ctypes.byref(r), E, FAKE, FAKE, FAKE, pair,
+                 None)
+    assert call(_cache(D=96)) == L.KVS_ERR_SHAPE
+    assert call(_cache(), E=None) == L.KVS_ERR_NULL
+    assert call(_cache(), pair=None) == L.KVS_ERR_NULL      # P > 0 needs the pair outputs
+    assert call(_cache(N=0)) == L.KVS_ERR_SHAPE
+
+
+def test_spectral_modes_validation(L):
+    f = L._lib.kvs_spectral_modes
+
+    def call(dt=L.KVS_BF16, X=FAKE, T=100, d=256, r=16, modes=FAKE, cos=FAKE):
+        return f(dt, X, T, d, modes, FAKE, r, FAKE, None, cos, None)
+    assert call(dt=L.KVS_F32) == L.KVS_ERR_DTYPE
+    assert call(d=96) == L.KVS_ERR_SHAPE                    # d_model a multiple of 64
+    assert call(r=0) == L.KVS_ERR_SHAPE
+    assert call(T=0) == L.KVS_ERR_SHAPE
+    assert call(X=None) == L.KVS_ERR_NULL
+    assert call(cos=None) == L.KVS_ERR_NULL
+    assert call(modes=ctypes.c_void_p(4104)) == L.KVS_ERR_ALIGN
