@@ -230,27 +230,32 @@ __global__ __launch_bounds__(kSelThreads) void sel_final_kernel(SelArgs a) {
   }
 }
 
-// Heads with at most kSmallSelPairs candidate pairs (short caches, e.g. a budgeted cache
-// between prefill chunks): the whole selection of one head in one workgroup, keys held in
-// registers, the four digit histograms in LDS, then the same header and chunk offsets as
-// the multi-workgroup path.  Wave w at step j holds the 64 pairs of chunk 16 j + w.
-constexpr int kSmallSelKeys = 4;
-constexpr int kSmallSelPairs = kSelThreads * kSmallSelKeys;   // 4096 pairs, 64 chunks
+// Heads with at most kOneWgMaxPairs candidate pairs: the whole selection of one head in one
+// workgroup, its keys held in registers (KPT per thread), the four digit histograms in
+// LDS, then the same header and chunk offsets as the multi-workgroup path.  Wave w at step
+// j holds the 64 pairs of chunk 16 j + w; thread t owns chunk t in the scans (at most 1024
+// chunks).  One launch instead of seven, for short caches (a budgeted cache between prefill
+// chunks): 9 us for 256 heads x 1264 pairs against ~40.  Only one CU works per head, so
+// long heads go to the multi-workgroup path (65536 pairs: 94 us here against 60).
+constexpr int kOneWgMaxKeys = 16;
+constexpr int kOneWgMaxPairs = kSelThreads * kOneWgMaxKeys;   // 16384 pairs, 256 chunks
 
-__global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelArgs a) {
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void select_onewg_kernel(SelArgs a) {
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t* st = a.st + bh * a.sel_stride;
   const float* cs = a.cos + bh * a.P;
+  constexpr int NCH = KPT * (kSelThreads / 64);   // chunks the keys cover
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
   __shared__ int lds[kSelThreads / 64];
-  __shared__ int eq_c[64], gt_c[64];
-  __shared__ uint64_t eq_m[64];
-  __shared__ int32_t sh_ptau;
-  uint32_t k[kSmallSelKeys];
+  __shared__ int eq_c[NCH], gt_c[NCH];
+  __shared__ uint64_t eq_m[NCH];
+  __shared__ int32_t sh_ct, sh_rank, sh_ptau;
+  uint32_t k[KPT];
 #pragma unroll
-  for (int j = 0; j < kSmallSelKeys; ++j) {
+  for (int j = 0; j < KPT; ++j) {
     const int64_t p = (int64_t)j * kSelThreads + tid;
     k[j] = p < a.P ? order_key(cs[p]) : 0u;
   }
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelArgs a) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kSmallSelKeys; ++j) {
+    for (int j = 0; j < KPT; ++j) {
       const int64_t p = (int64_t)j * kSelThreads + tid;
       wave_hist_add(hist, p < a.P && (k[j] & mask) == prefix, (k[j] >> shift) & 255u);
     }
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelArgs a) {
   const uint32_t tau = prefix;
   // per-chunk counts of keys equal to and above tau
 #pragma unroll
-  for (int j = 0; j < kSmallSelKeys; ++j) {
+  for (int j = 0; j < KPT; ++j) {
     const int64_t p = (int64_t)j * kSelThreads + tid;
     const uint64_t eq = __ballot(p < a.P && k[j] == tau);
     const uint64_t gt = __ballot(p < a.P && k[j] > tau);
@@ -293,50 +298,43 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelArgs a) {
       eq_m[c] = eq;
     }
   }
+  if (tid == 0) {
+    sh_ct = -1;
+    sh_rank = 0;
+    sh_ptau = -1;
+  }
   __syncthreads();
-  if (wv == 0) {
-    // chunk `lane`: the tie cut-off (the remaining-th key equal to tau), then the
-    // exclusive offsets of the selected pairs of every chunk
-    const int c = lane;
-    const int e = c < a.nchunks ? eq_c[c] : 0;
-    int incl = e;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    const int before = incl - e;
-    const bool hit = e > 0 && (uint32_t)before < remaining && remaining <= (uint32_t)incl;
-    const uint64_t hm = __ballot(hit);
-    const int ct = hm ? __ffsll((unsigned long long)hm) - 1 : -1;
-    const int rank = ct >= 0 ? (int)remaining - __shfl(before, ct, 64) : 0;   // 1-based
-    int32_t ptau = -1;
-    if (ct >= 0) {
-      const uint64_t m = eq_m[ct];
-      const bool bit = (m >> lane) & 1ull;
-      const uint64_t at = __ballot(bit && __popcll(m & ((1ull << lane) - 1ull)) + 1 == rank);
-      if (at) ptau = (int32_t)(ct * kChunkPairs + __ffsll((unsigned long long)at) - 1);
-    }
-    const int v = c < a.nchunks ? gt_c[c] + (c < ct ? e : c == ct ? rank : 0) : 0;
-    int vin = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(vin, off, 64);
-      if (lane >= off) vin += y;
-    }
-    if (c < a.nchunks) st[kSelHeaderInts + c] = vin - v;
-    const int total = __shfl(vin, 63, 64);
-    if (lane == 0) {
-      st[0] = (int32_t)tau;
-      st[1] = ptau;
-      st[2] = (int32_t)a.M;
-      st[3] = (int32_t)a.nchunks;
-      st[kSelHeaderInts + a.nchunks] = total;
-      sh_ptau = ptau;
-    }
+  // the chunk that holds the remaining-th key equal to tau, and its rank there
+  const int c = tid;
+  const bool live = c < a.nchunks && c < NCH;
+  const int e = live ? eq_c[c] : 0;
+  int tot;
+  const int before = block_exclusive_scan<kSelThreads>(e, &tot, lds);
+  if (e > 0 && (uint32_t)before < remaining && remaining <= (uint32_t)(before + e)) {
+    sh_ct = c;
+    sh_rank = (int32_t)remaining - before;   // 1-based
+  }
+  __syncthreads();
+  const int ct = sh_ct, rank = sh_rank;
+  if (wv == 0 && ct >= 0) {   // the index of that key: wave 0 scans the chunk's flag mask
+    const uint64_t m = eq_m[ct];
+    const bool bit = (m >> lane) & 1ull;
+    const uint64_t at = __ballot(bit && __popcll(m & ((1ull << lane) - 1ull)) + 1 == rank);
+    if (lane == 0 && at) sh_ptau = (int32_t)(ct * kChunkPairs + __ffsll((unsigned long long)at) - 1);
+  }
+  // selected per chunk: every key above tau, and the keys equal to tau up to the cut-off
+  const int v = live ? gt_c[c] + (c < ct ? e : c == ct ? rank : 0) : 0;
+  const int ex = block_exclusive_scan<kSelThreads>(v, &tot, lds);
+  if (live) st[kSelHeaderInts + c] = ex;
+  __syncthreads();   // sh_ptau is written
+  if (tid == 0) {
+    st[0] = (int32_t)tau;
+    st[1] = sh_ptau;
+    st[2] = (int32_t)a.M;
+    st[3] = (int32_t)a.nchunks;
+    st[kSelHeaderInts + a.nchunks] = tot;
   }
   if (a.selected || a.w) {
-    __syncthreads();
     SelHeader hd;
     hd.tau_key = tau;
     hd.p_tau = sh_ptau;
@@ -405,8 +403,12 @@ hipError_t launch_select(const Shape& s, const RoundP& r, const float* g_self, c
     KVS_LAUNCH("select", select_fixed_kernel, dim3(heads), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
   }
-  if (r.P <= kSmallSelPairs) {
-    KVS_LAUNCH("select", select_small_kernel, dim3(heads), dim3(kSelThreads), 0, st, a);
+  if (r.P <= kOneWgMaxPairs) {
+    const dim3 g(heads), b(kSelThreads);
+    if (r.P <= 4 * kSelThreads)
+      KVS_LAUNCH("select", select_onewg_kernel<4>, g, b, 0, st, a);
+    else
+      KVS_LAUNCH("select", select_onewg_kernel<16>, g, b, 0, st, a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((r.P + kHistBlock - 1) / kHistBlock), (unsigned)heads);

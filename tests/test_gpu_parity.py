@@ -109,12 +109,13 @@ def test_selection_index_tie_break():
         check_round_slice(bufs, K, V, n, Qw, 0, 0, 512, 0, 0, M, 1 / math.sqrt(128), label=f"ties M={M}")
 
 
-@pytest.mark.parametrize("P", [150001, 4097, 4096, 1264, 65])
+@pytest.mark.parametrize("P", [150001, 20000, 16385, 16384, 4097, 4096, 1264, 65])
 def test_selection_ties_against_brute_force(P):
     """Selection with long runs of bit-identical cosines at the threshold: the flags and the
     chunk offsets in the selection state equal a brute-force top-M with the lower index
-    winning ties.  P = 150001: many 4096-pair histogram workgroups, more than 1024 chunks;
-    4097: the smallest head that takes that path; 4096 and below: one workgroup per head."""
+    winning ties.  P = 150001, 20000 and 16385: many 4096-pair histogram workgroups (more
+    than 1024 chunks for the first); 16384 and below: one workgroup per head, with 16 and 4
+    keys per thread."""
     from long_context_kv_kvslimmer_amd import kvslim as L
     H = 3
     N = 2 * P + 1                                            # an odd leftover slot
