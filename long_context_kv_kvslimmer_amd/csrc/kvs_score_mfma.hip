@@ -494,8 +494,8 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
 //
 // A workgroup is four waves (128 queries) over one slot chunk; two workgroups share a CU.
 // K and V arrive by 16-byte buffer loads written straight into LDS (no register staging)
-// as 32-slot tiles in a four-deep ring: tile t is computed while t + 1 .. t + 3 are in
-// flight.  A tile's LDS row R holds slot 2 (R % 16) + R / 16 (even slots first).  Rows are
+// as 32-slot tiles in a four-deep ring: tile t is computed while tile t - 1 is merged and
+// tiles t + 1, t + 2 are in flight.  A tile's LDS row R holds slot 2 (R % 16) + R / 16 (even slots first).  Rows are
 // unpadded; the 16-byte chunks of row r sit at position c ^ swz(r), which keeps the MFMA
 // operand reads free of bank conflicts.  ||v||^2 and v_m . v_{m+1} come from the
 // diagonals of Gram products of the V operand registers, so a tile needs no setup pass
@@ -567,17 +567,12 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       dma4(rn, lds_addr(nr + buf * kT2), off);
     }
   };
-  // wait for every load of a tile after which `later` (0..2) tiles were issued
+  // wait for every load of a tile after which `later` (0 or 1) tiles were issued (the
+  // loads complete in order; stores issued in between only make the wait stricter)
   auto wait_tile = [&](int later) {
-    if (HAS_N && wv == 0) {
-      if (later >= 2) wait_vm<2 * (2 * M::IPW + 1)>();
-      else if (later == 1) wait_vm<2 * M::IPW + 1>();
-      else wait_vm<0>();
-    } else {
-      if (later >= 2) wait_vm<2 * (2 * M::IPW)>();
-      else if (later == 1) wait_vm<2 * M::IPW>();
-      else wait_vm<0>();
-    }
+    if (later == 0) wait_vm<0>();
+    else if (HAS_N && wv == 0) wait_vm<2 * M::IPW + 1>();
+    else wait_vm<2 * M::IPW>();
   };
 
   issue(0);
@@ -653,10 +648,9 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       }
     }
   }
-  // tile 0 and the operands travel together; later tiles are issued once they are in
+  // tile 0 and the operands travel together; tile 1 is issued once they are in
   asm volatile("" ::"v"(olo[1][KS - 1]), "v"(nbq[1][3]));
   if (ntiles > 1) issue(1);
-  if (ntiles > 2) issue(2);
   const float cs = a.scale * kLog2e;
   const float ics = 1.f / cs;
 
@@ -816,11 +810,16 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
         if (i < lo || i >= hi || (!cand && i >= a.S && i < pend)) continue;
         const int64_t pos = cand ? pos0 + r : i < a.S ? i : i - a.M;
         const uint4 kc = r ? k1 : k0, vc = r ? v1 : v0;
-        float f[E];
-        unpack<bf16>(kc, f);
-        store_elems<TO, E>(Ko + pos * D + ch * E, f);
-        unpack<bf16>(vc, f);
-        store_elems<TO, E>(Vo + pos * D + ch * E, f);
+        if constexpr (std::is_same<TO, bf16>::value) {   // same type: the row's bytes as they are
+          *reinterpret_cast<uint4*>(Ko + pos * D + ch * E) = kc;
+          *reinterpret_cast<uint4*>(Vo + pos * D + ch * E) = vc;
+        } else {
+          float f[E];
+          unpack<bf16>(kc, f);
+          store_elems<TO, E>(Ko + pos * D + ch * E, f);
+          unpack<bf16>(vc, f);
+          store_elems<TO, E>(Vo + pos * D + ch * E, f);
+        }
         if (ch == 0) {
           no[pos] = r ? n1 : n0;
           so[pos] = (int32_t)i;
@@ -829,17 +828,20 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     }
   };
 
+  // Iteration t: tile t is computed, tile t - 1 merged, tile t + 1 is in flight and tile
+  // t + 2 goes into the slot of tile t - 2, which every wave finished reading (its compute
+  // and its merge) before this iteration's barrier.  A merge reads rows and counts that
+  // other waves loaded, so no slot is refilled between a barrier and a merge of it.
   for (int t = 0; t < ntiles; ++t) {
-    wait_tile(ntiles - 1 - t < 2 ? ntiles - 1 - t : 2);   // tile t landed
+    wait_tile(t + 1 < ntiles ? 1 : 0);   // tile t landed
     __syncthreads();
+    if (t + 2 < ntiles) issue(t + 2);
     if (MERGE && t > 0) {
       // the merge sits between two barriers of this workgroup: let it finish first
       __builtin_amdgcn_s_setprio(2);
       merge_tile(t - 1);
       __builtin_amdgcn_s_setprio(0);
-      wait_lds();   // its LDS reads are done before the ring slot is refilled
     }
-    if (t + 3 < ntiles) issue(t + 3);
     compute(t);
   }
   __syncthreads();
