@@ -93,3 +93,38 @@ def test_fused_round_against_oracle():
     for h in range(Hkv):
         check_round_slice(bufs, K, V, n, Qw, 0, h, N, S, R, M, 1 / math.sqrt(D), label=f"fused partial h{h}",
                           with_cos=False)
+
+
+def _random_cases(count, seed=2024):
+    """Seeded shapes over the fused pass's edges: chunks of one to a few tiles, ragged
+    ends, sinks and recent slots of any parity, counts on and off, every GQA ratio."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(count):
+        D = int(rs.choice([64, 128]))
+        Hkv = int(rs.randint(1, 4))
+        G = int(rs.choice([1, 2, 4, 8]))
+        W = int(rs.choice([1, 3, 8, 16, 32]))
+        if G * W > 128:
+            W = 128 // G
+        N = int(rs.choice([5, 33, 64, 65, 97, 130, 600, 2049, 5000]))
+        S = int(rs.randint(0, min(N, 40)))
+        R = int(rs.randint(0, min(N - S, 40) + 1))
+        frac = float(rs.choice([1.0, 0.5, 0.13, 0.0]))
+        counts = bool(rs.randint(2))
+        odt = torch.bfloat16 if rs.randint(2) else torch.float32
+        out.append((f"rand{i}-d{D}-h{Hkv}-g{G}-w{W}-n{N}-s{S}-r{R}-f{frac}", 1 + int(rs.randint(2)), Hkv, G * Hkv, D,
+                    N, W, S, R, frac, counts, odt))
+    return out
+
+
+RANDOM_CASES = _random_cases(24)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[c[0] for c in RANDOM_CASES])
+def test_fused_random_shapes_match_separate_calls(case):
+    name, B, Hkv, Hq, D, N, W, S, R, frac, counts, odt = case
+    print(f"\n[fused random] {name} B={B}", flush=True)
+    K, V, n, Qw = make_inputs(zlib.crc32(name.encode()) % 10000, B, Hkv, Hq, D, N, N, W, torch.bfloat16, counts)
+    M = int(round(frac * O.num_pairs(N, S, R)))
+    _compare(K, V, n, Qw, Hq, W, S, R, M, N, odt)
