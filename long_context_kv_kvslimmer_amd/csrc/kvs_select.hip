@@ -69,8 +69,20 @@ __device__ void replay_digits(const int32_t* ghist, int passes, uint32_t M, uint
   const int tid = threadIdx.x;
   prefix = 0;
   remaining = M;
-  for (int s = 0; s < passes; ++s) {
-    const uint32_t v = tid < 256 ? (uint32_t)ghist[s * 256 + 255 - tid] : 0u;
+  // every histogram count this thread needs, loaded before the first scan (one memory
+  // round trip instead of one per digit); threads past 256 and digits past `passes` read
+  // bin 0 of digit 0 and drop it
+  uint32_t hv[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bool ok = tid < 256 && s < passes;
+    hv[s] = (uint32_t)ghist[ok ? s * 256 + 255 - tid : 0];
+    if (!ok) hv[s] = 0u;
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s >= passes) break;
+    const uint32_t v = hv[s];
     int tot;
     const uint32_t x = (uint32_t)block_exclusive_scan<T>((int)v, &tot, lds) + v;   // keys with digit >= 255 - tid
     if (tid < 256 && x >= remaining && x - v < remaining) {
@@ -110,17 +122,24 @@ __global__ __launch_bounds__(kHistThreads) void sel_hist_kernel(SelArgs a, int p
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[2];
   __shared__ int lds[kHistThreads / 64];
+  // the keys are loaded first, so that their loads overlap the replay
+  const int64_t b0 = (int64_t)blockIdx.x * kHistBlock;
+  uint32_t keys[kHistKeys];
+#pragma unroll
+  for (int j = 0; j < kHistKeys; ++j) {
+    const int64_t p = b0 + j * kHistThreads + tid;
+    keys[j] = order_key(cs[p < a.P ? p : 0]);
+  }
   uint32_t prefix, remaining;
   replay_digits<kHistThreads>(st + a.hist_off, pass, (uint32_t)a.M, prefix, remaining, sh, lds);
   const uint32_t mask = pass == 0 ? 0u : 0xffffffffu << (32 - 8 * pass);
   const int shift = 24 - 8 * pass;
   hist[tid] = 0;
   __syncthreads();
-  const int64_t b0 = (int64_t)blockIdx.x * kHistBlock;
 #pragma unroll
   for (int j = 0; j < kHistKeys; ++j) {
     const int64_t p = b0 + j * kHistThreads + tid;
-    const uint32_t k = p < a.P ? order_key(cs[p]) : 0u;
+    const uint32_t k = keys[j];
     wave_hist_add(hist, p < a.P && (k & mask) == prefix, (k >> shift) & 255u);
   }
   __syncthreads();
@@ -137,13 +156,19 @@ __global__ __launch_bounds__(kHistThreads) void sel_count_kernel(SelArgs a) {
   const float* cs = a.cos + bh * a.P;
   __shared__ uint32_t sh[2];
   __shared__ int lds[kHistThreads / 64];
-  uint32_t tau, remaining;
-  replay_digits<kHistThreads>(st + a.hist_off, 4, (uint32_t)a.M, tau, remaining, sh, lds);
   const int64_t b0 = (int64_t)blockIdx.x * kHistBlock;
+  uint32_t keys[kHistKeys];   // loaded before the replay, as in the histogram pass
 #pragma unroll
   for (int j = 0; j < kHistKeys; ++j) {
     const int64_t p = b0 + j * kHistThreads + tid;
-    const uint32_t k = p < a.P ? order_key(cs[p]) : 0u;
+    keys[j] = order_key(cs[p < a.P ? p : 0]);
+  }
+  uint32_t tau, remaining;
+  replay_digits<kHistThreads>(st + a.hist_off, 4, (uint32_t)a.M, tau, remaining, sh, lds);
+#pragma unroll
+  for (int j = 0; j < kHistKeys; ++j) {
+    const int64_t p = b0 + j * kHistThreads + tid;
+    const uint32_t k = keys[j];
     const uint64_t eq = __ballot(p < a.P && k == tau);
     const uint64_t gt = __ballot(p < a.P && k > tau);
     const int64_t c = b0 / kChunkPairs + j * (kHistThreads / 64) + wv;
