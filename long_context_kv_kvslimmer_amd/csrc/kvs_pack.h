@@ -17,7 +17,11 @@ __device__ __forceinline__ uint4 pack_query_chunk(const PackP& pk, int64_t u, in
   return *reinterpret_cast<const uint4*>(qrow + lane * 8);
 }
 
-// As below, with the lane's query chunk (pack_query_chunk) already loaded.
+// The MFMA pass-2 operands of row u (as combine_kernel writes them): lane c < D / 8 of the
+// calling wave packs elements 8c .. 8c + 7 of the row, fetched from the lanes that hold
+// them (lane l holds elements l + 64 e in ov[e]), and stores qchunk, the lane's query
+// chunk (pack_query_chunk, loaded early by the caller so that its latency overlaps other
+// loads); lane 0 writes ||o||^2 and -lse log2 e.  All 64 lanes call it.
 template <int D>
 __device__ __forceinline__ void pack_row_wave_q(const PackP& pk, int64_t u, const float (&ov)[D / 64], float lse_u,
                                                 int lane, const uint4& qchunk) {
@@ -54,16 +58,6 @@ __device__ __forceinline__ void pack_row_wave_q(const PackP& pk, int64_t u, cons
     pk.qc[(bh * pk.nwb * 32 + q) * 2] = on;
     pk.qc[(bh * pk.nwb * 32 + q) * 2 + 1] = -lse_u * kLog2e;
   }
-}
-
-// The MFMA pass-2 operands of row u (as combine_kernel writes them): lane c < D / 8 of the
-// calling wave packs elements 8c .. 8c + 7 of the row, fetched from the lanes that hold
-// them (lane l holds elements l + 64 e in ov[e]); lane 0 writes ||o||^2 and -lse log2 e.
-// All 64 lanes call it.
-template <int D>
-__device__ __forceinline__ void pack_row_wave(const PackP& pk, int64_t u, const float (&ov)[D / 64], float lse_u,
-                                              int lane) {
-  pack_row_wave_q<D>(pk, u, ov, lse_u, lane, pack_query_chunk<D>(pk, u, lane));
 }
 
 }  // namespace kvs

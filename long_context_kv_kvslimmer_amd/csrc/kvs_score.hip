@@ -146,6 +146,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   const int64_t rs = D + 4;
   const float* r = part + u * nsplit * rs;
   const int d = tid % D, g = tid / D, ng = kCombineThreads / D;
+  // the query chunk of the operand pack does not depend on the splits: load it first
+  uint4 qch = make_uint4(0, 0, 0, 0);
+  if (pk.ops && tid < D / 8) {
+    const int64_t bh = u / pk.GW, q = u - bh * pk.GW;
+    const int64_t b = bh / pk.Hkv, hk = bh - b * pk.Hkv;
+    const bf16* qrow = static_cast<const bf16*>(pk.Qw) + ((b * pk.Hq + hk * pk.G) * (int64_t)pk.W + q) * D;
+    qch = *reinterpret_cast<const uint4*>(qrow + tid * 8);
+  }
   float2 ml[kCombineML];
 #pragma unroll
   for (int k = 0; k < kCombineML; ++k) {
@@ -215,8 +223,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
     const int nch = D / 8, KS = D / 32;
     float on = 0.f;
     if (tid < nch) {
-      const int64_t b = bh / pk.Hkv, hk = bh - b * pk.Hkv;
-      const bf16* qrow = static_cast<const bf16*>(pk.Qw) + ((b * pk.Hq + hk * pk.G) * (int64_t)pk.W + q) * D;
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
         hi[j] = pack_bf16x2(m0, m1);
         lo[j] = pack_bf16x2(m0 - bf16_lo(hi[j]), m1 - bf16_hi(hi[j]));
       }
-      pk.ops[pack_ops_index(bh, pk.nwb, q, 0, tid, KS)] = *reinterpret_cast<const uint4*>(qrow + tid * 8);
+      pk.ops[pack_ops_index(bh, pk.nwb, q, 0, tid, KS)] = qch;
       pk.ops[pack_ops_index(bh, pk.nwb, q, 1, tid, KS)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       pk.ops[pack_ops_index(bh, pk.nwb, q, 2, tid, KS)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
@@ -256,6 +262,8 @@ __global__ __launch_bounds__(64 * kCombineWaveUnits) void combine_wave_kernel(co
   const int64_t u = (int64_t)blockIdx.x * kCombineWaveUnits + (threadIdx.x >> 6);
   if (u >= units) return;   // whole waves leave; nothing below synchronises the workgroup
   const float* r = part + u * nsplit * rs;
+  // the pack's query chunk does not depend on the splits: load it with them
+  const uint4 qch = pk.ops ? pack_query_chunk<D>(pk, u, lane) : make_uint4(0, 0, 0, 0);
   const float2 ml = lane < nsplit ? *reinterpret_cast<const float2*>(r + lane * rs) : make_float2(-INFINITY, 0.f);
   float o[8][E];
 #pragma unroll
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(64 * kCombineWaveUnits) void combine_wave_kernel(co
   }
   const float lse_u = (M + __log2f(L)) * kLn2;
   if (lse && lane == 0) lse[u] = lse_u;
-  if (pk.ops) pack_row_wave<D>(pk, u, ov, lse_u, lane);
+  if (pk.ops) pack_row_wave_q<D>(pk, u, ov, lse_u, lane, qch);
 }
 
 // One wave per row: the MFMA pass-2 operands of window statistics the caller supplies
@@ -305,10 +313,11 @@ __global__ __launch_bounds__(64 * kCombineWaveUnits) void pack_kernel(const floa
   const int lane = threadIdx.x & 63;
   const int64_t u = (int64_t)blockIdx.x * kCombineWaveUnits + (threadIdx.x >> 6);
   if (u >= units) return;
+  const uint4 qch = pack_query_chunk<D>(pk, u, lane);   // in flight with the loads below
   float ov[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) ov[e] = O[u * D + lane + 64 * e];
-  pack_row_wave<D>(pk, u, ov, lse[u], lane);
+  pack_row_wave_q<D>(pk, u, ov, lse[u], lane, qch);
 }
 
 hipError_t launch_pack(const float* lse, const float* O, int64_t units, int D, const PackP& pk, hipStream_t st) {

@@ -162,22 +162,27 @@ def stream_check(cfg, dev, track, check_rounds, decode_heads, n_rounds):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_append_rows(dtype):
+@pytest.mark.parametrize("shape", [(2, 3, 64, 200, 80, 100, 5, 37), (1, 2, 128, 4000, 2600, 1203, 17, 2501)],
+                         ids=["small", "many-blocks"])
+def test_append_rows(dtype, shape):
     """kvs_append writes exactly the requested rows and counts, from a strided source view."""
     from long_context_kv_kvslimmer_amd import kvslim as L
+    B, H, D, cap, scap, at, frm, cnt = shape
     g = torch.Generator(device=DEV)
     g.manual_seed(5)
-    K = torch.randn(2, 3, 200, 64, generator=g, device=DEV).to(dtype)
-    V = torch.randn(2, 3, 200, 64, generator=g, device=DEV).to(dtype)
-    n = torch.full((2, 3, 200), 7, dtype=torch.int32, device=DEV)
-    big = torch.randn(2, 3, 80, 64, generator=g, device=DEV).to(dtype)
-    Ks, Vs = big[:, :, :50], big[:, :, 30:80].contiguous()   # Ks: a view with capacity 80
+    K = torch.randn(B, H, cap, D, generator=g, device=DEV).to(dtype)
+    V = torch.randn(B, H, cap, D, generator=g, device=DEV).to(dtype)
+    n = torch.full((B, H, cap), 7, dtype=torch.int32, device=DEV)
+    big = torch.randn(B, H, scap, D, generator=g, device=DEV).to(dtype)
+    ns = frm + cnt + 3                                         # source rows described
+    Ks = big[:, :, :ns]                                        # a view with a larger capacity
+    Vs = torch.randn(B, H, ns, D, generator=g, device=DEV).to(dtype)
     Ke, Ve, ne = K.clone(), V.clone(), n.clone()
-    Ke[:, :, 100:137] = Ks[:, :, 5:42]
-    Ve[:, :, 100:137] = Vs[:, :, 5:42]
-    ne[:, :, 100:137] = 1
-    Vs_view = torch.empty_like(big)[:, :, :50]
+    Ke[:, :, at:at + cnt] = Ks[:, :, frm:frm + cnt]
+    Ve[:, :, at:at + cnt] = Vs[:, :, frm:frm + cnt]
+    ne[:, :, at:at + cnt] = 1
+    Vs_view = torch.empty_like(big)[:, :, :ns]
     Vs_view.copy_(Vs)
-    L.kvs_append(L.cache_desc(K, 6), K, V, n, 100, L.cache_desc(Ks, 6, 50), Ks, Vs_view, 5, 37)
+    L.kvs_append(L.cache_desc(K, 2 * H), K, V, n, at, L.cache_desc(Ks, 2 * H, ns), Ks, Vs_view, frm, cnt)
     torch.cuda.synchronize()
     assert torch.equal(K, Ke) and torch.equal(V, Ve) and torch.equal(n, ne)
