@@ -169,7 +169,8 @@ __device__ __forceinline__ uint32_t order_key(float c) {
 // g11 = sum ||c11||, g12 = sum ||c12||, g22 = sum ||c22|| (KVSlimmer deep-dive, section
 // 数学主线四, closed-form k*), with the plain average of section 数学主线二 when the
 // denominator is not finite or not clearly positive.  Explicit fma pins the rounding; one
-// division forms 1 / A for both weights.
+// hardware reciprocal (v_rcp_f32, within 1 ulp; every path calls this routine, so they all
+// round alike) forms 1 / A for both weights.
 __device__ __forceinline__ void closed_form_weights(float g11, float g12, float g22, float& w0, float& w1) {
   const float A = __builtin_fmaf(-2.f, g12, g11) + g22;
   const float scale = __builtin_fmaf(2.f, g12, g11 + g22);
@@ -177,7 +178,7 @@ __device__ __forceinline__ void closed_form_weights(float g11, float g12, float 
     w0 = 0.5f;
     w1 = 0.5f;
   } else {
-    const float inv = 1.f / A;
+    const float inv = __builtin_amdgcn_rcpf(A);
     w0 = (g11 - g12) * inv;
     w1 = (g22 - g12) * inv;
   }
@@ -185,7 +186,8 @@ __device__ __forceinline__ void closed_form_weights(float g11, float g12, float 
 
 // One merged slot, E elements of it: k* = w0 k_m + w1 k_{m+1}; v* = the count-weighted
 // mean, with weights n_m / (n_m + n_{m+1}) and n_{m+1} / (n_m + n_{m+1}) formed once per
-// pair from one division (no counts: both weights are 1/2 exactly).
+// pair from one hardware reciprocal (exact for a power-of-two total, so without counts both
+// weights are 1/2 exactly).
 template <int E>
 __device__ __forceinline__ void merge_keys(const float* kf0, const float* kf1, float w0, float w1, float* ko) {
 #pragma unroll
@@ -194,7 +196,7 @@ __device__ __forceinline__ void merge_keys(const float* kf0, const float* kf1, f
 
 template <int E>
 __device__ __forceinline__ void merge_values(const float* vf0, const float* vf1, int n0, int n1, float* vo) {
-  const float inv = 1.f / (float)(n0 + n1);
+  const float inv = __builtin_amdgcn_rcpf((float)(n0 + n1));
   const float u0 = (float)n0 * inv, u1 = (float)n1 * inv;
 #pragma unroll
   for (int e = 0; e < E; ++e) vo[e] = __builtin_fmaf(u0, vf0[e], u1 * vf1[e]);
