@@ -521,8 +521,20 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
   __shared__ __attribute__((aligned(1024))) uint8_t kr[kRing2 * M::TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t vr[kRing2 * M::TILEB];
   __shared__ int32_t nr[kRing2 * kT2];            // slot counts as loaded (LDS-row order)
-  __shared__ float red_s[kW2 * kChunk2Max];       // per-wave sums over its queries, per slot
-  __shared__ float red_x[kW2 * (kChunk2Max / 2)]; // and per candidate pair
+  // per-wave sums over the wave's queries, grouped by aligned slot pair j of the chunk:
+  // red[(3 j + k) kW2 + w], k = 0 the even slot, 1 the odd slot, 2 the pair term, so the
+  // four waves' values of one quantity are one 16-byte read
+  static_assert(kW2 == 4, "one float4 per quantity");
+  __shared__ __attribute__((aligned(16))) float red[(kChunk2Max / 2) * 3 * kW2];
+  // the four waves' values added in wave order (the order every reader uses)
+  auto sum_waves = [](const float4& v) {
+    float x = 0.f;
+    x += v.x;
+    x += v.y;
+    x += v.z;
+    x += v.w;
+    return x;
+  };
   // partial rounds: selection flags of the 64-pair compaction chunks the workgroup's pairs
   // fall in, and the selected pairs before each of those chunks
   constexpr int kSelChunks = kChunk2Max / 2 / kChunkPairs + 1;
@@ -727,9 +739,10 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     gso = sum_xor32(sum_xor16(gso));
     gx = sum_xor32(sum_xor16(gx));
     if (g4 == 0) {
-      red_s[wv * kChunk2Max + t * kT2 + 2 * n16] = gse;
-      red_s[wv * kChunk2Max + t * kT2 + 2 * n16 + 1] = gso;
-      red_x[wv * (kChunk2Max / 2) + t * (kT2 / 2) + n16] = gx;
+      float* rp = red + (t * (kT2 / 2) + n16) * 3 * kW2 + wv;
+      rp[0] = gse;
+      rp[kW2] = gso;
+      rp[2 * kW2] = gx;
     }
   };
 
@@ -773,14 +786,8 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       pos0 = a.S + (m0 - a.S) / 2;
     }
     if (mrg) {
-      const int ls = tt * kT2 + 2 * pn;
-      float g0 = 0.f, g1 = 0.f, gx = 0.f;
-#pragma unroll
-      for (int w = 0; w < kW2; ++w) {
-        g0 += red_s[w * kChunk2Max + ls];
-        g1 += red_s[w * kChunk2Max + ls + 1];
-        gx += red_x[w * (kChunk2Max / 2) + tt * (kT2 / 2) + pn];
-      }
+      const float4* rq = reinterpret_cast<const float4*>(red + (tt * (kT2 / 2) + pn) * 3 * kW2);
+      const float g0 = sum_waves(rq[0]), g1 = sum_waves(rq[1]), gx = sum_waves(rq[2]);
       float w0, w1;
       closed_form_weights(g0, gx, g1, w0, w1);
       {   // keys, then values: half the live temporaries
@@ -850,9 +857,8 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
   // per-slot totals of the chunk -> global (several query blocks accumulate)
   const bool acc = gridDim.x > (unsigned)(BH * nsplit);
   for (int64_t s = lo + tid; s < hi; s += kW2 * 64) {
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kW2; ++w) v += red_s[w * kChunk2Max + (s - c0)];
+    const int64_t ls = s - c0;
+    const float v = sum_waves(reinterpret_cast<const float4*>(red)[(ls >> 1) * 3 + (ls & 1)]);
     if (acc) atomicAdd(&a.g_self[bh * a.N + s], v);
     else a.g_self[bh * a.N + s] = v;
   }
@@ -860,9 +866,7 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     const int64_t m0 = c0 + 2 * pp;
     const int64_t p = (m0 - a.S) / 2;
     if (m0 >= a.S && m0 >= lo && m0 + 1 < hi && p < a.P) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kW2; ++w) v += red_x[w * (kChunk2Max / 2) + pp];
+      const float v = sum_waves(reinterpret_cast<const float4*>(red)[pp * 3 + 2]);
       if (acc) atomicAdd(&a.g_cross[bh * a.P + p], v);
       else a.g_cross[bh * a.P + p] = v;
     }
