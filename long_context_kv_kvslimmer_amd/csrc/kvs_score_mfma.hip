@@ -122,6 +122,7 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
   // K tiles, then V tiles; after the loop the whole ring holds the records being merged
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kGroups * kRing2 * M::TILEB];
   __shared__ __attribute__((aligned(16))) int32_t nr[kGroups * kRing2 * kT2];
+  __shared__ __attribute__((aligned(16))) float lgb[kGroups * kRing2 * kT2];   // count bias per slot
   __shared__ float xm[2 * kQB];
   static_assert(kQB * (D + 4) * 4 <= 2 * kGroups * kRing2 * M::TILEB, "record staging exceeds the ring");
   uint8_t* const kr = ring;
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
   uint8_t* kr_g = kr + grp * kRing2 * M::TILEB;
   uint8_t* vr_g = vr + grp * kRing2 * M::TILEB;
   int32_t* nr_g = nr + grp * kRing2 * kT2;
+  float* lgb_g = lgb + grp * kRing2 * kT2;
 
   // K tile j (with its counts) and V tile j go to ring slot j % 4 of their own ring.  The
   // loop below issues K(t + 3) and V(t + 2) at the top of iteration t, in that order: V is
@@ -184,6 +186,17 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
       dma16(rv, lds_addr(vr_g + buf * M::TILEB + u * 1024), (uint32_t)((t0 + R - lo) * M::ROWB) + (uint32_t)(c << 4));
     }
   };
+  // The count bias of tile t's slots, log2 n (-inf outside the group's range), computed once
+  // per slot by the wave that loads the counts (its own loads have landed) and read by
+  // every wave after the next barrier.
+  auto count_bias = [&](int t) {
+    if (HAS_N && gw == 0 && lane < kT2) {
+      const int buf = t % kRing2;
+      const int64_t s = g0 + (int64_t)t * kT2 + lane;
+      lgb_g[buf * kT2 + lane] = (s >= lo && s < hi) ? __log2f((float)nr_g[buf * kT2 + lane]) : -INFINITY;
+    }
+  };
+
   // Wait at the top of iteration t until K(t + 1) has landed (and with it every earlier
   // load, V(t - 1) included); issued after K(t + 1) are V(t), K(t + 2) if it exists, and
   // V(t + 1).  In the last iteration everything is awaited (V(t) feeds the final product).
@@ -214,6 +227,7 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
   bf16x8_t qop[KS];
   load_rows32<D>(Qp, a.GW, q, qop);
   asm volatile("" ::"v"(qop[KS - 1]));
+  if (nt > 0) count_bias(0);   // K(0) and its counts came before the queries
   if (nt > 2) issue_k(2);
   if (nt > 1) issue_v(1);
 
@@ -264,17 +278,24 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
 #pragma unroll
       for (int i = 0; i < 16; ++i) e[i] = st[i];
       sc = cs;
+    } else if (HAS_N) {
+      sc = 1.f;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const float4 lg = *reinterpret_cast<const float4*>(lgb_g + buf * kT2 + 8 * k4 + 4 * h);
+        e[4 * k4 + 0] = __builtin_fmaf(st[4 * k4 + 0], cs, lg.x);
+        e[4 * k4 + 1] = __builtin_fmaf(st[4 * k4 + 1], cs, lg.y);
+        e[4 * k4 + 2] = __builtin_fmaf(st[4 * k4 + 2], cs, lg.z);
+        e[4 * k4 + 3] = __builtin_fmaf(st[4 * k4 + 3], cs, lg.w);
+      }
     } else {
       sc = 1.f;
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
-        int4 n4 = make_int4(1, 1, 1, 1);
-        if (HAS_N) n4 = *reinterpret_cast<const int4*>(nr_g + buf * kT2 + 8 * k4 + 4 * h);
-        const int nn[4] = {n4.x, n4.y, n4.z, n4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t s = t0 + 8 * k4 + 4 * h + r;
-          const float lg = (s >= lo && s < hi) ? (HAS_N ? __log2f((float)nn[r]) : 0.f) : -INFINITY;
+          const float lg = (s >= lo && s < hi) ? 0.f : -INFINITY;
           e[4 * k4 + r] = __builtin_fmaf(st[4 * k4 + r], cs, lg);
         }
       }
@@ -355,6 +376,7 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     if (act) wait_top(t);
     __syncthreads();
     if (act) {
+      if (t + 1 < nt) count_bias(t + 1);   // K(t + 1) and its counts have landed
       if (t + 3 < nt) issue_k(t + 3);
       if (t + 2 < nt) issue_v(t + 2);
       if (do_cos) cosines(t);
