@@ -16,6 +16,8 @@
 //
 // Pass 1 also writes the adjacent-key cosine (the shared pair_cos routine on LDS rows in
 // row layout), so the merge pass can recompute bit-identical values.
+#include <type_traits>
+
 #include "kvs_common.h"
 #include "kvs_dma.h"
 #include "kvs_pack.h"
@@ -517,13 +519,13 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
 // A workgroup is four waves (128 queries) over one slot chunk; two workgroups share a CU.
 // K and V arrive by 16-byte buffer loads written straight into LDS (no register staging)
 // as 32-slot tiles in a four-deep ring: tile t is computed while tile t - 1 is merged and
-// tiles t + 1, t + 2 are in flight.  A tile's LDS row R holds slot 2 (R % 16) + R / 16 (even slots first).  Rows are
-// unpadded; the 16-byte chunks of row r sit at position c ^ swz(r), which keeps the MFMA
-// operand reads free of bank conflicts.  ||v||^2 and v_m . v_{m+1} come from the
-// diagonals of Gram products of the V operand registers, so a tile needs no setup pass
-// and one barrier.  Each wave keeps its per-slot sums in LDS; the four waves' sums are
-// added and written once, at the end, so the loop issues no global stores.  The query
-// operands come pre-packed in lane order from the log-sum-exp combine.
+// tiles t + 1, t + 2 are in flight.  A tile's LDS row R holds slot 2 (R % 16) + R / 16
+// (even slots first).  Rows are unpadded; the 16-byte chunks of row r sit at position
+// c ^ swz(r), which keeps the MFMA operand reads free of bank conflicts.  ||v||^2 and
+// v_m . v_{m+1} come from the diagonals of Gram products of the V operand registers, so a
+// tile needs no setup pass and one barrier.  Each wave keeps its per-slot sums in LDS; the
+// four waves' sums are added and written once, at the end, so the loop issues no global
+// stores.  The query operands come pre-packed in lane order from the log-sum-exp combine.
 constexpr int kChunk2Max = 512;      // pass-2 slots per workgroup at most
 
 // LDS row R of a tile holds slot 2 (R % 16) + R / 16 of the tile.
