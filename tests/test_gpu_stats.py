@@ -12,7 +12,7 @@ import torch
 
 from oracle import kvs_oracle as O
 from tests.parity import REL_TOL, host, maxrel
-from tests.test_gpu_fused import CASES
+from tests.test_gpu_fused import CASES, RANDOM_CASES
 from tests.test_gpu_parity import make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -37,12 +37,33 @@ def test_given_stats_match_score_merge(case, frac):
     got = pipeline.alloc_round(K, Hq, W, S, R, M, n_slots=N, out_dtype=odt)
     pipeline.run_round_given_stats(K, V, n, Qw, ref.lse, ref.O, Hq, W, S, R, M, got, n_slots=N)
     torch.cuda.synchronize()
+    _compare_outputs(got, ref, P, T)
+
+
+def _compare_outputs(got, ref, P, T):
     _same(got.g_self, ref.g_self, "g_self")
     _same(got.g_cross[..., :P], ref.g_cross[..., :P], "g_cross")
     _same(got.K[:, :, :T], ref.K[:, :, :T], "K_out")
     _same(got.V[:, :, :T], ref.V[:, :, :T], "V_out")
     _same(got.n[:, :, :T], ref.n[:, :, :T], "n_out")
     _same(got.src[:, :, :T], ref.src[:, :, :T], "src_out")
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[c[0] for c in RANDOM_CASES])
+def test_given_stats_random_shapes(case):
+    """The seeded random shapes of the fused-call tests, through the given-statistics call."""
+    from long_context_kv_kvslimmer_amd import pipeline
+    name, B, Hkv, Hq, D, N, W, S, R, frac, counts, odt = case
+    print(f"\n[stats random] {name} B={B}", flush=True)
+    K, V, n, Qw = make_inputs(zlib.crc32(name.encode()) % 10000, B, Hkv, Hq, D, N, N, W, torch.bfloat16, counts)
+    P = O.num_pairs(N, S, R)
+    M = int(round(frac * P))
+    ref = pipeline.alloc_round(K, Hq, W, S, R, M, n_slots=N, out_dtype=odt)
+    pipeline.run_round_fused(K, V, n, Qw, Hq, W, S, R, M, ref, n_slots=N)
+    got = pipeline.alloc_round(K, Hq, W, S, R, M, n_slots=N, out_dtype=odt)
+    pipeline.run_round_given_stats(K, V, n, Qw, ref.lse, ref.O, Hq, W, S, R, M, got, n_slots=N)
+    torch.cuda.synchronize()
+    _compare_outputs(got, ref, P, N - M)
 
 
 @pytest.mark.parametrize("frac", [1.0, 0.35])
