@@ -52,6 +52,7 @@ def _compare(K, V, n, Qw, Hq, W, S, R, M, N, odt):
     _same(fused.V[:, :, :T], ref.V[:, :, :T], "V_out")
     _same(fused.n[:, :, :T], ref.n[:, :, :T], "n_out")
     _same(fused.src[:, :, :T], ref.src[:, :, :T], "src_out")
+    return fused
 
 
 @pytest.mark.parametrize("frac", [1.0, 0.29, 0.0])
@@ -126,5 +127,11 @@ def test_fused_random_shapes_match_separate_calls(case):
     name, B, Hkv, Hq, D, N, W, S, R, frac, counts, odt = case
     print(f"\n[fused random] {name} B={B}", flush=True)
     K, V, n, Qw = make_inputs(zlib.crc32(name.encode()) % 10000, B, Hkv, Hq, D, N, N, W, torch.bfloat16, counts)
-    M = int(round(frac * O.num_pairs(N, S, R)))
-    _compare(K, V, n, Qw, Hq, W, S, R, M, N, odt)
+    P = O.num_pairs(N, S, R)
+    M = int(round(frac * P))
+    fused = _compare(K, V, n, Qw, Hq, W, S, R, M, N, odt)
+    # full and empty rounds (no selection to disagree on near a tie) also against the oracle
+    if M in (0, P) and N <= 2049:
+        for b, h in ((0, 0), (B - 1, Hkv - 1)):
+            check_round_slice(fused, K, V, n, Qw, b, h, N, S, R, M, 1 / math.sqrt(D), label=f"{name} b{b} h{h}",
+                              with_cos=False)
