@@ -81,7 +81,7 @@ typedef struct {
 } kvs_cache;
 
 typedef struct {
-  int32_t window;      /* W: observation-window queries per query head */
+  int32_t window;      /* W: observation-window queries per query head, 1..65536 */
   int64_t n_sink;      /* S: leading slots never merged */
   int64_t n_recent;    /* R: trailing slots never merged */
   int64_t n_merge;     /* M: pairs merged in this round, the same for every (b, h); 0 <= M <= P */

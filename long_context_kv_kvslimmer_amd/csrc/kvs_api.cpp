@@ -63,9 +63,12 @@ kvs_status check_cache(const kvs_cache* c, int dtype, kvs::Shape& s) {
   return KVS_OK;
 }
 
+constexpr int32_t kMaxWindow = 65536;   // keeps every query-indexed grid and workspace size in range
+
 kvs_status check_round(const kvs_round* r, const kvs::Shape& s, kvs::RoundP& rp, bool need_window) {
   if (!r) return fail(KVS_ERR_NULL, "round is NULL");
-  if (need_window && r->window < 1) return fail(KVS_ERR_SHAPE, "window must be >= 1");
+  if (need_window && (r->window < 1 || r->window > kMaxWindow))
+    return fail(KVS_ERR_SHAPE, "window must be in [1, %d]", kMaxWindow);
   if (r->n_sink < 0 || r->n_recent < 0) return fail(KVS_ERR_SHAPE, "n_sink and n_recent must be >= 0");
   if (!std::isfinite(r->sm_scale)) return fail(KVS_ERR_SHAPE, "sm_scale is not finite");
   rp.W = r->window;

@@ -92,6 +92,7 @@ def test_score_validation(L):
     assert _score(L, _cache(), L.round_desc(32, 0, 32, 16369, 0.1)) == L.KVS_ERR_INFEASIBLE
     assert _score(L, _cache(), L.round_desc(32, 0, 32, -1, 0.1)) == L.KVS_ERR_INFEASIBLE
     assert _score(L, _cache(), L.round_desc(0, 0, 32, 10, 0.1)) == L.KVS_ERR_SHAPE
+    assert _score(L, _cache(), L.round_desc(65537, 0, 32, 10, 0.1)) == L.KVS_ERR_SHAPE
     assert _score(L, _cache(N=0), L.round_desc(32, 0, 0, 0, 0.1)) == L.KVS_ERR_SHAPE
     assert _score(L, _cache(), L.round_desc(32, 0, 32, 10, float("nan"))) == L.KVS_ERR_SHAPE
     assert "n_merge" in L.last_error() or "sm_scale" in L.last_error()
