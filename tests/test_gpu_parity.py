@@ -71,6 +71,45 @@ def test_round_parity(case):
             check_round_slice(bufs, K, V, n, Qw, b, h, N, S, R, M, 1 / math.sqrt(D), label=f"{name} b{b} h{h}")
 
 
+def _random_partial_cases(count, seed=7):
+    """Seeded partial rounds over small caches: the one-workgroup selection at several key
+    counts per thread, sinks and recent slots of any parity, counts on and off."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(count):
+        D = int(rs.choice([64, 128]))
+        Hkv = int(rs.randint(1, 3))
+        G = int(rs.choice([1, 2, 4]))
+        W = int(rs.choice([2, 8, 16]))
+        N = int(rs.choice([70, 257, 800, 1500, 3000]))
+        S = int(rs.randint(0, 33))
+        R = int(rs.randint(0, 33))
+        frac = float(rs.choice([0.05, 0.3, 0.7, 0.95]))
+        counts = bool(rs.randint(2))
+        out.append((f"prand{i}-d{D}-h{Hkv}-g{G}-w{W}-n{N}-s{S}-r{R}-f{frac}", Hkv, G * Hkv, D, N, W, S, R, frac,
+                    counts))
+    return out
+
+
+PARTIAL_RANDOM = _random_partial_cases(12)
+
+
+@pytest.mark.parametrize("case", PARTIAL_RANDOM, ids=[c[0] for c in PARTIAL_RANDOM])
+def test_round_parity_random_partial(case):
+    """The separate calls (selection flags out) against the oracle on every slice, the
+    selection bit-exact outside the tie margin."""
+    from long_context_kv_kvslimmer_amd import pipeline
+    name, Hkv, Hq, D, N, W, S, R, frac, counts = case
+    print(f"\n[parity random] {name}", flush=True)
+    K, V, n, Qw = make_inputs(zlib.crc32(name.encode()) % 10000, 1, Hkv, Hq, D, N, N, W, torch.bfloat16, counts)
+    P = O.num_pairs(N, S, R)
+    M = int(round(frac * P))
+    bufs = pipeline.merge_round(K, V, n, Qw, Hq, W, S, R, M, n_slots=N, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for h in range(Hkv):
+        check_round_slice(bufs, K, V, n, Qw, 0, h, N, S, R, M, 1 / math.sqrt(D), label=f"{name} h{h}")
+
+
 def test_bf16_output_is_rne_of_fp32_output_and_deterministic():
     from long_context_kv_kvslimmer_amd import pipeline
     K, V, n, Qw = make_inputs(7, 1, 2, 8, 128, 2048, 2048, 8, torch.bfloat16, True)
