@@ -302,7 +302,6 @@ def copy_calibration(dev):
 
 def cpu_baseline(cfg, K, V, Qw, heads=2):
     """The oracle as it stands, on `heads` KV heads of one layer (one thread)."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import kvs_oracle as O

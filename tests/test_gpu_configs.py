@@ -10,7 +10,6 @@ the oracle on the very inputs the GPU consumed in that round.
 """
 import math
 
-import numpy as np
 import pytest
 import torch
 

@@ -4,7 +4,6 @@ Each test checks an oracle function against something that is not the oracle
 itself: finite differences, brute-force minimisation, library routines,
 closed forms, exact invariants, or numbers the pages print (tests/golden/).
 """
-import itertools
 import json
 import math
 import os
