@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kSelThreads) void select_onewg_kernel(SelArgs a) {
   int32_t* st = a.st + bh * a.sel_stride;
   const float* cs = a.cos + bh * a.P;
   constexpr int NCH = KPT * (kSelThreads / 64);   // chunks the keys cover
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[4][256];   // one histogram per digit, cleared once
   __shared__ uint32_t sh[2];
   __shared__ int lds[kSelThreads / 64];
   __shared__ int eq_c[NCH], gt_c[NCH];
@@ -285,29 +285,48 @@ __global__ __launch_bounds__(kSelThreads) void select_onewg_kernel(SelArgs a) {
     k[j] = p < a.P ? order_key(cs[p]) : 0u;
   }
   uint32_t prefix = 0, remaining = (uint32_t)a.M;
+  static_assert(kSelThreads == 4 * 256, "one thread per histogram bin");
+  reinterpret_cast<uint32_t*>(hist)[tid] = 0;
+  __syncthreads();
   for (int s = 0; s < 4; ++s) {
     const uint32_t mask = s == 0 ? 0u : 0xffffffffu << (32 - 8 * s);
     const int shift = 24 - 8 * s;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int64_t p = (int64_t)j * kSelThreads + tid;
-      wave_hist_add(hist, p < a.P && (k[j] & mask) == prefix, (k[j] >> shift) & 255u);
+      wave_hist_add(hist[s], p < a.P && (k[j] & mask) == prefix, (k[j] >> shift) & 255u);
     }
     __syncthreads();
-    // digit s: the largest d whose count of keys >= d reaches `remaining`
-    const uint32_t v = tid < 256 ? hist[255 - tid] : 0u;
-    int tot;
-    const uint32_t x = (uint32_t)block_exclusive_scan<kSelThreads>((int)v, &tot, lds) + v;
-    if (tid < 256 && x >= remaining && x - v < remaining) {
-      sh[0] = prefix | ((uint32_t)(255 - tid) << shift);
-      sh[1] = remaining - (x - v);
+    // digit s: the largest d whose count of keys >= d reaches `remaining`; wave 0 alone,
+    // lane l holding digits 255 - 4 l .. 252 - 4 l (counts of keys >= d by a wave scan)
+    if (wv == 0) {
+      uint32_t v[4], c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = hist[s][255 - 4 * lane - j];
+      c[0] = v[0];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) c[j] = c[j - 1] + v[j];
+      uint32_t x = c[3];   // inclusive scan of the lane totals
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, off, 64);
+        if (lane >= off) x += y;
+      }
+      const uint32_t before = x - c[3];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t xj = before + c[j];
+        if (xj >= remaining && xj - v[j] < remaining) {
+          sh[0] = prefix | ((uint32_t)(255 - 4 * lane - j) << shift);
+          sh[1] = remaining - (xj - v[j]);
+        }
+      }
     }
     __syncthreads();
+    // sh is rewritten only after the next digit's barrier, which every thread reaches after
+    // reading it here
     prefix = sh[0];
     remaining = sh[1];
-    __syncthreads();
   }
   const uint32_t tau = prefix;
   // per-chunk counts of keys equal to and above tau
