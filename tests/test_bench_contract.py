@@ -1,0 +1,26 @@
+"""CPU: the parts of bench.py's contract that need no GPU."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode != 0
+    assert "--gpus 2 is not supported" in (r.stdout + r.stderr)
+
+
+def test_counter_summary_is_machine_readable():
+    """The committed HBM-counter summary carries the sources digest and per-kernel bytes the
+    bench reads back (the value is reported only while the digest matches the sources)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    lines = open(bench.TRAFFIC_FILE).read().splitlines()
+    vals = dict(l.strip("` ").split(" = ", 1) for l in lines if l.startswith("`") and " = " in l)
+    assert len(vals["sources"]) == 16
+    assert int(vals["traffic_bytes[score_pass2_merge]"]) > 0
+    got = bench.recorded_traffic("score_pass2_merge")
+    assert got is None or got == int(vals["traffic_bytes[score_pass2_merge]"])
