@@ -52,8 +52,8 @@ def kernel_bytes(N, H, D, P, T, GW, has_n=False, elt=2):
 # rocprofv3 kernel names -> the labels the library gives its launches
 KERNEL_LABELS = (("p1_mfma_kernel", "score_pass1"), ("pass1_valu_kernel", "score_pass1"),
                  ("p2_mfma_kernel", "score_pass2"), ("pass2_valu_kernel", "score_pass2"),
-                 ("combine_kernel", "combine"), ("fill_zero_kernel", "fill_zero"), ("pair_cos_kernel", "pair_cos"),
-                 ("combine_wave_kernel", "combine"), ("select_fixed_kernel", "select"),
+                 ("combine_kernel", "combine"), ("pair_cos_kernel", "pair_cos"),
+                 ("combine_wave_kernel", "combine"), ("qsum_kernel", "qsum"), ("select_fixed_kernel", "select"),
                  ("select_small_kernel", "select"), ("sel_clear_kernel", "select"), ("sel_hist_kernel", "select"),
                  ("sel_count_kernel", "select"), ("sel_final_kernel", "select"), ("append_kernel", "append"),
                  ("pack_kernel", "pack"), ("exact_e_kernel", "exact_e"), ("spectral_proj_kernel", "spectral_proj"),
@@ -159,15 +159,15 @@ def summarize_trace(stats_csv, bench_json, cmd):
             c, t = rows.get(lab, (0, 0.0))
             rows[lab] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
     line = json.loads([l for l in open(bench_json).read().splitlines() if l.startswith("{")][-1])
-    ev = line.get("kernels_warmup_marked", {})
+    ev = line.get("kernels_ranked", {})
     out = ["# Kernel durations, C2 layer (32K ctx, 8x128 KV heads, bf16)", "", "Made by:", "", "```", cmd, "```",
-           "", "rocprofv3 averages over every launch in the run; HIP-event averages over the marked warm-up "
-           "steps (every kernel marked).", "",
-           "| kernel | launches | rocprofv3 avg us | HIP-event avg us | algorithmic MB | GB/s (events) |",
+           "", "rocprofv3 averages over every launch in the run; HIP-event medians over the ranking steps (every "
+           "launch marked, after the warm-up).", "",
+           "| kernel | launches | rocprofv3 avg us | HIP-event median us | algorithmic MB | GB/s (events) |",
            "|---|---:|---:|---:|---:|---:|"]
     for lab, (c, t) in sorted(rows.items(), key=lambda kv: -kv[1][1]):
         e = ev.get(lab, {})
-        out.append(f"| {lab} | {c} | {t / c / 1e3:.2f} | {e.get('avg_ms', float('nan')) * 1e3:.2f} | "
+        out.append(f"| {lab} | {c} | {t / c / 1e3:.2f} | {e.get('median_ms', float('nan')) * 1e3:.2f} | "
                    f"{e.get('algorithmic_MB', 0)} | {e.get('GBps')} |")
     out += ["", f"ms_per_step {line['ms_per_step']}, value {line['value']} {line['unit']}, roofline "
             f"{json.dumps(line['roofline'])}"]
@@ -300,26 +300,107 @@ def copy_calibration(dev):
     del src, dst
 
 
-def cpu_baseline(cfg, K, V, Qw, heads=2):
-    """The oracle as it stands, on `heads` KV heads of one layer (one thread)."""
+def cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, K, V, Qw, q):
+    """The oracle as it stands on the whole C2 layer: every KV head's merge round and one
+    decode query over its merged cache.  The heads are independent slices, so they run on
+    a pool of worker threads (one per host core the process may use, at most one per head),
+    each with one BLAS thread."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from threadpoolctl import threadpool_limits
 
     from oracle import kvs_oracle as O
     G = cfg.group
     M = cfg.rounds[0]
+    scale = 1 / math.sqrt(cfg.head_dim)
+    heads = cfg.kv_heads
+    slices = []
+    for h in range(heads):
+        slices.append((K[0, h].double().cpu().numpy(), V[0, h].double().cpu().numpy(),
+                       Qw[0, h * G:(h + 1) * G].double().cpu().numpy().reshape(-1, cfg.head_dim),
+                       q[0, h * G].double().cpu().numpy()))
+
+    def one(s):
+        Ks, Vs, Qs, qd = s
+        r = O.merge_round(Ks, Vs, None, Qs, scale, cfg.n_sink, cfg.n_recent, M)
+        O.decode(r.K, r.V, r.n, qd, scale)
+
+    workers = max(1, min(heads, len(os.sched_getaffinity(0))))
     t0 = time.perf_counter()
     with threadpool_limits(1):
-        for h in range(heads):
-            Ks = K[0, h].double().cpu().numpy()
-            Vs = V[0, h].double().cpu().numpy()
-            Qs = Qw[0, h * G:(h + 1) * G].double().cpu().numpy().reshape(-1, cfg.head_dim)
-            r = O.merge_round(Ks, Vs, None, Qs, 1 / math.sqrt(cfg.head_dim), cfg.n_sink, cfg.n_recent, M)
-            O.decode(r.K, r.V, r.n, Qs[0], 1 / math.sqrt(cfg.head_dim))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, slices))
     dt = time.perf_counter() - t0
-    tokens = cfg.n_slots * heads / cfg.kv_heads        # share of the layer's token positions
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} of {cfg.kv_heads} KV heads of one C2 layer (N={cfg.n_slots}), merge round + "
-                      f"one decode query, fp64 NumPy, 1 BLAS thread, {dt:.1f} s"}
+    tokens = cfg.batch * cfg.n_slots
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cores_available": len(os.sched_getaffinity(0)),
+            "sample": f"the whole C2 layer: all {heads} KV heads (N={cfg.n_slots}, merge of {M} pairs) plus one "
+                      f"decode query per KV head over its merged cache, fp64 NumPy, {workers} worker threads "
+                      f"(one KV head each, one BLAS thread each; the oracle's Python-level loops hold the "
+                      f"interpreter lock), {dt:.1f} s"}
+
+
+def gpu_clock_info():
+    """Peak shader clock (HIP device attribute, kHz -> MHz) and, where the driver's sysfs
+    table is readable, the current shader clock level; ROCm and HIP versions."""
+    import ctypes
+    info = {"gpu_peak_sclk_MHz": None, "gpu_sclk_now": None, "rocm_version": None, "hip_runtime": None}
+    try:
+        import torch
+        info["hip_runtime"] = torch.version.hip
+        lib = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if lib.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:     # hipDeviceAttributeClockRate
+            info["gpu_peak_sclk_MHz"] = v.value // 1000
+    except (OSError, AttributeError):
+        pass
+    try:
+        info["rocm_version"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            cur = [l.strip() for l in open(path) if l.strip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            info["gpu_sclk_now"] = cur[0]
+            break
+    return info
+
+
+def rank_kernels(marks, steps):
+    """Per-label launches per step, median launch time and time per step from
+    (label, ms) marks of `steps` whole steps.  The median keeps one slow launch (a first
+    launch that loads its code object, say) from deciding the ranking."""
+    import statistics
+    per = {}
+    for name, ms in marks:
+        per.setdefault(name, []).append(ms)
+    out = {}
+    for name, v in per.items():
+        lps = len(v) / max(steps, 1)
+        med = statistics.median(v)
+        out[name] = {"launches_per_step": lps, "median_ms": med, "mean_ms": sum(v) / len(v),
+                     "ms_per_step": med * lps}
+    return out
+
+
+def dominant_kernel(ranked):
+    """The kernel that takes the most time per step."""
+    return max(ranked, key=lambda n: ranked[n]["ms_per_step"]) if ranked else None
 
 
 def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016)):
@@ -576,8 +657,12 @@ def diag_timing(dev, reps=5):
     tf = flop / (ms * 1e-3) / 1e12
     return {"config": "exact-gradient diagnostics, C2 layer (32K slots x 8 KV heads, 128 window queries per head), "
                       "E ~ N(0, 1)", "kernel_ms": round(ms, 4),
-            "roofline": {"bound": "alu", "achieved": round(tf, 1), "peak": 157.3, "unit": "TFLOP/s",
-                         "frac": round(tf / 157.3, 3), "flop_per_launch": flop},
+            # the library is built without packed fp32 instructions, so the fp32 vector peak is
+            # the unpacked one: 256 CUs x 4 SIMDs x 16 lanes x 2 flop (fma) x 2.4 GHz = 78.6 TFLOP/s
+            # (157.3 counts two fp32 operations per lane per packed instruction)
+            "roofline": {"bound": "alu", "achieved": round(tf, 1), "peak": 78.6, "unit": "TFLOP/s",
+                         "frac": round(tf / 78.6, 3), "flop_per_launch": flop,
+                         "peak_note": "unpacked fp32 vector rate; packed fp32 forms are compiled out"},
             "cos_E_c11": round(c11, 4), "cos_E_c22": round(c22, 4), "cos_E_c12": round(c12, 4),
             "median_abs_w_exact_minus_w_fwd": round(dw.median().item(), 4),
             "note": "a random E is no trained model's gradient: the angle relation the forward-only weights "
@@ -747,31 +832,27 @@ def main():
                             bufs.K, bufs.V, bufs.n, bufs.src)
         L.kvs_decode_attn(dec_cache, bufs.K, bufs.V, bufs.n, q, 1.0 / math.sqrt(D), dec_out, dec_ws)
 
-    # warm-up; its last steps mark every kernel launch with HIP events to rank the kernels
-    n_marked = min(args.warmup, 5)
-    for i in range(args.warmup - n_marked):
+    # warm-up: W steps (at least one, so that every kernel has loaded its code object
+    # before any launch is marked); then, still outside the timed region, a few steps with
+    # every launch marked rank the kernels by median time per step
+    for i in range(max(args.warmup, 1)):
         step(i)
-    every = L.KernelMarks(max_launches=16 * max(n_marked, 1))
+    n_rank = 3
+    every = L.KernelMarks(max_launches=16 * n_rank)
     with every:
-        for i in range(args.warmup - n_marked, args.warmup):
-            step(i)
+        for i in range(n_rank):
+            step(args.warmup + i)
     torch.cuda.synchronize()
-    per_kernel = {}
-    for name, ms in every.times():
-        tot, cnt = per_kernel.get(name, (0.0, 0))
-        per_kernel[name] = (tot + ms, cnt + 1)
+    ranked = rank_kernels(every.times(), n_rank)
     step_separate(0)            # first launches of these kernels load their code
     torch.cuda.synchronize()
-    sep = L.KernelMarks(max_launches=16 * max(n_marked, 1))
+    sep = L.KernelMarks(max_launches=16 * n_rank)
     with sep:
-        for i in range(n_marked):
+        for i in range(n_rank):
             step_separate(i)
     torch.cuda.synchronize()
-    separate = {}
-    for name, ms in sep.times():
-        tot, cnt = separate.get(name, (0.0, 0))
-        separate[name] = (tot + ms, cnt + 1)
-    dominant = max(per_kernel, key=lambda n: per_kernel[n][0]) if per_kernel else None
+    ranked_sep = rank_kernels(sep.times(), n_rank)
+    dominant = dominant_kernel(ranked)
 
     # timed region: K whole steps; the library records HIP events right before and after
     # each launch of the dominant kernel (on its stream), timing that kernel live
@@ -793,19 +874,18 @@ def main():
         dominant = marks.times()[0][0]
     kb = kernel_bytes(N, H, D, P, T, cfg.group * W)
     kernels = {}
-    for name, (tot, cnt) in per_kernel.items():
-        avg = tot / cnt
+    for name, r in ranked.items():
         by = kb.get(name, 0)
-        kernels[name] = {"launches_per_step": cnt // max(n_marked, 1), "avg_ms": round(avg, 4),
+        kernels[name] = {"launches_per_step": r["launches_per_step"], "median_ms": round(r["median_ms"], 4),
                          "algorithmic_MB": round(by / 1e6, 2),
-                         "GBps": round(by / (avg * 1e-3) / 1e9, 1) if by else None}
+                         "GBps": round(by / (r["median_ms"] * 1e-3) / 1e9, 1) if by else None}
     kernels_separate = {}
-    for name, (tot, cnt) in separate.items():
-        avg = tot / cnt
+    for name, r in ranked_sep.items():
         by = kb.get(name, 0)
-        kernels_separate[name] = {"avg_ms": round(avg, 4), "algorithmic_MB": round(by / 1e6, 2),
-                                  "GBps": round(by / (avg * 1e-3) / 1e9, 1) if by else None,
-                                  "hbm_frac": round(by / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if by else None}
+        med = r["median_ms"]
+        kernels_separate[name] = {"median_ms": round(med, 4), "algorithmic_MB": round(by / 1e6, 2),
+                                  "GBps": round(by / (med * 1e-3) / 1e9, 1) if by else None,
+                                  "hbm_frac": round(by / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if by else None}
     dom_ms = sum(timed) / len(timed)
     dom_gbps = kb[dominant] / (dom_ms * 1e-3) / 1e9
     step_bytes = sum(kb[n] * kernels[n]["launches_per_step"] for n in kernels if n in kb)
@@ -828,7 +908,7 @@ def main():
                    "accumulate": "f32"},
         "hbm_GBps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "gpu_ms_per_step": round(gpu_ms, 4),
-        "kernels_warmup_marked": kernels,
+        "kernels_ranked": kernels,
         "kernels_separate_calls": kernels_separate,
         "roofline": {"kernel": dominant, "avg_ms": round(dom_ms, 4), "launches": len(timed),
                      "algorithmic_bytes": kb[dominant], "bound": "hbm", "achieved": round(dom_gbps, 1),
@@ -837,9 +917,10 @@ def main():
     }
     line["given_window_stats"] = given_stats_timing(args, sets, step, bufs, cache, rnd, out_desc, dec_cache, dec_out,
                                                     dec_ws, D, B * N, kb)
+    line["machine"] = gpu_clock_info()
     if not args.no_cpu_baseline:
-        K, V, Qw, _ = sets[0]
-        line["cpu_baseline"] = cpu_baseline(cfg, K, V, Qw)
+        K, V, Qw, q = sets[0]
+        line["cpu_baseline"] = cpu_baseline(cfg, K, V, Qw, q)
     print(json.dumps(line), flush=True)
 
 

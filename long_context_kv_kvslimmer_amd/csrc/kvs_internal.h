@@ -101,7 +101,6 @@ hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, f
 // [units], O [units, D]).
 hipError_t launch_pack(const float* lse, const float* O, int64_t units, int D, const PackP& pk, hipStream_t st);
 
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 // ---- decode ----
 size_t decode_workspace_bytes(const Shape& s);

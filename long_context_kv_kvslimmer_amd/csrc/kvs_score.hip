@@ -332,18 +332,6 @@ hipError_t launch_pack(const float* lse, const float* O, int64_t units, int D, c
   return hipGetLastError();
 }
 
-__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0.f;
-}
-
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
-  KVS_LAUNCH("fill_zero", fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
-  return hipGetLastError();
-}
-
 hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, float* lse, float* out,
                           hipStream_t st, const PackP* pack) {
   if (units == 0) return hipSuccess;

@@ -48,6 +48,9 @@ struct P2Args {
   const float* cos;
   const int32_t* sel;
   int64_t sel_stride;
+  // more than one 128-query block per kv head: each block's sums go to its own slice,
+  // [query block][B*Hkv][N] then [query block][B*Hkv][P], added in block order afterwards
+  float* qpart;
 };
 
 struct CosArgs {

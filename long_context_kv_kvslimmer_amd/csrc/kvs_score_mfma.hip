@@ -878,22 +878,37 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
   __syncthreads();
   if (MERGE) merge_tile(ntiles - 1);
 
-  // per-slot totals of the chunk -> global (several query blocks accumulate)
-  const bool acc = gridDim.x > (unsigned)(BH * nsplit);
+  // per-slot totals of the chunk -> global; with several query blocks each block writes its
+  // own slice and a second kernel adds the slices in block order (no atomics, so the sums
+  // do not depend on the order the blocks finish in)
+  float* gs = a.g_self;
+  float* gx = a.g_cross;
+  if (a.qpart) {
+    gs = a.qpart + qb * (int64_t)BH * (a.N + a.P);
+    gx = gs + (int64_t)BH * a.N;
+  }
   for (int64_t s = lo + tid; s < hi; s += kW2 * 64) {
     const int64_t ls = s - c0;
-    const float v = sum_waves(reinterpret_cast<const float4*>(red)[(ls >> 1) * 3 + (ls & 1)]);
-    if (acc) atomicAdd(&a.g_self[bh * a.N + s], v);
-    else a.g_self[bh * a.N + s] = v;
+    gs[bh * a.N + s] = sum_waves(reinterpret_cast<const float4*>(red)[(ls >> 1) * 3 + (ls & 1)]);
   }
   for (int64_t pp = tid; 2 * pp < hi - c0; pp += kW2 * 64) {
     const int64_t m0 = c0 + 2 * pp;
     const int64_t p = (m0 - a.S) / 2;
-    if (m0 >= a.S && m0 >= lo && m0 + 1 < hi && p < a.P) {
-      const float v = sum_waves(reinterpret_cast<const float4*>(red)[pp * 3 + 2]);
-      if (acc) atomicAdd(&a.g_cross[bh * a.P + p], v);
-      else a.g_cross[bh * a.P + p] = v;
-    }
+    if (m0 >= a.S && m0 >= lo && m0 + 1 < hi && p < a.P)
+      gx[bh * a.P + p] = sum_waves(reinterpret_cast<const float4*>(red)[pp * 3 + 2]);
+  }
+}
+
+// Sums of the per-query-block slices of pass 2, added in block order: element i < BN of the
+// slices goes to g_self[i], element BN + j to g_cross[j].
+__global__ void qsum_kernel(const float* __restrict__ part, int nqb, int64_t BN, int64_t BP,
+                            float* __restrict__ g_self, float* __restrict__ g_cross) {
+  const int64_t tot = BN + BP;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < tot; i += (int64_t)gridDim.x * blockDim.x) {
+    float x = part[i];
+    for (int q = 1; q < nqb; ++q) x += part[q * tot + i];
+    if (i < BN) g_self[i] = x;
+    else g_cross[i - BN] = x;
   }
 }
 
@@ -947,8 +962,21 @@ static size_t pack_ops_bytes(const Shape& s, const RoundP& r) {
   return ((size_t)s.B * s.Hkv * pack_blocks(s, r) * 32 * 3 * s.D * 2 + 255) / 256 * 256;
 }
 
+static size_t pack_qc_bytes(const Shape& s, const RoundP& r) {
+  return ((size_t)s.B * s.Hkv * pack_blocks(s, r) * 32 * 2 * sizeof(float) + 255) / 256 * 256;
+}
+
+// Per-query-block slices of the pass-2 sums (several 128-query blocks per kv head only).
+static int64_t query_blocks(const Shape& s, const RoundP& r) { return ((int64_t)s.G * r.W + kQB - 1) / kQB; }
+static size_t qpart_bytes(const Shape& s, const RoundP& r) {
+  const int64_t nqb = query_blocks(s, r);
+  return nqb > 1 ? (size_t)nqb * s.B * s.Hkv * (s.N + r.P) * sizeof(float) : 0;
+}
+
+// Workspace: pass-1 partial records, the pass-2 operand pack, the per-query constants and
+// the per-query-block slices of the sums, each 256-byte aligned.
 size_t mfma_score_workspace_bytes(const Shape& s, const RoundP& r) {
-  return part_bytes(s, r) + pack_ops_bytes(s, r) + (size_t)s.B * s.Hkv * pack_blocks(s, r) * 32 * 2 * sizeof(float);
+  return part_bytes(s, r) + pack_ops_bytes(s, r) + pack_qc_bytes(s, r) + qpart_bytes(s, r);
 }
 
 // merge: 0 = plain pass 2; 1 = fused merge with bf16 output; 2 = fused merge with fp32 output
@@ -1001,10 +1029,7 @@ static hipError_t launch_p2_d(const Shape& s, const RoundP& r, const P2Args& p2,
   hipError_t e = hipSuccess;
   if (nqb > 1) {
     if (merge) return hipErrorInvalidValue;   // the fused merge needs every query in one workgroup
-    // several query blocks accumulate into the same sums
-    e = launch_fill_zero(p2.g_self, BH * s.N, st);
-    if (e == hipSuccess) e = launch_fill_zero(p2.g_cross, BH * r.P, st);
-    if (e != hipSuccess) return e;
+    if (!p2.qpart) return hipErrorInvalidValue;
   }
   if (merge && r.M > 0 && r.M < r.P) {
     // partial round: choose the pairs from the pass-1 cosine before pass 2 merges them
@@ -1041,6 +1066,12 @@ static hipError_t launch_p2_d(const Shape& s, const RoundP& r, const P2Args& p2,
     }
   }
 #undef KVS_P2
+  e = hipGetLastError();
+  if (e != hipSuccess || nqb == 1) return e;
+  const int64_t BN = BH * s.N, BP = BH * r.P;
+  const int64_t blocks = (BN + BP + 255) / 256 < 2048 ? (BN + BP + 255) / 256 : 2048;
+  KVS_LAUNCH("qsum", qsum_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p2.qpart, nqb, BN, BP, p2.g_self,
+             p2.g_cross);
   return hipGetLastError();
 }
 
@@ -1069,6 +1100,9 @@ static hipError_t launch_score_any(const Shape& s, const RoundP& r, const void* 
   p2.nwb = pack_blocks(s, r);
   p2.ops = reinterpret_cast<const uint4*>(static_cast<uint8_t*>(ws) + part_bytes(s, r));
   p2.qc = reinterpret_cast<const float*>(static_cast<uint8_t*>(ws) + part_bytes(s, r) + pack_ops_bytes(s, r));
+  p2.qpart = qpart_bytes(s, r) ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + part_bytes(s, r) +
+                                                          pack_ops_bytes(s, r) + pack_qc_bytes(s, r))
+                               : nullptr;
   p2.K = K;
   p2.V = V;
   p2.n = n;
@@ -1141,7 +1175,7 @@ namespace kvs {
 // Workspace of a round given the window statistics: the pass-2 operand pack and the
 // per-query constants (the cosine and the selection state follow, in the API layer).
 size_t stats_pack_bytes(const Shape& s, const RoundP& r) {
-  return pack_ops_bytes(s, r) + (size_t)s.B * s.Hkv * pack_blocks(s, r) * 32 * 2 * sizeof(float);
+  return pack_ops_bytes(s, r) + pack_qc_bytes(s, r) + qpart_bytes(s, r);
 }
 
 hipError_t launch_stats_merge_mfma(const Shape& s, const RoundP& r, const void* K, const void* V, const int32_t* n,
@@ -1153,6 +1187,9 @@ hipError_t launch_stats_merge_mfma(const Shape& s, const RoundP& r, const void* 
   p2.nwb = pack_blocks(s, r);
   p2.ops = static_cast<const uint4*>(ws);
   p2.qc = reinterpret_cast<const float*>(static_cast<uint8_t*>(ws) + pack_ops_bytes(s, r));
+  p2.qpart = qpart_bytes(s, r) ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pack_ops_bytes(s, r) +
+                                                          pack_qc_bytes(s, r))
+                               : nullptr;
   p2.K = K;
   p2.V = V;
   p2.n = n;
