@@ -13,6 +13,7 @@
  *                      closed-form key-merge weights
  *   kvs_merge_compact  key merge, lossless value-slot merge, stream compaction
  *   kvs_decode_attn    GQA decode attention over a (merged) cache
+ *   kvs_decode_attn_static  the same with a library-owned scratch (no workspace argument)
  *   kvs_append         write raw tokens (count 1) into a cache: a prefill chunk or a decode step
  *   kvs_exact_e_diag   diagnostics: exact-gradient scalars and weights against the forward-only ones
  *   kvs_spectral_modes analysis: per-eigen-mode split of adjacent-key cosines
@@ -31,7 +32,8 @@
  *    kvs_round structs are host memory, read during the call only.
  *  - The library allocates no memory and keeps no state: scratch space is the caller's
  *    `workspace` (size from kvs_workspace_bytes).  Calls on different streams are
- *    independent; outputs must not alias inputs.
+ *    independent; outputs must not alias inputs.  The one exception is
+ *    kvs_decode_attn_static, whose scratch is a static device array of the library.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *    returns without synchronising.  Output lengths are host-computable up front.
  *  - Arguments are validated before anything is enqueued; on a validation error nothing is
@@ -304,6 +306,26 @@ kvs_status kvs_decode_attn(const kvs_cache* cache, kvs_dtype dtype,
                            const void* K, const void* V, const int32_t* n,
                            const void* q, float sm_scale, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvs_decode_attn_static — kvs_decode_attn for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, arithmetic and outputs as kvs_decode_attn (the same
+ * kernels, bit for bit), without the workspace: its scratch is a library-owned static
+ * device array of KVS_STATIC_SCRATCH_BYTES bytes, one per GPU, held from the first call on
+ * that GPU until the process ends.  The call itself allocates and frees nothing.  Nothing
+ * in the scratch needs clearing: every call writes each record it reads.  All calls on one
+ * GPU share that GPU's scratch, so calls that overlap in time on one GPU (on different
+ * streams, or from different threads) race and must be serialised by the caller; the
+ * stream must belong to the current device.  Errors: as kvs_decode_attn; KVS_ERR_WORKSPACE
+ * when kvs_workspace_bytes(KVS_OP_DECODE) for these shapes exceeds
+ * KVS_STATIC_SCRATCH_BYTES (nothing is enqueued); KVS_ERR_HIP if the scratch address cannot
+ * be obtained on the first call on a device.
+ */
+#define KVS_STATIC_SCRATCH_BYTES (8u << 20)
+kvs_status kvs_decode_attn_static(const kvs_cache* cache, kvs_dtype dtype,
+                                  const void* K, const void* V, const int32_t* n,
+                                  const void* q, float sm_scale, float* out, void* stream);
 
 /* Kernel timing marks (instrumentation, off by default).
  *

@@ -460,23 +460,48 @@ kvs_status kvs_merge_compact(const kvs_cache* cache, kvs_dtype in_dtype, const v
                     "kvs_merge_compact");
 }
 
+static kvs_status check_decode(const kvs_cache* cache, kvs_dtype dtype, const void* K, const void* V, const void* q,
+                               float sm_scale, const float* out, kvs::Shape& s, const char* name) {
+  kvs_status st = check_cache(cache, dtype, s);
+  if (st) return st;
+  if (s.N < 1) return fail(KVS_ERR_SHAPE, "%s needs n_slots >= 1", name);
+  if (s.G != 1 && s.G != 2 && s.G != 4 && s.G != 8)
+    return fail(KVS_ERR_SHAPE, "%s supports n_q_heads / n_kv_heads in {1, 2, 4, 8}, got %d", name, s.G);
+  if (!std::isfinite(sm_scale)) return fail(KVS_ERR_SHAPE, "sm_scale is not finite");
+  if (!K || !V || !q || !out) return fail(KVS_ERR_NULL, "%s: K, V, q, out are required", name);
+  if (!aligned16(K) || !aligned16(V) || !aligned16(q)) return fail(KVS_ERR_ALIGN, "K, V, q must be 16-byte aligned");
+  return KVS_OK;
+}
+
 kvs_status kvs_decode_attn(const kvs_cache* cache, kvs_dtype dtype, const void* K, const void* V, const int32_t* n,
                            const void* q, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
                            void* stream) {
   kvs::Shape s;
-  kvs_status st = check_cache(cache, dtype, s);
+  kvs_status st = check_decode(cache, dtype, K, V, q, sm_scale, out, s, "kvs_decode_attn");
   if (st) return st;
-  if (s.N < 1) return fail(KVS_ERR_SHAPE, "kvs_decode_attn needs n_slots >= 1");
-  if (s.G != 1 && s.G != 2 && s.G != 4 && s.G != 8)
-    return fail(KVS_ERR_SHAPE, "kvs_decode_attn supports n_q_heads / n_kv_heads in {1, 2, 4, 8}, got %d", s.G);
-  if (!std::isfinite(sm_scale)) return fail(KVS_ERR_SHAPE, "sm_scale is not finite");
-  if (!K || !V || !q || !out) return fail(KVS_ERR_NULL, "kvs_decode_attn: K, V, q, out are required");
-  if (!aligned16(K) || !aligned16(V) || !aligned16(q)) return fail(KVS_ERR_ALIGN, "K, V, q must be 16-byte aligned");
   const size_t need = kvs::decode_workspace_bytes(s);
   if (workspace_bytes < need || !workspace)
     return fail(KVS_ERR_WORKSPACE, "kvs_decode_attn needs %zu workspace bytes, got %zu", need, workspace_bytes);
   return hip_status(kvs::launch_decode(s, K, V, n, q, sm_scale, out, workspace, static_cast<hipStream_t>(stream)),
                     "kvs_decode_attn");
+}
+
+kvs_status kvs_decode_attn_static(const kvs_cache* cache, kvs_dtype dtype, const void* K, const void* V,
+                                  const int32_t* n, const void* q, float sm_scale, float* out, void* stream) {
+  kvs::Shape s;
+  kvs_status st = check_decode(cache, dtype, K, V, q, sm_scale, out, s, "kvs_decode_attn_static");
+  if (st) return st;
+  const size_t need = kvs::decode_workspace_bytes(s);
+  if (need > KVS_STATIC_SCRATCH_BYTES)
+    return fail(KVS_ERR_WORKSPACE,
+                "kvs_decode_attn_static: these shapes need %zu bytes of scratch, above the library's %zu; use "
+                "kvs_decode_attn with a workspace",
+                need, (size_t)KVS_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  hipError_t e = kvs::static_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "kvs_decode_attn_static (scratch address)");
+  return hip_status(kvs::launch_decode(s, K, V, n, q, sm_scale, out, ws, static_cast<hipStream_t>(stream)),
+                    "kvs_decode_attn_static");
 }
 
 const char* kvs_status_str(kvs_status s) {

@@ -10,6 +10,9 @@
 // (running max, sum, partial output) per head, updated once per block of RB rows.
 // Groups are merged in LDS into one partial record per (query head, split); the shared
 // log-sum-exp combine turns the records into the output.
+#include <mutex>
+
+#include "../../include/kvslim.h"
 #include "kvs_common.h"
 #include "kvs_dma.h"
 #include "kvs_internal.h"
@@ -474,6 +477,34 @@ size_t decode_workspace_bytes(const Shape& s) {
   decode_plan(sf, chunk, ns2);
   if (ns2 > nsplit) nsplit = ns2;   // the workspace query does not know the element type
   return (size_t)s.B * s.Hq * nsplit * (s.D + 4) * sizeof(float);
+}
+
+// Library-owned scratch of kvs_decode_attn_static (the split partial records of a decode
+// call), for callers that cannot allocate.  Every GPU the library runs on holds its own copy
+// from the first use of this code object until the process ends.  Host code never uses the
+// array's name as an address: static_scratch() asks HIP for the current device's address
+// of it once per device and keeps it.
+static __device__ __align__(256) uint8_t scratch[KVS_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const Shape& s, const void* K, const void* V, const int32_t* n, const void* q,

@@ -106,5 +106,8 @@ hipError_t launch_pack(const float* lse, const float* O, int64_t units, int D, c
 size_t decode_workspace_bytes(const Shape& s);
 hipError_t launch_decode(const Shape& s, const void* K, const void* V, const int32_t* n, const void* q,
                          float scale, float* out, void* ws, hipStream_t st);
+// Device address of the library's static decode scratch on the current device
+// (KVS_STATIC_SCRATCH_BYTES bytes), looked up once per device.
+hipError_t static_scratch(void** ptr);
 
 }  // namespace kvs

@@ -22,7 +22,7 @@ KVS_OP_SCORE, KVS_OP_SELECT, KVS_OP_SEL_STATE, KVS_OP_DECODE, KVS_OP_SCORE_MERGE
 
 EXPORTS = ("kvs_num_pairs", "kvs_workspace_bytes", "kvs_score", "kvs_score_merge", "kvs_merge_weights", "kvs_merge_compact",
            "kvs_append", "kvs_score_merge_stats", "kvs_exact_e_diag", "kvs_spectral_modes",
-           "kvs_decode_attn", "kvs_marks_begin", "kvs_marks_end", "kvs_mark_name", "kvs_mark_ms", "kvs_status_str",
+           "kvs_decode_attn", "kvs_decode_attn_static", "kvs_marks_begin", "kvs_marks_end", "kvs_mark_name", "kvs_mark_ms", "kvs_status_str",
            "kvs_last_error", "kvs_version")
 
 
@@ -58,6 +58,7 @@ def _load():
         "kvs_merge_weights": (ctypes.c_int, [C, R, P, P, P, P, P, P, SZ, P, SZ, P]),
         "kvs_merge_compact": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, P, R, P, C, ctypes.c_int, P, P, P, P, P]),
         "kvs_decode_attn": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, F, P, P, SZ, P]),
+        "kvs_decode_attn_static": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, F, P, P]),
         "kvs_append": (ctypes.c_int, [C, ctypes.c_int, P, P, P, I64, C, P, P, I64, I64, P]),
         "kvs_exact_e_diag": (ctypes.c_int, [C, ctypes.c_int, P, P, P, P, R, P, P, P, P, P, P]),
         "kvs_spectral_modes": (ctypes.c_int, [ctypes.c_int, P, I64, I32, P, P, I32, P, P, P, P]),
@@ -224,6 +225,13 @@ def kvs_decode_attn(cache: KvsCache, K, V, n, q, sm_scale: float, out, workspace
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.kvs_decode_attn(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(q),
                                 ctypes.c_float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream()))
+
+
+def kvs_decode_attn_static(cache: KvsCache, K, V, n, q, sm_scale: float, out):
+    """kvs_decode_attn with the library's static scratch instead of a workspace."""
+    _same_layout(K, V)
+    _check(_lib.kvs_decode_attn_static(ctypes.byref(cache), dtype_code(K), _ptr(K), _ptr(V), _ptr(n), _ptr(q),
+                                       ctypes.c_float(sm_scale), _ptr(out), _stream()))
 
 
 def kvs_append(cache: KvsCache, K, V, n, at: int, src: KvsCache, K_new, V_new, from_: int, count: int):

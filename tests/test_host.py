@@ -249,3 +249,18 @@ def test_spectral_modes_validation(L):
     assert call(X=None) == L.KVS_ERR_NULL
     assert call(cos=None) == L.KVS_ERR_NULL
     assert call(modes=ctypes.c_void_p(4104)) == L.KVS_ERR_ALIGN
+
+
+def test_static_decode_rejects_shapes_beyond_its_scratch(L):
+    """kvs_decode_attn_static refuses, before touching the GPU, shapes whose split records
+    would not fit the library's static scratch."""
+    big = _cache(B=8, H=8, Hq=32, D=128, N=65536)
+    assert L.workspace_bytes(L.KVS_OP_DECODE, big, None) > (8 << 20)
+    st = L._lib.kvs_decode_attn_static(ctypes.byref(big), 1, FAKE, FAKE, None, FAKE, ctypes.c_float(0.1), FAKE,
+                                       None)
+    assert st == 7 and "static" in L.last_error()
+    st = L._lib.kvs_decode_attn_static(ctypes.byref(big), 1, None, FAKE, None, FAKE, ctypes.c_float(0.1), FAKE, None)
+    assert st == 1
+    bad = _cache(Hq=24)
+    st = L._lib.kvs_decode_attn_static(ctypes.byref(bad), 0, FAKE, FAKE, None, FAKE, ctypes.c_float(0.1), FAKE, None)
+    assert st == 2
