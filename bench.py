@@ -232,6 +232,56 @@ def summarize_mfma(sq_csv, stats_csv, cmd):
     return "\n".join(out) + "\n"
 
 
+def summarize_pmc(csvs, stats_csv, cmd, title):
+    """Markdown summary of several rocprofv3 --pmc runs (comma-separated counter_collection
+    CSVs) next to a kernel-trace stats CSV: per kernel label, the mean per-dispatch value of
+    every counter, then the ratios that show which pipe binds.  GRBM_GUI_ACTIVE is summed
+    over the 8 XCDs in the CSV, so one eighth of it is the dispatch's active cycles."""
+    import csv
+    import statistics
+    per = {}
+    for path in csvs.split(","):
+        for r in csv.DictReader(open(path)):
+            lab = kernel_label(r["Kernel_Name"])
+            if lab:
+                per.setdefault(lab, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    dur = {}
+    for r in csv.DictReader(open(stats_csv)):
+        lab = kernel_label(r["Name"])
+        if lab:
+            c, t = dur.get(lab, (0, 0.0))
+            dur[lab] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
+    names = sorted({n for d in per.values() for n in d})
+    out = [f"# {title}", "", "Made by:", "", "```", cmd, "```", "",
+           "Mean value per dispatch (sums over the chip as rocprofv3 reports them).", "",
+           "| counter | " + " | ".join(sorted(per)) + " |", "|---|" + "---:|" * len(per)]
+    for n in names:
+        out.append(f"| {n} | " + " | ".join(f"{statistics.mean(per[k][n]):.4g}" if n in per[k] else "" for k in
+                                            sorted(per)) + " |")
+    out += ["", "Derived (SIMDs = 1024; cycles = GRBM_GUI_ACTIVE / 8; quad-cycle counters x 4):", "",
+            "| kernel | mean us | active cycles | VALU instr per SIMD | trans share | VALU busy | MFMA busy | "
+            "MFMA-VALU co-exec / MFMA busy | LDS busy | LDS bank-conflict rate | wave wait share |",
+            "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+
+    def m(k, n):
+        v = per[k].get(n)
+        return statistics.mean(v) if v else float("nan")
+    for k in sorted(per):
+        cyc = m(k, "GRBM_GUI_ACTIVE") / 8
+        us = dur[k][1] / dur[k][0] / 1e3 if k in dur else float("nan")
+        valu = m(k, "SQ_INSTS_VALU") / SIMDS
+        trans = m(k, "SQ_INSTS_VALU_TRANS_F32") / max(m(k, "SQ_INSTS_VALU"), 1)
+        vbusy = m(k, "SQ_ACTIVE_INST_VALU") * 4 / SIMDS / cyc
+        mbusy = m(k, "SQ_VALU_MFMA_BUSY_CYCLES") / SIMDS / cyc
+        coex = m(k, "SQ_VALU_MFMA_COEXEC_CYCLES") / max(m(k, "SQ_VALU_MFMA_BUSY_CYCLES"), 1)
+        lbusy = m(k, "SQ_ACTIVE_INST_LDS") * 4 / SIMDS / cyc
+        bc = m(k, "SQ_LDS_BANK_CONFLICT") / max(m(k, "SQ_LDS_IDX_ACTIVE") - m(k, "SQ_LDS_BANK_CONFLICT"), 1)
+        wait = m(k, "SQ_WAIT_ANY") / max(m(k, "SQ_WAVE_CYCLES"), 1)
+        out.append(f"| {k} | {us:.2f} | {cyc:.0f} | {valu:.0f} | {trans:.3f} | {vbusy:.3f} | {mbusy:.3f} | {coex:.3f} | "
+                   f"{lbusy:.3f} | {bc:.4f} | {wait:.3f} |")
+    return "\n".join(out) + "\n"
+
+
 def summarize_per_config(jsonl, cmd):
     """Markdown table of the JSON lines printed by `bench.py --per-config`."""
     allrows = [json.loads(line) for line in open(jsonl) if line.startswith("{")]
@@ -741,6 +791,7 @@ def main():
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "CMD"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "BENCH_JSON", "CMD"))
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("SQ_CSV", "STATS_CSV", "CMD"))
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("CSVS", "STATS_CSV", "CMD", "TITLE"))
     ap.add_argument("--summarize-per-config", nargs=2, metavar=("JSONL", "CMD"))
     ap.add_argument("--summarize-stats", nargs=3, metavar=("STATS_CSV", "TITLE", "CMD"))
     ap.add_argument("--spectral", action="store_true",
@@ -760,6 +811,9 @@ def main():
         return
     if args.summarize_mfma:
         sys.stdout.write(summarize_mfma(*args.summarize_mfma))
+        return
+    if args.summarize_pmc:
+        sys.stdout.write(summarize_pmc(*args.summarize_pmc))
         return
     if args.summarize_counters:
         sys.stdout.write(summarize_counters(*args.summarize_counters))

@@ -56,14 +56,17 @@ __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, co
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Split 8 floats into bf16 hi (RNE) and lo = bf16(x - hi).
+// Split 8 floats into bf16 hi (RNE) and lo = bf16(x - hi), two elements per conversion.
 __device__ __forceinline__ void split_hi_lo(const float* x, bf16x8_t& hi, bf16x8_t& lo) {
+  u32x4_t h, l;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)x[j];
-    hi[j] = h;
-    lo[j] = (__bf16)(x[j] - (float)h);
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t hp = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+    h[j] = hp;
+    l[j] = pack_bf16x2(x[2 * j] - bf16_lo(hp), x[2 * j + 1] - bf16_hi(hp));
   }
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
 // ------------------------------------------------------------------ tiling ----
@@ -653,7 +656,8 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       for (int r = 0; r < 4; ++r) {
         const bool vc = wb * 32 + q2 * 16 + 4 * g4 + r < a.GW;
         onv[q2][r] = vc ? c8[2 * r] : 0.f;
-        nbq[q2][r] = vc ? c8[2 * r + 1] : -INFINITY;
+        // + 1: the exponent gives twice the attention weight (see the sums below)
+        nbq[q2][r] = vc ? c8[2 * r + 1] + 1.f : -INFINITY;
       }
     }
   }
@@ -744,6 +748,9 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     const float vno = __shfl(pick(goo), src, 64);
     const float veo = __shfl(pick(geo), src, 64);
     const float dvp = vne + vno - 2.f * veo;          // ||v_m - v_{m+1}||^2
+    // With a = 2 alpha (the exponent carries + 1): alpha |1 - 2 alpha| = |a - a^2| / 2 and
+    // alpha_m alpha_{m+1} = a_m a_{m+1} / 4, one fma for the first; the factors 1/2 and
+    // 1/4 (exact) are applied to the tile's sums.
     float gse = 0.f, gso = 0.f, gx = 0.f;
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2)
@@ -752,16 +759,16 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
         const float ae = __builtin_amdgcn_exp2f(__builtin_fmaf(se[q2][r], cs, nbq[q2][r]));
         const float ao = __builtin_amdgcn_exp2f(__builtin_fmaf(so[q2][r], cs, nbq[q2][r]));
         const float rre = re[q2][r] + vne, rro = ro[q2][r] + vno;
-        gse = __builtin_fmaf(ae * fabsf(__builtin_fmaf(-2.f, ae, 1.f)), __builtin_amdgcn_sqrtf(fabsf(rre)), gse);
-        gso = __builtin_fmaf(ao * fabsf(__builtin_fmaf(-2.f, ao, 1.f)), __builtin_amdgcn_sqrtf(fabsf(rro)), gso);
+        gse = __builtin_fmaf(fabsf(__builtin_fmaf(-ae, ae, ae)), __builtin_amdgcn_sqrtf(fabsf(rre)), gse);
+        gso = __builtin_fmaf(fabsf(__builtin_fmaf(-ao, ao, ao)), __builtin_amdgcn_sqrtf(fabsf(rro)), gso);
         // ||v_m + v_{m+1} - 2 o||^2 = 2 r_m^2 + 2 r_{m+1}^2 - ||v_m - v_{m+1}||^2
         const float rc = __builtin_fmaf(2.f, rre + rro, -dvp);
         gx = __builtin_fmaf(ae * ao, __builtin_amdgcn_sqrtf(fabsf(rc)), gx);
       }
     // sum the four lane groups (queries 4 g + r)
-    gse = sum_xor32(sum_xor16(gse));
-    gso = sum_xor32(sum_xor16(gso));
-    gx = sum_xor32(sum_xor16(gx));
+    gse = 0.5f * sum_xor32(sum_xor16(gse));
+    gso = 0.5f * sum_xor32(sum_xor16(gso));
+    gx = 0.25f * sum_xor32(sum_xor16(gx));
     if (g4 == 0) {
       float* rp = red + (t * (kT2 / 2) + n16) * 3 * kW2 + wv;
       rp[0] = gse;
