@@ -67,10 +67,20 @@ typedef enum {
   KVS_ERR_ALIGN = 5,       /* K/V/output base pointers not 16-byte aligned */
   KVS_ERR_INFEASIBLE = 6,  /* n_merge < 0 or n_merge > number of candidate pairs */
   KVS_ERR_WORKSPACE = 7,   /* workspace / selection-state buffer missing or too small */
-  KVS_ERR_HIP = 8          /* a HIP launch failed */
+  KVS_ERR_HIP = 8,         /* a HIP launch failed */
+  KVS_STATUS_INT32_LO_ = -0x7fffffff - 1, /* range markers: every int32_t is a value of the type */
+  KVS_STATUS_INT32_HI_ = 0x7fffffff
 } kvs_status;
 
-typedef enum { KVS_BF16 = 0, KVS_F32 = 1 } kvs_dtype;
+/* Element types.  Every public enum spans the whole int32_t range, so an unknown value
+ * passed from C or another language is a valid argument that the call rejects
+ * (KVS_ERR_DTYPE here, 0 bytes for an unknown kvs_op), not undefined behaviour. */
+typedef enum {
+  KVS_BF16 = 0,
+  KVS_F32 = 1,
+  KVS_DTYPE_INT32_LO_ = -0x7fffffff - 1,
+  KVS_DTYPE_INT32_HI_ = 0x7fffffff
+} kvs_dtype;
 
 typedef struct {
   int32_t batch;       /* B */
@@ -97,7 +107,9 @@ typedef enum {
   KVS_OP_SEL_STATE = 2,  /* size of the selection-state buffer (kvs_merge_weights -> kvs_merge_compact) */
   KVS_OP_DECODE = 3,     /* workspace of kvs_decode_attn */
   KVS_OP_SCORE_MERGE = 4, /* workspace of kvs_score_merge (equals KVS_OP_SCORE when n_merge is 0 or P) */
-  KVS_OP_STATS_MERGE = 5  /* workspace of kvs_score_merge_stats */
+  KVS_OP_STATS_MERGE = 5, /* workspace of kvs_score_merge_stats */
+  KVS_OP_INT32_LO_ = -0x7fffffff - 1,
+  KVS_OP_INT32_HI_ = 0x7fffffff
 } kvs_op;
 
 /* Number of candidate pairs P = floor((N - S - R) / 2) (0 if negative).  Pair p is the

@@ -219,6 +219,8 @@ size_t kvs_workspace_bytes(kvs_op op, const kvs_cache* cache, const kvs_round* r
       return (size_t)s.B * s.Hkv * kvs::sel_stride_ints(r.P) * sizeof(int32_t);
     case KVS_OP_DECODE:
       return kvs::decode_workspace_bytes(s);
+    default:
+      break;
   }
   return 0;
 }
@@ -515,6 +517,7 @@ const char* kvs_status_str(kvs_status s) {
     case KVS_ERR_INFEASIBLE: return "KVS_ERR_INFEASIBLE";
     case KVS_ERR_WORKSPACE: return "KVS_ERR_WORKSPACE";
     case KVS_ERR_HIP: return "KVS_ERR_HIP";
+    default: break;
   }
   return "KVS_ERR_UNKNOWN";
 }

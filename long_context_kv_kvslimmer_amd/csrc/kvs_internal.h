@@ -11,12 +11,15 @@ namespace kvs {
 void mark_before(hipStream_t st, const char* name);
 void mark_after(hipStream_t st);
 
-// Launch with timing marks around it.
+// Launch with timing marks around it.  Used only inside functions that return hipError_t:
+// a launch that fails returns its error at once, so a later successful launch cannot hide it.
 #define KVS_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                 \
   do {                                                                           \
     ::kvs::mark_before((stream), (name));                                        \
     hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);         \
+    const hipError_t kvs_launch_err_ = hipGetLastError();                        \
     ::kvs::mark_after((stream));                                                 \
+    if (kvs_launch_err_ != hipSuccess) return kvs_launch_err_;                   \
   } while (0)
 
 constexpr int kChunkPairs = 64;      // pairs per compaction chunk (one wavefront)

@@ -496,7 +496,8 @@ static hipError_t launch_score_valu(const Shape& s, const RoundP& r, const P1Arg
   const int64_t BH = (int64_t)s.B * s.Hkv;
   const int nqb = (int)((p1.GW + 127) / 128);
   KVS_LAUNCH("score_pass1", (pass1_valu_kernel<T, D>), dim3(p1.nsplit, nqb, BH), dim3(256), 0, st, p1);
-  launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st);
+  hipError_t e = launch_combine(p1.part, BH * p1.GW, p1.nsplit, D, lse, O, st);
+  if (e != hipSuccess) return e;
   if (ca.cos && r.P > 0) {
     constexpr int GPB = 256 / (D / Elt<T>::kPerChunk);
     KVS_LAUNCH("pair_cos", (pair_cos_kernel<T, D>), dim3((r.P + GPB - 1) / GPB, BH), dim3(256), 0, st, ca);
