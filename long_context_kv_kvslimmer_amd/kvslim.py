@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvslim.so")
+# KVSLIM_LIBRARY names another build of the same library (for instance one with the host
+# code under AddressSanitizer); the in-tree build is the default.
+LIB_PATH = os.environ.get("KVSLIM_LIBRARY") or os.path.join(_PKG, "libkvslim.so")
 
 KVS_OK, KVS_ERR_NULL, KVS_ERR_SHAPE, KVS_ERR_DTYPE, KVS_ERR_STRIDE, KVS_ERR_ALIGN, \
     KVS_ERR_INFEASIBLE, KVS_ERR_WORKSPACE, KVS_ERR_HIP = range(9)
