@@ -19,9 +19,20 @@ struct Dma {
   static constexpr int IPW = TILEB / 1024 / kW2;   // such loads per wave per K (or V) tile
 };
 
+// Position of row r's 16-byte chunks: chunk c sits at c ^ swz(r).  The XOR masks are linear
+// in the row bits and were chosen by measuring LDS bank conflicts (SQ_LDS_BANK_CONFLICT) of
+// every read pattern these kernels use: 16 rows x 4 chunks per 16x16x32 MFMA operand (pass 2,
+// decode), 32 rows x 2 chunks per 32x32x16 operand (pass 1), the transposed V reads of pass 1
+// and of the decode, and whole-row reads (merge, cosine).  At D = 128 all of them are
+// conflict-free; at D = 64 all but the whole-row reads.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  if constexpr (D == 128) {
+    // row bits 0..3 -> masks 0xE, 0x8, 0xB, 0x4
+    return ((r & 1) ? 0xE : 0) ^ ((r & 2) ? 0x8 : 0) ^ ((r & 4) ? 0xB : 0) ^ ((r & 8) ? 0x4 : 0);
+  } else {
+    return (r ^ ((r & 2) << 1)) & 7;
+  }
 }
 
 // byte offset of 16-byte chunk c of row r inside a tile
