@@ -307,11 +307,13 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     }
   };
 
-  // softmax of one tile from its logits, with no branch: the reference maximum m rises only
-  // when the tile maximum exceeds it by more than 2^8 (then corr = 2^(m_old - m_new) < 1,
-  // otherwise corr = 1 exactly); the caller rescales the output accumulators by corr.
-  // P^T operands come out as bf16 hi + lo for two 16-slot k steps.
-  auto softmax = [&](const float (&e)[16], float sc, bf16x8_t (&phi)[2], bf16x8_t (&plo)[2], float& corr) {
+  // softmax of one tile from its logits, with no branch, in two halves that run beside the
+  // two blocks of matrix products: the reference maximum m rises only when the tile maximum
+  // exceeds it by more than 2^8 (then corr = 2^(m_old - m_new) < 1, otherwise corr = 1
+  // exactly); the caller rescales the output accumulators by corr.  The first half finds
+  // the maximum and the first eight probabilities, the second the other eight, the sum and
+  // the P^T operands as bf16 hi + lo for two 16-slot k steps.
+  auto softmax_a = [&](const float (&e)[16], float sc, float (&p)[16], float& corr) {
     float mx = e[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, e[i]);
@@ -319,9 +321,13 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     const float mn = mx > m + kLazyMax ? mx : m;
     corr = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
-    float p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(e[i], sc, -m));
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(e[i], sc, -m));
+  };
+  auto softmax_b = [&](const float (&e)[16], float sc, float (&p)[16], float corr, bf16x8_t (&phi)[2],
+                       bf16x8_t (&plo)[2]) {
+#pragma unroll
+    for (int i = 8; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(e[i], sc, -m));
     float ls = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) ls += p[i];
@@ -399,21 +405,30 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
       read_vt(t + kRing2 - 1, 0, vop[0]);
       read_vt(t + kRing2 - 1, 1, vop[1]);
       __builtin_amdgcn_sched_barrier(0);
+      // S^T of tile t + 1 (a chain of dependent products) beside the first half of the
+      // softmax; the maximum starts while the operand reads land
       f32x16_t s_next;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s_next[i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) s_next = mfma32(ka[ks], qop[ks], s_next);
-      bf16x8_t phi[2], plo[2];
-      float corr;
-      softmax(e, sc, phi, plo, corr);
-      pv(vop, pphi, pplo);
-      // the softmax starts while the operand reads land, then MFMAs and softmax alternate
-      __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+      float p[16], corr;
+      softmax_a(e, sc, p, corr);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
 #pragma unroll
-      for (int i = 0; i < KS + 4 * DB; ++i) {
+      for (int i = 0; i < KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // then softmax instructions
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then softmax instructions
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // O^T += V^T . P^T of tile t - 1 (four independent chains) beside the second half
+      bf16x8_t phi[2], plo[2];
+      softmax_b(e, sc, p, corr, phi, plo);
+      pv(vop, pphi, pplo);
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       // the softmax results are needed here, so nothing of it sinks below the branch
