@@ -150,7 +150,8 @@ def summarize_counters(fetch_csv, write_csv, cmd):
 
 def summarize_trace(stats_csv, bench_json, cmd):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run of bench.py next to the
-    per-kernel HIP-event times the same run printed."""
+    per-kernel HIP-event times of a bench.py run with the same arguments and no profiler
+    (under the profiler the event-timed launches read a few microseconds long)."""
     import csv
     rows = {}
     for r in csv.DictReader(open(stats_csv)):
@@ -161,8 +162,10 @@ def summarize_trace(stats_csv, bench_json, cmd):
     line = json.loads([l for l in open(bench_json).read().splitlines() if l.startswith("{")][-1])
     ev = line.get("kernels_ranked", {})
     out = ["# Kernel durations, C2 layer (32K ctx, 8x128 KV heads, bf16)", "", "Made by:", "", "```", cmd, "```",
-           "", "rocprofv3 averages over every launch in the run; HIP-event medians over the ranking steps (every "
-           "launch marked, after the warm-up).", "",
+           "", "rocprofv3 averages over every launch of the profiled run.  The HIP-event columns and the last "
+           "line come from a run of the same bench.py command without the profiler: medians over the ranking "
+           "steps (every launch timed by its own start/stop events, after the warm-up), and the roofline object "
+           "of the timed region (only the dominant kernel timed).", "",
            "| kernel | launches | rocprofv3 avg us | HIP-event median us | algorithmic MB | GB/s (events) |",
            "|---|---:|---:|---:|---:|---:|"]
     for lab, (c, t) in sorted(rows.items(), key=lambda kv: -kv[1][1]):

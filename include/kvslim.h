@@ -342,11 +342,13 @@ kvs_status kvs_decode_attn_static(const kvs_cache* cache, kvs_dtype dtype,
 /* Kernel timing marks (instrumentation, off by default).
  *
  * kvs_marks_begin(max_launches, label): from now on, on the calling thread, the library
- * records a HIP event on a launch's stream just before and just after each of its kernel
- * launches whose label equals `label` (every launch if `label` is NULL or ""), for the
- * first `max_launches` such launches.  Labels: "score_pass1", "score_pass2", "combine",
- * "qsum", "pair_cos", "select", "merge_compact", "decode",
- * "append", "pack", "exact_e", "spectral_proj", "spectral_pair".  The events are owned by
+ * times each of its kernel launches whose label equals `label` (every launch if `label` is
+ * NULL or ""), for the first `max_launches` such launches: a marked launch goes through
+ * hipExtLaunchKernelGGL with a start and a stop HIP event, which the runtime records at the
+ * kernel's own dispatch boundaries on the launch's stream.  Labels: "score_pass1",
+ * "score_pass2", "score_pass2_merge", "combine", "qsum", "pair_cos", "select",
+ * "merge_compact", "decode", "append", "pack", "exact_e", "spectral_proj",
+ * "spectral_pair".  The events are owned by
  * the library (a per-thread pool created with hipEventDisableSystemFence, grown on demand
  * and kept until the process ends).  Errors: KVS_ERR_SHAPE if max_launches is outside
  * [1, 65536] or the label is longer than 63 bytes; KVS_ERR_HIP if an event cannot be made.

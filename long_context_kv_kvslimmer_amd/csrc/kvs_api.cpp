@@ -85,7 +85,7 @@ kvs_status check_round(const kvs_round* r, const kvs::Shape& s, kvs::RoundP& rp,
 // timing marks (kvs_marks_begin): library-owned HIP events, thread-local, off by default
 constexpr int kMaxMarks = 1 << 16;
 struct Marks {
-  std::vector<hipEvent_t> ev;           // 2 per marked launch: before, after
+  std::vector<hipEvent_t> ev;           // 2 per marked launch: start, stop
   std::vector<const char*> names;
   int cap = 0;                          // launches that fit the event pool
   int k = 0;                            // launches marked so far
@@ -98,21 +98,17 @@ thread_local Marks g_marks;
 
 namespace kvs {
 
-void mark_before(hipStream_t st, const char* name) {
+void mark_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   Marks& m = g_marks;
+  *start = *stop = nullptr;
   if (!m.on || m.k >= m.cap) return;
   if (m.filter[0] && std::strcmp(m.filter, name) != 0) return;
-  if (hipEventRecord(m.ev[2 * m.k], st) != hipSuccess) return;
+  *start = m.ev[2 * m.k];
+  *stop = m.ev[2 * m.k + 1];
   m.names[m.k] = name;
-  m.k = -m.k - 1;                       // pending: the matching mark_after completes it
 }
 
-void mark_after(hipStream_t st) {
-  Marks& m = g_marks;
-  if (!m.on || m.k >= 0) return;
-  const int k = -m.k - 1;
-  m.k = (hipEventRecord(m.ev[2 * k + 1], st) == hipSuccess) ? k + 1 : k;
-}
+void mark_commit() { ++g_marks.k; }
 
 }  // namespace kvs
 
@@ -140,7 +136,6 @@ kvs_status kvs_marks_begin(int32_t max_launches, const char* label) {
 int32_t kvs_marks_end(void) {
   Marks& m = g_marks;
   m.on = false;
-  if (m.k < 0) m.k = -m.k - 1;
   return m.k;
 }
 

@@ -1,25 +1,34 @@
 // Host-side launch interface between the C-ABI layer (kvs_api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace kvs {
 
-// Timing marks (see kvs_set_marks): before / after every kernel launch.
-void mark_before(hipStream_t st, const char* name);
-void mark_after(hipStream_t st);
+// Timing marks (kvs_marks_begin): the start and stop events for the next launch of kernel
+// `name`, or null when that launch is not marked; mark_commit counts the launch once it is
+// issued.  A marked launch goes through hipExtLaunchKernelGGL, which records the two events
+// at the kernel's own dispatch boundaries, so the events time the kernel alone.
+void mark_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
+void mark_commit();
 
-// Launch with timing marks around it.  Used only inside functions that return hipError_t:
-// a launch that fails returns its error at once, so a later successful launch cannot hide it.
-#define KVS_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                 \
-  do {                                                                           \
-    ::kvs::mark_before((stream), (name));                                        \
-    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);         \
-    const hipError_t kvs_launch_err_ = hipGetLastError();                        \
-    ::kvs::mark_after((stream));                                                 \
-    if (kvs_launch_err_ != hipSuccess) return kvs_launch_err_;                   \
+// Launch (with timing marks when they are on).  Used only inside functions that return
+// hipError_t: a launch that fails returns its error at once, so a later successful launch
+// cannot hide it.
+#define KVS_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                          \
+  do {                                                                                    \
+    hipEvent_t kvs_e0_ = nullptr, kvs_e1_ = nullptr;                                      \
+    ::kvs::mark_events((name), &kvs_e0_, &kvs_e1_);                                       \
+    if (kvs_e0_)                                                                          \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, kvs_e0_, kvs_e1_, 0u, __VA_ARGS__); \
+    else                                                                                  \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                \
+    const hipError_t kvs_launch_err_ = hipGetLastError();                                 \
+    if (kvs_launch_err_ != hipSuccess) return kvs_launch_err_;                            \
+    if (kvs_e0_) ::kvs::mark_commit();                                                    \
   } while (0)
 
 constexpr int kChunkPairs = 64;      // pairs per compaction chunk (one wavefront)
