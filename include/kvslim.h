@@ -39,7 +39,13 @@
  *  - Arguments are validated before anything is enqueued; on a validation error nothing is
  *    written.  A failed kernel launch returns KVS_ERR_HIP; outputs are then undefined.
  *    kvs_last_error() gives a message for the last failure on the calling thread.
- *  - Floating point: inputs bf16 or fp32, all arithmetic and every statistic in fp32.
+ *  - Floating point: inputs bf16 or fp32; every sum and statistic accumulates in fp32.  On
+ *    bf16 caches the matrix products take 16-bit operands: Q, K and V as given, P (decode)
+ *    and -2O (second scorer pass) as bf16 hi + lo pairs (~16 significant bits), and in the
+ *    scorer's first pass, which forms the window output O, P and V as f16 (11 significant
+ *    bits; O within ~3e-4 of exact, relative to the row's largest element).  V must then
+ *    be finite with |v| <= 65504 (f16's range); values below 2^-14 keep f16's absolute
+ *    precision of 2^-24.
  *
  * Cache layout (kvs_cache).  K and V of one (batch b, kv-head h) are n_slots rows of
  * head_dim contiguous elements, starting at element offset b*stride_b + h*stride_h.

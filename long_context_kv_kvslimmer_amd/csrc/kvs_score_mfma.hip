@@ -1,18 +1,18 @@
 // bf16 MFMA scorer for gfx950 (the math is stated in kvs_score.hip).
 //
-// Both passes tile one (batch, kv-head) as [window queries] x [slots]; a workgroup owns a
-// contiguous slot chunk and up to 128 window queries, four waves of 32 queries each, and
-// stages 64-slot K and V tiles in LDS (row pitch padded to keep ds_read_b128 conflict-free).
-// All contractions run on v_mfma_f32_16x16x32_bf16, always in the transposed form
-// (slots or head-dim as the M side, queries as the N side) so that every lane's results
-// belong to ONE query, lane % 16:
+// Both passes tile one (batch, kv-head) as [window queries] x [slots]: a workgroup owns a
+// contiguous slot chunk and up to 128 window queries, and streams 32-slot K and V tiles
+// through LDS rings (16-byte buffer loads written straight to LDS, rows XOR-swizzled).
+// Every contraction runs in transposed form (slots or head-dim as the M side, queries as
+// the N side), so each lane's results belong to one query:
 //
-//   S^T[slot, q]  = K . Q^T            A = K tile rows (ds_read_b128), B = Q rows (registers)
-//   pass 1:  O^T[d, q] += V^T . P^T    A = V^T via ds_read_tr16_b64 (LDS transpose read),
-//                                      B = P^T straight from the S^T registers; P is split
-//                                      into bf16 hi + lo parts so the product keeps ~16 bits
-//   pass 2:  R^T[slot, q] = V . (-2 O)^T + ||v||^2 + ||o||^2   (accumulator pre-loaded),
-//                                      giving ||v_i - o_w||^2 directly; -2 O split hi + lo
+//   pass 1 (v_mfma_f32_32x32x16):  S^T[slot, q] = K . Q^T in bf16, then
+//            O^T[d, q] += V^T . P^T in f16: V^T by LDS transpose reads of the tile, which
+//            the group converts to f16 in place once it has landed, P^T straight from the
+//            S^T registers
+//   pass 2 (v_mfma_f32_16x16x32_bf16):  S[q, slot] = Q . K^T and
+//            R^T[slot, q] = V . (-2 O)^T + ||o||^2 (+ ||v||^2), giving ||v_i - o_w||^2;
+//            -2 O is split into bf16 hi + lo parts so the product keeps ~16 bits
 //
 // Pass 1 also writes the adjacent-key cosine (the shared pair_cos routine on LDS rows in
 // row layout), so the merge pass can recompute bit-identical values.
@@ -27,6 +27,8 @@ namespace kvs {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -69,11 +71,36 @@ __device__ __forceinline__ void split_hi_lo(const float* x, bf16x8_t& hi, bf16x8
   lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
+// 8 floats to f16, round to nearest even (two elements per conversion).
+__device__ __forceinline__ f16x8_t to_f16x8(const float* x) {
+  f16x8_t r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (_Float16)x[j];
+  return r;
+}
+
+// 8 bf16 (16 bytes) to 8 f16 in the same positions: exact for |x| in f16's normal range
+// [2^-14, 65504], rounded to f16's grid below it, infinite above.
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  f16x8_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[2 * j] = (_Float16)bf16_lo(w[j]);
+    r[2 * j + 1] = (_Float16)bf16_hi(w[j]);
+  }
+  const u32x4_t v = __builtin_bit_cast(u32x4_t, r);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ------------------------------------------------------------------ tiling ----
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32(const f16x8_t& a, const f16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Q rows as a 32x32x16 operand: lane l holds row[q][16 ks + 8 (l / 32) .. +7] of query q.
@@ -109,8 +136,9 @@ __device__ __forceinline__ float sum_halves(float x) {
 // each lane's accumulators belong to one query.  The QK product of tile t + 1 is issued
 // before the softmax of tile t so that the matrix cores run while the vector units work.
 // The running maximum is raised only when it grows by more than 2^8 (P <= 256 in
-// between), which makes rescales of the output accumulators rare.  P is split into bf16
-// hi + lo parts; O^T += V^T . P^T reads V^T with LDS transpose reads.
+// between), which makes rescales of the output accumulators rare.  O^T += V^T . P^T takes
+// f16 operands: P^T from the softmax, V^T by LDS transpose reads of the tile, which the
+// group converts to f16 in place in the iteration its loads land.
 constexpr int kGroupWaves = 4;
 constexpr int kGroups = 2;
 constexpr int kGT = 64 * kGroupWaves;              // threads per group
@@ -202,19 +230,26 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     }
   };
 
-  // Wait at the top of iteration t until K(t + 1) has landed (and with it every earlier
-  // load, V(t - 1) included); issued after K(t + 1) are V(t), K(t + 2) if it exists, and
-  // V(t + 1).  In the last iteration everything is awaited (V(t) feeds the final product).
+  // Wait at the top of iteration t until V(t) has landed (and with it every earlier load,
+  // K(t + 1) included: it was issued just before V(t)); issued after V(t) are K(t + 2) if
+  // it exists and V(t + 1) if it exists.  V(t) is converted to f16 in this iteration.
   const bool nload = HAS_N && gw == 0;   // this wave also loads the counts with each K tile
   auto wait_top = [&](int t) {
     if (t + 1 >= nt) {
       wait_vm<0>();
     } else if (t + 2 < nt) {
-      if (nload) wait_vm<3 * M::IPW + 1>();
-      else wait_vm<3 * M::IPW>();
+      if (nload) wait_vm<2 * M::IPW + 1>();
+      else wait_vm<2 * M::IPW>();
     } else {
-      wait_vm<2 * M::IPW>();
+      wait_vm<M::IPW>();
     }
+  };
+  // V tile t to f16 in place, element by element (the swizzled chunk positions stay), by
+  // the group's threads: the O^T product takes V^T and P^T as f16 operands
+  auto v_to_f16 = [&](int t) {
+    uint4* V_ = reinterpret_cast<uint4*>(vr_g + (t % kRing2) * M::TILEB);
+#pragma unroll
+    for (int i = 0; i < M::TILEB / 16 / kGT; ++i) V_[gt + i * kGT] = bf16x8_to_f16x8(V_[gt + i * kGT]);
   };
 
   // K(0), K(1), V(0) and the query operands travel together (loads complete in order, so
@@ -312,7 +347,8 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
   // exceeds it by more than 2^8 (then corr = 2^(m_old - m_new) < 1, otherwise corr = 1
   // exactly); the caller rescales the output accumulators by corr.  The first half finds
   // the maximum and the first eight probabilities, the second the other eight, the sum and
-  // the P^T operands as bf16 hi + lo for two 16-slot k steps.
+  // the P^T operands in f16 for two 16-slot k steps (11-bit significands: P <= 2^8 stays in
+  // f16's range, and the product keeps O within ~3e-4 of exact on these shapes).
   auto softmax_a = [&](const float (&e)[16], float sc, float (&p)[16], float& corr) {
     float mx = e[0];
 #pragma unroll
@@ -324,8 +360,7 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(e[i], sc, -m));
   };
-  auto softmax_b = [&](const float (&e)[16], float sc, float (&p)[16], float corr, bf16x8_t (&phi)[2],
-                       bf16x8_t (&plo)[2]) {
+  auto softmax_b = [&](const float (&e)[16], float sc, float (&p)[16], float corr, f16x8_t (&pf)[2]) {
 #pragma unroll
     for (int i = 8; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(e[i], sc, -m));
     float ls = 0.f;
@@ -333,37 +368,36 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
     for (int i = 0; i < 16; ++i) ls += p[i];
     lsum = __builtin_fmaf(lsum, corr, ls);
     // k index (h, j) of step ks <-> slot 16 ks + 8 (j / 4) + 4 h + j % 4: the lane's p[8 ks + j]
-    split_hi_lo(p, phi[0], plo[0]);
-    split_hi_lo(p + 8, phi[1], plo[1]);
+    pf[0] = to_f16x8(p);
+    pf[1] = to_f16x8(p + 8);
   };
 
   // V^T operands of one 16-slot k step by transposed reads: source lane i = lane % 16 points
   // at row r0 + i / 4 (and + 8), columns 32 db + 16 (G16 % 2) + 4 (i % 4); lane t receives
   // column + t of 4 consecutive rows
-  auto read_vt = [&](int t, int ks, bf16x8_t (&vop)[DB]) {
+  auto read_vt = [&](int t, int ks, f16x8_t (&vop)[DB]) {
     const uint8_t* V_ = vr_g + (t % kRing2) * M::TILEB;
     const int r0 = ks * 16 + 4 * h + (t16 >> 2);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+      typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
+      typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
       const int col = db * 32 + 16 * (G16 & 1) + 4 * (t16 & 3);
       const int cb = (col & 7) * 2;
-      const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(V_ + chunk_off<D>(r0, col >> 3) + cb));
-      const bf16x4_t v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(V_ + chunk_off<D>(r0 + 8, col >> 3) + cb));
+      const f16x4_t v0 = __builtin_bit_cast(
+          f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(V_ + chunk_off<D>(r0, col >> 3) + cb)));
+      const f16x4_t v1 = __builtin_bit_cast(
+          f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(V_ + chunk_off<D>(r0 + 8, col >> 3) + cb)));
       vop[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
 
-  // O^T += V^T . P^T of one tile
-  auto pv = [&](const bf16x8_t (&vop)[2][DB], const bf16x8_t (&phi)[2], const bf16x8_t (&plo)[2]) {
+  // O^T += V^T . P^T of one tile (f16 operands)
+  auto pv = [&](const f16x8_t (&vop)[2][DB], const f16x8_t (&pf)[2]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        acc[db] = mfma32(vop[ks][db], phi[ks], acc[db]);
-        acc[db] = mfma32(vop[ks][db], plo[ks], acc[db]);
-      }
+      for (int db = 0; db < DB; ++db) acc[db] = mfma32(vop[ks][db], pf[ks], acc[db]);
   };
 
   // Software pipeline: iteration t computes the softmax of tile t on the vector units while
@@ -373,15 +407,11 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
   __syncthreads();   // K(0) of both groups is in (each wave waited on its own loads)
   f32x16_t s_cur;
   if (nt > 0) s_cur = qk(0);
-  bf16x8_t pphi[2], pplo[2];
-  {
-    const uint4 zero = make_uint4(0, 0, 0, 0);
+  f16x8_t pp[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      pphi[ks] = as_bf16x8(zero);
-      pplo[ks] = as_bf16x8(zero);
-    }
-  }
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pp[ks][j] = (_Float16)0.f;
   for (int t = 0; t < nt0; ++t) {
     const bool act = t < nt;
     if (act) wait_top(t);
@@ -395,7 +425,8 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
       logits(t, s_cur, e, sc);
       // operands: K rows of tile t + 1 (stale past the last tile; that product is unused)
       // and V^T of tile t - 1 (stale in the first iteration, where P^T is zero)
-      bf16x8_t ka[KS], vop[2][DB];
+      bf16x8_t ka[KS];
+      f16x8_t vop[2][DB];
       {
         const uint8_t* K_ = kr_g + ((t + 1) % kRing2) * M::TILEB;
 #pragma unroll
@@ -418,38 +449,38 @@ __global__ __launch_bounds__(kThreads, 2 / kGroups) void p1_mfma_kernel(P1Args a
 #pragma unroll
       for (int i = 0; i < KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then softmax instructions
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then softmax instructions
       }
       __builtin_amdgcn_sched_barrier(0);
-      // O^T += V^T . P^T of tile t - 1 (four independent chains) beside the second half
-      bf16x8_t phi[2], plo[2];
-      softmax_b(e, sc, p, corr, phi, plo);
-      pv(vop, pphi, pplo);
+      // O^T += V^T . P^T of tile t - 1 (independent chains) beside the second half, and
+      // V(t), landed at the top of this iteration, to f16 (it is read in the next one)
+      f16x8_t pf[2];
+      softmax_b(e, sc, p, corr, pf);
+      pv(vop, pp);
+      v_to_f16(t);
 #pragma unroll
-      for (int i = 0; i < 4 * DB; ++i) {
+      for (int i = 0; i < 2 * DB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       // the softmax results are needed here, so nothing of it sinks below the branch
-      asm volatile("" ::"v"(phi[0]), "v"(phi[1]), "v"(plo[0]), "v"(plo[1]), "v"(lsum));
+      asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(lsum));
       if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] *= corr;
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        pphi[ks] = phi[ks];
-        pplo[ks] = plo[ks];
-      }
+      for (int ks = 0; ks < 2; ++ks) pp[ks] = pf[ks];
       s_cur = s_next;
     }
   }
+  __syncthreads();   // V(nt - 1), converted in the last iteration by the whole group
   if (nt > 0) {
-    bf16x8_t vop[2][DB];
+    f16x8_t vop[2][DB];
     read_vt(nt - 1, 0, vop[0]);
     read_vt(nt - 1, 1, vop[1]);
-    pv(vop, pphi, pplo);
+    pv(vop, pp);
   }
 
   // merge the two groups' running states through LDS, then write the partial records with

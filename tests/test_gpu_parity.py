@@ -260,3 +260,21 @@ def test_c2_full_layer_sampled_heads():
         print(f"\n[C2] head {h}", flush=True)
         check_round_slice(bufs, K, V, None, Qw, 0, h, cfg.n_slots, cfg.n_sink, cfg.n_recent, M,
                           1 / math.sqrt(cfg.head_dim), label=f"C2 h{h}")
+
+
+@pytest.mark.parametrize("vscale", [3000.0, 1e-4])
+def test_value_range_of_the_f16_output_product(vscale):
+    """The first scorer pass forms O from f16 probabilities and f16 values: values scaled
+    up toward f16's largest normal and down into its subnormal range still give a round
+    within the usual tolerance of the oracle (full and partial rounds, counts on)."""
+    from long_context_kv_kvslimmer_amd import pipeline
+    B, Hkv, Hq, D, N, W, S, R = 1, 2, 8, 128, 1200, 16, 2, 6
+    K, V, n, Qw = make_inputs(5150, B, Hkv, Hq, D, N, N, W, torch.bfloat16, True)
+    V = (V.float() * vscale).clamp(-60000.0, 60000.0).to(torch.bfloat16)
+    print(f"\n[f16 range] scale {vscale}, max |V| {V.float().abs().max().item():.3g}", flush=True)
+    P = O.num_pairs(N, S, R)
+    for M in (P, 150):
+        bufs = pipeline.merge_round(K, V, n, Qw, Hq, W, S, R, M, n_slots=N, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        for h in range(Hkv):
+            check_round_slice(bufs, K, V, n, Qw, 0, h, N, S, R, M, 1 / math.sqrt(D), label=f"x{vscale} M{M} h{h}")
