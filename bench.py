@@ -195,10 +195,11 @@ def summarize_stats(stats_csv, title, cmd):
 
 
 def summarize_mfma(sq_csv, stats_csv, cmd):
-    """Markdown summary of a rocprofv3 --pmc run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and
-    SQ_VALU_MFMA_BUSY_CYCLES (per-dispatch sums over the chip) next to each kernel's mean
-    duration from a kernel-trace run: bf16 MFMA work per launch, achieved rate against the
-    dense bf16 peak, and matrix-core busy cycles per SIMD against the launch duration."""
+    """Markdown summary of a rocprofv3 --pmc run with SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    SQ_INSTS_VALU_MFMA_MOPS_F16 and SQ_VALU_MFMA_BUSY_CYCLES (per-dispatch sums over the
+    chip) next to each kernel's mean duration from a kernel-trace run: 16-bit MFMA work per
+    launch (bf16 and f16 products, which have the same dense peak), achieved rate against
+    that peak, and matrix-core busy cycles per SIMD against the launch duration."""
     import csv
     import statistics
     per = {}
@@ -214,24 +215,26 @@ def summarize_mfma(sq_csv, stats_csv, cmd):
             dur[lab] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
     out = ["# MFMA work and utilisation of the scorer, C2 layer (32K ctx, 8x128 KV heads, bf16)", "", "Made by:", "",
            "```", cmd, "```", "",
-           f"Peak: dense bf16 MFMA {PEAK_MFMA_BF16_TFLOPS} TFLOP/s; {SIMDS} SIMDs at {PEAK_CLOCK_GHZ} GHz.  FLOP per "
-           "launch = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the counter's unit).  Busy = SQ_VALU_MFMA_BUSY_CYCLES / "
-           "SIMDs / (mean duration x peak clock).", "",
-           "| kernel | MFMA instructions | GFLOP per launch | mean us | TFLOP/s | of peak | MFMA busy per SIMD |",
-           "|---|---:|---:|---:|---:|---:|---:|"]
+           f"Peak: dense bf16 / f16 MFMA {PEAK_MFMA_BF16_TFLOPS} TFLOP/s; {SIMDS} SIMDs at {PEAK_CLOCK_GHZ} GHz.  FLOP "
+           "per launch = (SQ_INSTS_VALU_MFMA_MOPS_BF16 + SQ_INSTS_VALU_MFMA_MOPS_F16) x 512 (the counters' unit).  "
+           "Busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / (mean duration x peak clock).", "",
+           "| kernel | MFMA instructions | bf16 GFLOP | f16 GFLOP | GFLOP per launch | mean us | TFLOP/s | of peak | "
+           "MFMA busy per SIMD |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for lab in sorted({k[0] for k in per}):
-        mops = per.get((lab, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
-        if not mops or statistics.mean(mops) == 0 or lab not in dur:
+        mb = statistics.mean(per.get((lab, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), [0.0]))
+        mh = statistics.mean(per.get((lab, "SQ_INSTS_VALU_MFMA_MOPS_F16"), [0.0]))
+        if mb + mh == 0 or lab not in dur:
             continue
-        flop = statistics.mean(mops) * 512
+        flop = (mb + mh) * 512
         inst = statistics.mean(per.get((lab, "SQ_INSTS_MFMA"), [float("nan")]))
         busy = statistics.mean(per.get((lab, "SQ_VALU_MFMA_BUSY_CYCLES"), [float("nan")]))
         c, t = dur[lab]
         us = t / c / 1e3
         tf = flop / (us * 1e-6) / 1e12
         frac_busy = busy / SIMDS / (us * 1e-6 * PEAK_CLOCK_GHZ * 1e9)
-        out.append(f"| {lab} | {inst:.0f} | {flop / 1e9:.2f} | {us:.2f} | {tf:.1f} | {tf / PEAK_MFMA_BF16_TFLOPS:.3f} | "
-                   f"{frac_busy:.3f} |")
+        out.append(f"| {lab} | {inst:.0f} | {mb * 512 / 1e9:.2f} | {mh * 512 / 1e9:.2f} | {flop / 1e9:.2f} | {us:.2f} | "
+                   f"{tf:.1f} | {tf / PEAK_MFMA_BF16_TFLOPS:.3f} | {frac_busy:.3f} |")
     return "\n".join(out) + "\n"
 
 
