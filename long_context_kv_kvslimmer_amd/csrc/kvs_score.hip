@@ -247,11 +247,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
 // Few splits and many units (many heads, short caches): one wave per unit, four units per
 // workgroup, no barriers.  Lane l reads the maximum and sum of split l; the wave reduces
 // them; lane l then owns output elements l (and l + 64 at D = 128) and sums the splits in
-// order, the weight of split s read from lane s.
+// order, the weight of split s read from lane s.  The outputs of CH splits are loaded at a
+// time: 8 for up to 16 splits; 32 (every split in one round of loads) for 17 to 32 splits
+// when there are enough units to fill the chip (with few units the workgroup-per-unit
+// kernel is faster).
 constexpr int kCombineWaveMaxSplit = 16;
+constexpr int kCombineWaveMaxSplitWide = 32;
+constexpr int64_t kCombineWaveWideMinUnits = 256;
 constexpr int kCombineWaveUnits = 4;
 
-template <int D>
+template <int D, int CH>
 __global__ __launch_bounds__(64 * kCombineWaveUnits) void combine_wave_kernel(const float* __restrict__ part,
                                                                              int64_t units, int nsplit,
                                                                              float* __restrict__ lse,
@@ -265,9 +270,9 @@ __global__ __launch_bounds__(64 * kCombineWaveUnits) void combine_wave_kernel(co
   // the pack's query chunk does not depend on the splits: load it with them
   const uint4 qch = pk.ops ? pack_query_chunk<D>(pk, u, lane) : make_uint4(0, 0, 0, 0);
   const float2 ml = lane < nsplit ? *reinterpret_cast<const float2*>(r + lane * rs) : make_float2(-INFINITY, 0.f);
-  float o[8][E];
+  float o[CH][E];
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
+  for (int k = 0; k < CH; ++k)
 #pragma unroll
     for (int e = 0; e < E; ++e) o[k][e] = k < nsplit ? r[k * rs + 4 + lane + 64 * e] : 0.f;
   const float M = group_max<64>(ml.x);
@@ -276,15 +281,15 @@ __global__ __launch_bounds__(64 * kCombineWaveUnits) void combine_wave_kernel(co
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+  for (int s0 = 0; s0 < nsplit; s0 += CH) {
     if (s0 > 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
+      for (int k = 0; k < CH; ++k)
 #pragma unroll
         for (int e = 0; e < E; ++e) o[k][e] = s0 + k < nsplit ? r[(s0 + k) * rs + 4 + lane + 64 * e] : 0.f;
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < CH; ++k) {
       if (s0 + k < nsplit) {
         const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s0 + k));
 #pragma unroll
@@ -339,14 +344,19 @@ hipError_t launch_combine(const float* part, int64_t units, int nsplit, int D, f
   if (D > 128) return hipErrorInvalidValue;
   PackP pk{};
   if (pack) pk = *pack;
-  if (nsplit <= kCombineWaveMaxSplit && (D == 64 || D == 128)) {
+  const bool wide = nsplit > kCombineWaveMaxSplit && nsplit <= kCombineWaveMaxSplitWide &&
+                    units >= kCombineWaveWideMinUnits;
+  if ((nsplit <= kCombineWaveMaxSplit || wide) && (D == 64 || D == 128)) {
     const dim3 grid((unsigned)((units + kCombineWaveUnits - 1) / kCombineWaveUnits));
-    if (D == 128)
-      KVS_LAUNCH("combine", combine_wave_kernel<128>, grid, dim3(64 * kCombineWaveUnits), 0, st, part, units, nsplit,
-                 lse, out, pk);
+    const dim3 block(64 * kCombineWaveUnits);
+    if (D == 128 && wide)
+      KVS_LAUNCH("combine", (combine_wave_kernel<128, 32>), grid, block, 0, st, part, units, nsplit, lse, out, pk);
+    else if (D == 128)
+      KVS_LAUNCH("combine", (combine_wave_kernel<128, 8>), grid, block, 0, st, part, units, nsplit, lse, out, pk);
+    else if (wide)
+      KVS_LAUNCH("combine", (combine_wave_kernel<64, 32>), grid, block, 0, st, part, units, nsplit, lse, out, pk);
     else
-      KVS_LAUNCH("combine", combine_wave_kernel<64>, grid, dim3(64 * kCombineWaveUnits), 0, st, part, units, nsplit,
-                 lse, out, pk);
+      KVS_LAUNCH("combine", (combine_wave_kernel<64, 8>), grid, block, 0, st, part, units, nsplit, lse, out, pk);
     return hipGetLastError();
   }
   KVS_LAUNCH("combine", combine_kernel, dim3((unsigned)units), dim3(kCombineThreads), 0, st, part, nsplit, D, lse, out,
