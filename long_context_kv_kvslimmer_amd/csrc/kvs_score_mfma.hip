@@ -32,18 +32,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 64;      // slots per LDS tile
-constexpr int kQB = 128;       // window queries per workgroup
-
-template <int D>
-struct TileCfg {
-  static constexpr int KB = D / 32;          // 32-wide k blocks of the head dim
-  static constexpr int DB = D / 16;          // 16-wide blocks of the head dim
-  // bf16 elements per LDS row: a 32-byte pad moves consecutive rows 8 banks apart, so the
-  // 16-byte row reads (8 lanes per cycle) and the 4-row transpose reads are conflict-free
-  static constexpr int PITCH = D + 16;
-  static constexpr int CPR = D / 8;          // 16-byte chunks per row
-};
+constexpr int kChunk1Unit = 2 * kT2;   // pass-1 chunks: each tile group's half is whole tiles
+constexpr int kQB = 128;               // window queries per workgroup
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
   u32x4_t v = {u.x, u.y, u.z, u.w};
@@ -56,19 +46,6 @@ constexpr float kNoMax = -1e30f;
 
 __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Split 8 floats into bf16 hi (RNE) and lo = bf16(x - hi), two elements per conversion.
-__device__ __forceinline__ void split_hi_lo(const float* x, bf16x8_t& hi, bf16x8_t& lo) {
-  u32x4_t h, l;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t hp = pack_bf16x2(x[2 * j], x[2 * j + 1]);
-    h[j] = hp;
-    l[j] = pack_bf16x2(x[2 * j] - bf16_lo(hp), x[2 * j + 1] - bf16_hi(hp));
-  }
-  hi = __builtin_bit_cast(bf16x8_t, h);
-  lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
 // 8 floats to f16, round to nearest even (two elements per conversion).
@@ -980,7 +957,7 @@ static void mfma_plan(const Shape& s, const RoundP& r, int64_t& base, int64_t& c
   if (want < 1) want = 1;
   int64_t c = (span + want - 1) / want;
   if (c < 512 * kGroups) c = 512 * kGroups;             // keep partial records small
-  c = (c + kTile - 1) / kTile * kTile;
+  c = (c + kChunk1Unit - 1) / kChunk1Unit * kChunk1Unit;
   chunk = c;
   nsplit = (int)((span + c - 1) / c);
 }
