@@ -52,6 +52,8 @@ CASES = [
     ("no-pairs", 1, 1, 1, 64, 40, 40, 2, 32, 8, 0.0, torch.float32, False),
     ("single-slot", 1, 1, 1, 64, 1, 1, 2, 0, 0, 0.0, torch.float32, False),
     ("d64-f32-partial-g4", 1, 2, 8, 64, 4100, 4100, 8, 0, 32, 0.29, torch.float32, True),
+    # 24 pass-1 splits over 256 window-query rows: the wave-per-row combine with every split in one round
+    ("d64-bf16-24-splits", 1, 2, 8, 64, 24000, 24000, 32, 0, 16, 1.0, torch.bfloat16, False),
 ]
 
 
