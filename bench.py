@@ -305,6 +305,30 @@ def summarize_per_config(jsonl, cmd):
         out.append(f"| {r['config']} | {r['batch']} x {r['layers']} | {r['rounds']} | {r['merge_ms_per_layer']} | "
                    f"{r['merge_ms_all_layers']} | {r['merge_tokens_per_s']:.3g} | "
                    f"{r['merge_algorithmic_MB_per_layer']} | {r['merge_GBps']} |")
+    cpu = [r for r in rows if "cpu_oracle" in r]
+    if cpu:
+        c0 = cpu[0]["cpu_oracle"]
+        out += ["", f"CPU oracle on the same layer (fp64 NumPy on the host's {c0['host_cores_available']} cores, "
+                    f"{c0['cpu_model']}; worker threads one per slice up to the cores, one BLAS thread each).  A slice "
+                    "is one (batch item, KV head) through every round of the layer; configs with a sample of slices "
+                    "are scaled to the layer by slices / sample at the sample's thread count (extrapolated).  A "
+                    "reported baseline, not a target.", "",
+                "| config | slices timed | threads | merge | merge s / layer | merge s, all layers | tokens/s | "
+                "GPU speed-up |",
+                "|---|---|---:|---|---:|---:|---:|---:|"]
+        for r in cpu:
+            c = r["cpu_oracle"]
+            out.append(f"| {r['config']} | {c['slices']} | {c['cores']} | {c['merge']} | {c['merge_s_per_layer']} | "
+                       f"{c['merge_s_all_layers']} | {c['merge_tokens_per_s']:.3g} | "
+                       f"{c['merge_s_per_layer'] * 1e3 / r['merge_ms_per_layer']:.0f}x |")
+        for r in cpu:
+            c = r["cpu_oracle"]
+            if "decode_steps" in c:
+                out.append("")
+                out.append(f"CPU oracle decode ({r['config']}): every step of every query head, measured: "
+                           f"{c['decode_ms_per_layer_step']} ms per layer-step, {c['decode_ms_per_step_all_layers']} "
+                           f"ms per {r['layers']}-layer step ({c['decode_cores']} worker threads); GPU "
+                           f"{r.get('decode_us_per_layer_step', 'n/a')} us per layer-step.")
     out += ["", "Kernel time per layer, summed over the layer's rounds (library event marks, one marked run; each "
                 "mark adds ~1 us):", "", "| config | kernels (us) |", "|---|---|"]
     for r in rows:
@@ -407,6 +431,82 @@ def cpu_baseline(cfg, K, V, Qw, q):
                       f"interpreter lock), {dt:.1f} s"}
 
 
+ORACLE_SLICES = {1: None, 2: None, 3: 2, 4: 2, 5: 2}   # None: every slice of the layer
+
+
+def cpu_oracle_config(cfg, K0, V0, Qws, decode=None):
+    """The oracle as it stands on one layer of a config, on the host cores.  A slice is one
+    (batch item, KV head) chained through every merge round of the layer (each round's input
+    is the oracle's own output of the round before).  Slices run on a pool of worker threads
+    (one per host core the process may use, at most one per slice), one BLAS thread each.
+    C1 and C2 time every slice of the layer ("measured"); the larger configs time a seeded
+    sample of slices and scale the layer by slices / sample ("extrapolated").  `decode`:
+    the merged cache, slot counts and per-step queries the GPU decoded; every step of every
+    query head runs, in full.  The model-wide figures multiply by the layers, as the GPU's."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kvs_oracle as O
+    G, D = cfg.group, cfg.head_dim
+    scale = 1 / math.sqrt(D)
+    total = cfg.batch * cfg.kv_heads
+    want = ORACLE_SLICES.get(cfg.idx)
+    pairs = [(b, h) for b in range(cfg.batch) for h in range(cfg.kv_heads)]
+    if want is not None and want < total:
+        rs = np.random.RandomState(1000 + cfg.idx)
+        pairs = [pairs[i] for i in sorted(rs.choice(total, want, replace=False))]
+    cores = len(os.sched_getaffinity(0))
+    slices = [(K0[b, h].double().cpu().numpy(), V0[b, h].double().cpu().numpy(),
+               [Qw[b, h * G:(h + 1) * G].double().cpu().numpy().reshape(-1, D) for Qw in Qws]) for b, h in pairs]
+
+    def chain(sl):
+        Ks, Vs, Qs = sl
+        ns = None
+        for Qr, M in zip(Qs, cfg.rounds):
+            r = O.merge_round(Ks, Vs, ns, Qr, scale, cfg.n_sink, cfg.n_recent, M)
+            Ks, Vs, ns = r.K, r.V, r.n
+
+    workers = max(1, min(len(slices), cores))
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(chain, slices))
+    wall = time.perf_counter() - t0
+    measured = len(slices) == total
+    layer_s = wall if measured else wall * total / len(slices)
+    tokens = cfg.batch * cfg.n_slots
+    res = {"kind": "oracle", "slices": f"{len(slices)} of {total} (batch, KV head) slices per layer",
+           "merge": "measured" if measured else "extrapolated", "sample_wall_s": round(wall, 2),
+           "merge_s_per_layer": round(layer_s, 2), "merge_s_all_layers": round(layer_s * cfg.layers, 1),
+           "merge_tokens_per_s": round(tokens / layer_s, 1), "cores": workers, "host_cores_available": cores,
+           "cpu_model": cpu_model()}
+    if decode is not None:
+        Kc, Vc, nc, qs, slot_counts = decode
+        Kh = [Kc[0, h].double().cpu().numpy() for h in range(cfg.kv_heads)]
+        Vh = [Vc[0, h].double().cpu().numpy() for h in range(cfg.kv_heads)]
+        nh = [nc[0, h].cpu().numpy().astype(np.int64) for h in range(cfg.kv_heads)]
+        qh = [q[0].double().cpu().numpy() for q in qs]
+
+        def head(hq):
+            h = hq // G
+            for t, Nt in enumerate(slot_counts):
+                O.decode(Kh[h][:Nt], Vh[h][:Nt], nh[h][:Nt], qh[t][hq], scale)
+
+        dw = max(1, min(cfg.q_heads, cores))
+        t0 = time.perf_counter()
+        with threadpool_limits(1):
+            with ThreadPoolExecutor(max_workers=dw) as ex:
+                list(ex.map(head, range(cfg.q_heads)))
+        dt = time.perf_counter() - t0
+        res.update({"decode": "measured", "decode_steps": len(slot_counts),
+                    "decode_ms_per_layer_step": round(dt * 1e3 / len(slot_counts), 3),
+                    "decode_ms_per_step_all_layers": round(dt * 1e3 / len(slot_counts) * cfg.layers, 2),
+                    "decode_cores": dw})
+    return res
+
+
 def gpu_clock_info():
     """Peak shader clock (HIP device attribute, kHz -> MHz) and, where the driver's sysfs
     table is readable, the current shader clock level; ROCm and HIP versions."""
@@ -459,12 +559,13 @@ def dominant_kernel(ranked):
     return max(ranked, key=lambda n: ranked[n]["ms_per_step"]) if ranked else None
 
 
-def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016)):
+def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016), cpu=True):
     """Per-config GPU timings (not the bench line): every merge round of one layer of each
     seeded workload through kvs_score_merge (one call per round), timed with
     events on the library's stream over `reps` repetitions after one warm-up; all layers of a
     config have the same shape, so the whole-model time is the per-layer time x layers.  The
-    decode workload (C5) appends one token per step and times each kvs_decode_attn."""
+    decode workload (C5) appends one token per step and times each kvs_decode_attn.  With
+    `cpu`, the oracle is timed on the same layer (cpu_oracle_config) after the GPU."""
     import statistics
     import torch
     from long_context_kv_kvslimmer_amd import configs, pipeline, synth
@@ -483,10 +584,12 @@ def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016)):
         elt = K0.element_size()
         row = 2 * cfg.head_dim * elt           # K + V bytes of one slot
         plan = []
+        Qws = []
         K, V, n, N = K0, V0, None, cfg.n_slots
         alg = 0
         for r, M in enumerate(cfg.rounds):
             Qw = torch.stack([synth.window_queries(cfg, layer, b, r, dev) for b in range(cfg.batch)])
+            Qws.append(Qw)
             cap = N - M + (cfg.decode_steps if r == len(cfg.rounds) - 1 else 0)
             bufs = pipeline.alloc_round(K, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, n_slots=N,
                                         out_capacity=cap, want_flags=False)
@@ -578,6 +681,11 @@ def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016)):
                         "decode_step_GBps": round(dbytes / (us * 1e-6) / 1e9, 1),
                         "decode_note": "per step: kvs_decode_attn calls enqueued back to back (decode kernel + "
                                        "combine); kernel times from library event marks (include ~1 us of mark gap)"})
+        if cpu:
+            dec = None
+            if cfg.decode_steps:
+                dec = (Kc, Vc, nc, qs, [N + t + 1 for t in range(steps)])
+            res["cpu_oracle"] = cpu_oracle_config(cfg, K0, V0, Qws, dec)
         lines.append(res)
         print(json.dumps(res), flush=True)
         del plan, K0, V0
@@ -847,7 +955,7 @@ def main():
         return
     if args.per_config:
         per_config(dev, [int(x) for x in args.per_config.split(",")],
-                   chunk_sweep=() if args.no_chunk_sweep else (256, 512, 1024, 2016))
+                   chunk_sweep=() if args.no_chunk_sweep else (256, 512, 1024, 2016), cpu=not args.no_cpu_baseline)
         return
     cfg = configs.C2
     if args.copy_calibration:
