@@ -1,4 +1,5 @@
 """CPU: the parts of bench.py's contract that need no GPU."""
+import json
 import os
 import subprocess
 import sys
@@ -51,3 +52,29 @@ def test_cpu_model_and_machine_fields():
     assert m is None or isinstance(m, str)
     info = bench.gpu_clock_info()
     assert set(info) >= {"gpu_peak_sclk_MHz", "gpu_sclk_now", "rocm_version", "hip_runtime"}
+
+
+def test_cpu_oracle_config_on_c1_and_its_summary(tmp_path):
+    """The per-config oracle timing on C1 (every slice measured, plus a small decode) and
+    the per-config summary's CPU table."""
+    import torch
+    import bench
+    from long_context_kv_kvslimmer_amd import configs, pipeline, synth
+    cfg = configs.CONFIGS[1]
+    K0, V0, _ = pipeline.config_cache(cfg, 0, "cpu")
+    Qws = [torch.stack([synth.window_queries(cfg, 0, b, r, "cpu") for b in range(cfg.batch)])
+           for r in range(len(cfg.rounds))]
+    N = K0.shape[2]
+    n = torch.ones(K0.shape[0], K0.shape[1], N, dtype=torch.int32)
+    qs = [torch.randn(1, cfg.q_heads, cfg.head_dim) for _ in range(2)]
+    res = bench.cpu_oracle_config(cfg, K0, V0, Qws, (K0, V0, n, qs, [N - 1, N]))
+    assert res["kind"] == "oracle" and res["merge"] == "measured" and res["slices"].startswith("1 of 1")
+    assert res["merge_s_per_layer"] > 0 and res["cores"] >= 1 and res["cpu_model"]
+    assert res["decode"] == "measured" and res["decode_steps"] == 2
+    line = {"config": "C1 x", "batch": 1, "layers": 1, "rounds": list(cfg.rounds), "merge_ms_per_layer": 0.07,
+            "merge_ms_all_layers": 0.07, "merge_tokens_per_s": 7e6, "merge_algorithmic_MB_per_layer": 0.66,
+            "merge_GBps": 9.0, "kernel_us_per_layer": {}, "cpu_oracle": res}
+    f = tmp_path / "pc.jsonl"
+    f.write_text(json.dumps(line) + "\n")
+    out = bench.summarize_per_config(str(f), "cmd")
+    assert "CPU oracle on the same layer" in out and "| C1 x | 1 of 1" in out and "CPU oracle decode" in out
