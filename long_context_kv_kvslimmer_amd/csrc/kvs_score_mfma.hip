@@ -738,13 +738,21 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
     // the two workgroups that share a CU pair their waves on each SIMD: the one issuing its
     // matrix block goes first, the other fills the vector slots in between
     __builtin_amdgcn_s_setprio(1);
+    // operands of k step ks: K and V rows of the even and the odd slots; the reads of step
+    // ks + 1 are issued before the products of step ks, so they land while those run
+    auto read_ops = [&](int ks, bf16x8_t (&op)[4]) {
+      const int ch = 4 * ks + g4;
+      op[0] = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(n16, ch)));
+      op[1] = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(16 + n16, ch)));
+      op[2] = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(n16, ch)));
+      op[3] = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(16 + n16, ch)));
+    };
+    bf16x8_t ops2[2][4];
+    read_ops(0, ops2[0]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int ch = 4 * ks + g4;
-      const bf16x8_t ke = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(n16, ch)));
-      const bf16x8_t ko = as_bf16x8(*reinterpret_cast<const uint4*>(K_ + chunk_off<D>(16 + n16, ch)));
-      const bf16x8_t ve = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(n16, ch)));
-      const bf16x8_t vo = as_bf16x8(*reinterpret_cast<const uint4*>(V_ + chunk_off<D>(16 + n16, ch)));
+      if (ks + 1 < KS) read_ops(ks + 1, ops2[(ks + 1) & 1]);
+      const bf16x8_t ke = ops2[ks & 1][0], ko = ops2[ks & 1][1], ve = ops2[ks & 1][2], vo = ops2[ks & 1][3];
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         se[q2] = mfma(qop[q2][ks], ke, ks == 0 ? be : se[q2]);
@@ -759,6 +767,14 @@ __global__ __launch_bounds__(kW2 * 64, 2) void p2_mfma_kernel(P2Args a, int64_t 
       gee = mfma(ve, ve, gee);
       goo = mfma(vo, vo, goo);
       geo = mfma(ve, vo, geo);
+    }
+    // order: the reads of steps 0 and 1, then each step's fifteen products followed by the
+    // reads of the step after the next
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);
+      if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     }
     __builtin_amdgcn_s_setprio(0);
     // diagonal element n of a 16x16 result sits in lane n + 16 (n / 4), register n % 4
