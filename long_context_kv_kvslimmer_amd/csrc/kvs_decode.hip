@@ -317,6 +317,18 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_mfma_kernel(DecArgs a, 
     const uint8_t* K_ = kw + buf * M::TILEB;
     const uint8_t* V_ = vw + buf * M::TILEB;
     const int64_t t0 = s0 + (int64_t)(wv + kDecWaves * i) * kT2;
+    // V^T operands of the whole tile first: their reads land while S^T and the softmax run
+    dbf16x8_t vop[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      typedef __attribute__((address_space(3))) dbf16x4_t lds_t;
+      const int col = db * 16 + scol;
+      const int cb = (col & 7) * 2;
+      const dbf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + chunk_off<D>(srow, col >> 3) + cb));
+      const dbf16x4_t v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + chunk_off<D>(srow + 16, col >> 3) + cb));
+      vop[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
     // S^T = K . Q^T: lane holds slots 16 sb + 4 g + r of head c16
     df32x4_t st[2];
 #pragma unroll
@@ -364,15 +376,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_mfma_kernel(DecArgs a, 
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      typedef __attribute__((address_space(3))) dbf16x4_t lds_t;
-      const int col = db * 16 + scol;
-      const int cb = (col & 7) * 2;
-      const dbf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + chunk_off<D>(srow, col >> 3) + cb));
-      const dbf16x4_t v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)(V_ + chunk_off<D>(srow + 16, col >> 3) + cb));
-      const dbf16x8_t vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[db] = d_mfma(vop, phi, acc[db]);
-      acc[db] = d_mfma(vop, plo, acc[db]);
+      acc[db] = d_mfma(vop[db], phi, acc[db]);
+      acc[db] = d_mfma(vop[db], plo, acc[db]);
     }
     if (i + R < nmine) {
       wait_lds();   // this buffer's LDS reads are done before it is refilled
