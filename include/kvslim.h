@@ -88,6 +88,9 @@ typedef enum {
   KVS_DTYPE_INT32_HI_ = 0x7fffffff
 } kvs_dtype;
 
+/* Size limits (KVS_ERR_SHAPE beyond them): B * H_q <= 2^20 query heads, n_slots <= 2^31 - 1,
+ * and B * H_kv * n_slots <= 2^36 slots in all, which keeps every launch grid and index of
+ * the kernels in range; a cache at the limit would take 16 TB at head_dim 128 in bf16. */
 typedef struct {
   int32_t batch;       /* B */
   int32_t n_kv_heads;  /* H_kv */

@@ -38,6 +38,11 @@ int64_t pairs_of(int64_t N, int64_t S, int64_t R) {
   return r > 0 ? r / 2 : 0;
 }
 
+// Size limits of a cache (stated in kvslim.h): they keep every grid size and 32-bit block
+// count of the launches in range.
+constexpr int64_t kMaxQueryHeads = int64_t(1) << 20;
+constexpr int64_t kMaxSlots = int64_t(1) << 36;
+
 // Validates the cache description; fills the kernel shape.
 kvs_status check_cache(const kvs_cache* c, int dtype, kvs::Shape& s) {
   if (!c) return fail(KVS_ERR_NULL, "cache is NULL");
@@ -49,6 +54,10 @@ kvs_status check_cache(const kvs_cache* c, int dtype, kvs::Shape& s) {
   if (c->head_dim != 64 && c->head_dim != 128) return fail(KVS_ERR_SHAPE, "head_dim %d not in {64, 128}", c->head_dim);
   if (c->n_slots < 0) return fail(KVS_ERR_SHAPE, "n_slots < 0");
   if (c->n_slots > (int64_t)INT32_MAX) return fail(KVS_ERR_SHAPE, "n_slots above 2^31 - 1");
+  if ((int64_t)c->batch * c->n_q_heads > kMaxQueryHeads)
+    return fail(KVS_ERR_SHAPE, "batch x n_q_heads above 2^20");
+  if ((int64_t)c->batch * c->n_kv_heads * c->n_slots > kMaxSlots)
+    return fail(KVS_ERR_SHAPE, "batch x n_kv_heads x n_slots above 2^36");
   if (c->stride_b < 0 || c->stride_h < 0 || c->stride_b % c->head_dim || c->stride_h % c->head_dim)
     return fail(KVS_ERR_STRIDE, "strides must be non-negative multiples of head_dim");
   s.B = c->batch;

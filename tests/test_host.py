@@ -98,6 +98,20 @@ def test_score_validation(L):
     assert "n_merge" in L.last_error() or "sm_scale" in L.last_error()
 
 
+def test_cache_size_limits(L):
+    # B * H_q <= 2^20 and B * H_kv * N <= 2^36: checked before anything is sized or launched
+    r = L.round_desc(32, 0, 0, 0, 0.1)
+    assert _score(L, _cache(B=(1 << 15) + 1, H=8, Hq=32, N=64), r) == L.KVS_ERR_SHAPE
+    assert "n_q_heads" in L.last_error()
+    assert _score(L, _cache(B=1 << 10, H=1 << 10, Hq=1 << 10, N=(1 << 16) + 1), r) == L.KVS_ERR_SHAPE
+    assert "n_slots" in L.last_error()
+    assert _score(L, _cache(N=(1 << 31)), r) == L.KVS_ERR_SHAPE
+    # at the limits exactly the shape is accepted (the workspace query sizes it)
+    assert L.workspace_bytes(L.KVS_OP_DECODE, _cache(B=1 << 15, H=8, Hq=32, N=1 << 18), None) > 0
+    assert L.workspace_bytes(L.KVS_OP_DECODE, _cache(B=(1 << 15) + 1, H=8, Hq=32, N=64), None) == 0
+    assert L.workspace_bytes(L.KVS_OP_DECODE, _cache(B=1, H=1 << 6, Hq=1 << 6, N=(1 << 31) - 1), None) == 0
+
+
 def test_merge_weights_validation(L):
     c = _cache()
     r = L.round_desc(32, 0, 32, 100, 0.1)
