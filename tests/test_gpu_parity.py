@@ -54,6 +54,9 @@ CASES = [
     ("d64-f32-partial-g4", 1, 2, 8, 64, 4100, 4100, 8, 0, 32, 0.29, torch.float32, True),
     # 24 pass-1 splits over 256 window-query rows: the wave-per-row combine with every split in one round
     ("d64-bf16-24-splits", 1, 2, 8, 64, 24000, 24000, 32, 0, 16, 1.0, torch.bfloat16, False),
+    # the largest window the calls accept: 65536 queries per head, 512 query blocks in pass 2
+    ("max-window-bf16", 1, 1, 1, 64, 96, 96, 65536, 0, 0, 0.5, torch.bfloat16, False),
+    ("max-window-f32-counts", 1, 1, 1, 128, 70, 72, 65536, 3, 1, 0.4, torch.float32, True),
 ]
 
 
