@@ -293,18 +293,26 @@ def summarize_per_config(jsonl, cmd):
     allrows = [json.loads(line) for line in open(jsonl) if line.startswith("{")]
     rows = [r for r in allrows if "merge_ms_per_layer" in r]
     streams = [r for r in allrows if "chunk_sweep" in r]
-    out = ["# Per-config GPU timings (one layer of each seeded workload)", "", "Made by:", "", "```", cmd, "```", "",
+    out = ["# Per-config GPU timings (every layer of each seeded workload)", "", "Made by:", "", "```", cmd, "```", "",
            "Every merge round is one kvs_score_merge call (for partial rounds the selection runs between the "
-           "scorer's passes and the merge inside the second); median of 5 repetitions after a warm-up, events around "
-           "the layer's rounds.  All layers of a config have one shape, so the model-wide time is the per-layer time "
-           "x layers.  Algorithmic MB: K and V read by both scorer passes, merged rows written once.", "",
-           "| config | batch x layers | rounds (pairs merged) | merge ms / layer | merge ms, all layers | tokens/s | "
-           "algorithmic MB / layer | GB/s |",
-           "|---|---|---|---:|---:|---:|---:|---:|"]
+           "scorer's passes and the merge inside the second).  One layer alone: median of 5 repetitions after a "
+           "warm-up, events around the layer's rounds.  All layers: every layer's cache resident, all layers merged "
+           "back to back, median of 3 passes, on one stream and with the layers alternating over two streams (the "
+           "layers share nothing; both orders give the same merged rows); the whole-model figures use the faster. "
+           " Algorithmic MB: K and V read by both scorer passes, merged rows written once.", "",
+           "| config | batch x layers | rounds (pairs merged) | merge ms, one layer alone | merge ms, all layers "
+           "(one stream / two streams) | per layer in the sequence | tokens/s | algorithmic MB / layer | GB/s |",
+           "|---|---|---|---:|---:|---:|---:|---:|---:|"]
     for r in rows:
+        if "merge_ms_all_layers_one_stream" in r:
+            al = f"{r['merge_ms_all_layers_one_stream']} / {r['merge_ms_all_layers_two_streams']}"
+            per = round(r["merge_ms_all_layers"] / r["layers"], 4)
+            tps, gbs = r["merge_tokens_per_s_all_layers"], r["merge_GBps_all_layers"]
+        else:
+            al, per = f"{r['merge_ms_all_layers']}", r["merge_ms_per_layer"]
+            tps, gbs = r["merge_tokens_per_s"], r["merge_GBps"]
         out.append(f"| {r['config']} | {r['batch']} x {r['layers']} | {r['rounds']} | {r['merge_ms_per_layer']} | "
-                   f"{r['merge_ms_all_layers']} | {r['merge_tokens_per_s']:.3g} | "
-                   f"{r['merge_algorithmic_MB_per_layer']} | {r['merge_GBps']} |")
+                   f"{al} | {per} | {tps:.3g} | {r['merge_algorithmic_MB_per_layer']} | {gbs} |")
     cpu = [r for r in rows if "cpu_oracle" in r]
     if cpu:
         c0 = cpu[0]["cpu_oracle"]
@@ -320,7 +328,7 @@ def summarize_per_config(jsonl, cmd):
             c = r["cpu_oracle"]
             out.append(f"| {r['config']} | {c['slices']} | {c['cores']} | {c['merge']} | {c['merge_s_per_layer']} | "
                        f"{c['merge_s_all_layers']} | {c['merge_tokens_per_s']:.3g} | "
-                       f"{c['merge_s_per_layer'] * 1e3 / r['merge_ms_per_layer']:.0f}x |")
+                       f"{c['merge_s_all_layers'] * 1e3 / r['merge_ms_all_layers']:.0f}x |")
         for r in cpu:
             c = r["cpu_oracle"]
             if "decode_steps" in c:
@@ -562,9 +570,10 @@ def dominant_kernel(ranked):
 def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016), cpu=True):
     """Per-config GPU timings (not the bench line): every merge round of one layer of each
     seeded workload through kvs_score_merge (one call per round), timed with
-    events on the library's stream over `reps` repetitions after one warm-up; all layers of a
-    config have the same shape, so the whole-model time is the per-layer time x layers.  The
-    decode workload (C5) appends one token per step and times each kvs_decode_attn.  With
+    events on the library's stream over `reps` repetitions after one warm-up.  Configs with
+    several layers are also timed with every layer resident and merged back to back
+    (all_layer_timing); the whole-model time is the faster of its one- and two-stream orders.
+    The decode workload (C5) appends one token per step and times each kvs_decode_attn.  With
     `cpu`, the oracle is timed on the same layer (cpu_oracle_config) after the GPU."""
     import statistics
     import torch
@@ -633,6 +642,14 @@ def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016), cpu=True)
                "merge_algorithmic_MB_per_layer": round(alg / 1e6, 2),
                "merge_GBps": round(alg / (ms * 1e-3) / 1e9, 1),
                "kernel_us_per_layer": per_kernel}
+        if cfg.layers > 1:
+            # all layers measured back to back (the line above scales one isolated layer)
+            al = all_layer_timing(cfg, dev, plan)
+            best = min(al["merge_ms_all_layers_one_stream"], al["merge_ms_all_layers_two_streams"])
+            res.update(al)
+            res.update({"merge_ms_all_layers": best, "merge_ms_all_layers_scaled": round(ms * cfg.layers, 3),
+                        "merge_tokens_per_s_all_layers": round(tokens * cfg.layers / (best * 1e-3), 1),
+                        "merge_GBps_all_layers": round(alg * cfg.layers / (best * 1e-3) / 1e9, 1)})
         if cfg.decode_steps:
             bufs = plan[-1][7]
             Kc, Vc, nc = bufs.K, bufs.V, bufs.n
@@ -691,6 +708,79 @@ def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016), cpu=True)
         del plan, K0, V0
         torch.cuda.empty_cache()
     return lines
+
+
+def all_layer_timing(cfg, dev, plan0, reps=3):
+    """Every layer of a config merged back to back: the caches of all layers resident at once
+    (layer 0's rounds are `plan0`), every layer's rounds enqueued on one stream, then with the
+    layers alternating over two streams (fork and join by events; the layers share nothing).
+    Medians over `reps` passes over all layers; both orders must give the same merged rows."""
+    import statistics
+    import torch
+    from long_context_kv_kvslimmer_amd import pipeline, synth
+    plans = [plan0]
+    for layer in range(1, cfg.layers):
+        K, V, _ = pipeline.config_cache(cfg, layer, dev)
+        n, N = None, cfg.n_slots
+        p = []
+        for r, M in enumerate(cfg.rounds):
+            Qw = torch.stack([synth.window_queries(cfg, layer, b, r, dev) for b in range(cfg.batch)])
+            bufs = pipeline.alloc_round(K, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, n_slots=N,
+                                        out_capacity=N - M, want_flags=False)
+            p.append((K, V, n, Qw, M, N, None, bufs))
+            K, V, n, N = bufs.K, bufs.V, bufs.n, N - M
+        plans.append(p)
+
+    def layer_rounds(p):
+        for (Ki, Vi, ni, Qw, M, Ni, _, bufs) in p:
+            pipeline.run_round_fused(Ki, Vi, ni, Qw, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, bufs,
+                                     n_slots=Ni)
+
+    main = torch.cuda.current_stream()
+    side = [torch.cuda.Stream(), torch.cuda.Stream()]
+
+    def one_stream():
+        for p in plans:
+            layer_rounds(p)
+
+    def two_streams():
+        fork = torch.cuda.Event()
+        fork.record(main)
+        for s in side:
+            s.wait_event(fork)
+        for i, p in enumerate(plans):
+            with torch.cuda.stream(side[i % 2]):
+                layer_rounds(p)
+        for s in side:
+            join = torch.cuda.Event()
+            join.record(s)
+            main.wait_event(join)
+
+    def last_rows():
+        torch.cuda.synchronize()
+        return [p[-1][-1].K[..., :p[-1][5] - p[-1][4], :].float().sum().item() for p in plans]
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return statistics.median(times)
+
+    one_ms = timed(one_stream)
+    ref = last_rows()
+    two_ms = timed(two_streams)
+    same = last_rows() == ref
+    del plans[1:]
+    torch.cuda.empty_cache()
+    return {"merge_ms_all_layers_one_stream": round(one_ms, 3), "merge_ms_all_layers_two_streams": round(two_ms, 3),
+            "all_layers_outputs_equal": same}
 
 
 def stream_timing(cfg, dev, reps=5, chunks=(256, 512, 1024, 2016)):

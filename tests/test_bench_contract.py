@@ -74,7 +74,15 @@ def test_cpu_oracle_config_on_c1_and_its_summary(tmp_path):
     line = {"config": "C1 x", "batch": 1, "layers": 1, "rounds": list(cfg.rounds), "merge_ms_per_layer": 0.07,
             "merge_ms_all_layers": 0.07, "merge_tokens_per_s": 7e6, "merge_algorithmic_MB_per_layer": 0.66,
             "merge_GBps": 9.0, "kernel_us_per_layer": {}, "cpu_oracle": res}
+    many = {"config": "C3 y", "batch": 1, "layers": 32, "rounds": [38011], "merge_ms_per_layer": 0.44,
+            "merge_ms_all_layers": 11.7, "merge_ms_all_layers_one_stream": 12.3, "merge_ms_all_layers_two_streams": 11.7,
+            "merge_ms_all_layers_scaled": 14.08, "merge_tokens_per_s": 2.98e8, "merge_tokens_per_s_all_layers": 3.58e8,
+            "merge_algorithmic_MB_per_layer": 1460.88, "merge_GBps": 3320.0, "merge_GBps_all_layers": 3995.5,
+            "all_layers_outputs_equal": True, "kernel_us_per_layer": {}}
     f = tmp_path / "pc.jsonl"
-    f.write_text(json.dumps(line) + "\n")
+    f.write_text(json.dumps(line) + "\n" + json.dumps(many) + "\n")
     out = bench.summarize_per_config(str(f), "cmd")
     assert "CPU oracle on the same layer" in out and "| C1 x | 1 of 1" in out and "CPU oracle decode" in out
+    # several layers: measured whole-model time (one stream / two streams) and the per-layer share of the faster
+    assert "| C3 y | 1 x 32 | [38011] | 0.44 | 12.3 / 11.7 | 0.3656 | 3.58e+08 | 1460.88 | 3995.5 |" in out
+    assert "| C1 x | 1 x 1 | [256] | 0.07 | 0.07 | 0.07 | 7e+06 | 0.66 | 9.0 |" in out
