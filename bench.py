@@ -713,12 +713,13 @@ def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016), cpu=True)
 def all_layer_timing(cfg, dev, plan0, reps=3):
     """Every layer of a config merged back to back: the caches of all layers resident at once
     (layer 0's rounds are `plan0`), every layer's rounds enqueued on one stream, then with the
-    layers alternating over two streams (fork and join by events; the layers share nothing).
-    Medians over `reps` passes over all layers; both orders must give the same merged rows."""
+    layers alternating over two streams (pipeline.run_layers_fused; the layers share
+    nothing).  Medians over `reps` passes over all layers; both orders must give the same
+    merged rows."""
     import statistics
     import torch
     from long_context_kv_kvslimmer_amd import pipeline, synth
-    plans = [plan0]
+    plans = [[(K, V, n, Qw, M, N, bufs) for (K, V, n, Qw, M, N, _, bufs) in plan0]]
     for layer in range(1, cfg.layers):
         K, V, _ = pipeline.config_cache(cfg, layer, dev)
         n, N = None, cfg.n_slots
@@ -727,34 +728,15 @@ def all_layer_timing(cfg, dev, plan0, reps=3):
             Qw = torch.stack([synth.window_queries(cfg, layer, b, r, dev) for b in range(cfg.batch)])
             bufs = pipeline.alloc_round(K, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, n_slots=N,
                                         out_capacity=N - M, want_flags=False)
-            p.append((K, V, n, Qw, M, N, None, bufs))
+            p.append((K, V, n, Qw, M, N, bufs))
             K, V, n, N = bufs.K, bufs.V, bufs.n, N - M
         plans.append(p)
 
-    def layer_rounds(p):
-        for (Ki, Vi, ni, Qw, M, Ni, _, bufs) in p:
-            pipeline.run_round_fused(Ki, Vi, ni, Qw, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent, M, bufs,
-                                     n_slots=Ni)
+    def run(n_streams):
+        return lambda: pipeline.run_layers_fused(plans, cfg.q_heads, cfg.window, cfg.n_sink, cfg.n_recent,
+                                                 n_streams=n_streams)
 
-    main = torch.cuda.current_stream()
-    side = [torch.cuda.Stream(), torch.cuda.Stream()]
-
-    def one_stream():
-        for p in plans:
-            layer_rounds(p)
-
-    def two_streams():
-        fork = torch.cuda.Event()
-        fork.record(main)
-        for s in side:
-            s.wait_event(fork)
-        for i, p in enumerate(plans):
-            with torch.cuda.stream(side[i % 2]):
-                layer_rounds(p)
-        for s in side:
-            join = torch.cuda.Event()
-            join.record(s)
-            main.wait_event(join)
+    one_stream, two_streams = run(1), run(2)
 
     def last_rows():
         torch.cuda.synchronize()

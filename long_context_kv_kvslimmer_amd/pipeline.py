@@ -91,6 +91,40 @@ def run_round_fused(K, V, n, Qw, n_q_heads: int, window: int, n_sink: int, n_rec
     return bufs
 
 
+def run_layers_fused(layers: list, n_q_heads: int, window: int, n_sink: int, n_recent: int,
+                     n_streams: int = 2) -> None:
+    """Merge rounds of several independent layers, enqueued without a host wait.
+
+    `layers[l]` is the list of layer l's rounds, each (K, V, n, Qw, n_merge, n_slots, bufs) in
+    order (round r + 1 reads round r's bufs).  Layer l's rounds go to stream l % n_streams in
+    order; the streams start after the work already on the current stream and the current
+    stream waits for all of them at the end.  Layers share no buffer, so the order of
+    layers across streams does not change a result; what overlaps is one layer's short,
+    latency-bound launches (the selection, the combine, kernel tails) with another layer's
+    scorer passes.  With n_streams = 1 the layers run in order on the current stream."""
+    def rounds(plan):
+        for (K, V, n, Qw, M, N, bufs) in plan:
+            run_round_fused(K, V, n, Qw, n_q_heads, window, n_sink, n_recent, M, bufs, n_slots=N)
+
+    if n_streams <= 1:
+        for plan in layers:
+            rounds(plan)
+        return
+    main = torch.cuda.current_stream()
+    side = [torch.cuda.Stream(device=main.device) for _ in range(n_streams)]
+    fork = torch.cuda.Event()
+    fork.record(main)
+    for s in side:
+        s.wait_event(fork)
+    for i, plan in enumerate(layers):
+        with torch.cuda.stream(side[i % n_streams]):
+            rounds(plan)
+    for s in side:
+        join = torch.cuda.Event()
+        join.record(s)
+        main.wait_event(join)
+
+
 def run_round_given_stats(K, V, n, Qw, lse, O, n_q_heads: int, window: int, n_sink: int, n_recent: int,
                           n_merge: int, bufs: RoundBuffers, n_slots: int | None = None):
     """A whole round through kvs_score_merge_stats: the window statistics lse [B, H_q, W] and

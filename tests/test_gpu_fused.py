@@ -158,3 +158,45 @@ def test_three_query_blocks_are_deterministic():
         for h in range(Hkv):
             check_round_slice(a, K, V, n, Qw, 0, h, N, S, R, M, 1 / math.sqrt(D), label=f"gw384 M{M} h{h}",
                               with_cos=False)
+
+
+def test_layers_over_two_streams_match_one_stream():
+    """pipeline.run_layers_fused: five independent layers, each a partial round then a full
+    round on its output (counts 2 in the second), on one stream and alternating over two
+    streams: every output of every round bit for bit the same (the rounds' oracle parity is
+    checked by the tests above)."""
+    from long_context_kv_kvslimmer_amd import kvslim as L
+    from long_context_kv_kvslimmer_amd import pipeline
+    B, Hkv, Hq, D, N, W, S, R = 1, 2, 8, 128, 2048, 16, 4, 16
+    print("\n[layers] 5 layers x 2 rounds, one stream against two", flush=True)
+    layers = []
+    for layer in range(5):
+        K, V, n, Qw = make_inputs(900 + layer, B, Hkv, Hq, D, N, N, W, torch.bfloat16, False)
+        plan = []
+        Ni, Ki, Vi, ni = N, K, V, None
+        for r, frac in enumerate((0.3, 1.0)):
+            P = L.num_pairs(Ni, S, R)
+            M = int(round(frac * P))
+            bufs = pipeline.alloc_round(Ki, Hq, W, S, R, M, n_slots=Ni)
+            plan.append((Ki, Vi, ni, Qw, M, Ni, bufs))
+            Ki, Vi, ni, Ni = bufs.K, bufs.V, bufs.n, Ni - M
+        layers.append(plan)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [[(b.K[:, :, :Nr - M].clone(), b.V[:, :, :Nr - M].clone(), b.n[:, :, :Nr - M].clone(),
+                  b.src[:, :, :Nr - M].clone(), b.g_self[:, :, :Nr].clone(), b.lse.clone(), b.O.clone())
+                 for (_, _, _, _, M, Nr, b) in plan] for plan in layers]
+
+    pipeline.run_layers_fused(layers, Hq, W, S, R, n_streams=1)
+    one = snapshot()
+    for plan in layers:   # clear every output so the second run must write them again
+        for (_, _, _, _, _, _, b) in plan:
+            for t in (b.K, b.V, b.n, b.src, b.g_self, b.lse, b.O):
+                t.zero_()
+    pipeline.run_layers_fused(layers, Hq, W, S, R, n_streams=2)
+    two = snapshot()
+    for li, (a_l, b_l) in enumerate(zip(one, two)):
+        for r, (a_r, b_r) in enumerate(zip(a_l, b_l)):
+            for name, x, y in zip(("K", "V", "n", "src", "g_self", "lse", "O"), a_r, b_r):
+                _same(x, y, f"layer {li} round {r} {name}")
