@@ -184,6 +184,8 @@ def summarize_stats(stats_csv, title, cmd):
     rows = {}
     for r in csv.DictReader(open(stats_csv)):
         lab = kernel_label(r["Name"])
+        if lab == "combine":   # the two variants serve different callers (window statistics, decode)
+            lab += " (one wave per row)" if "combine_wave_kernel" in r["Name"] else " (one workgroup per row)"
         if lab:
             c, t = rows.get(lab, (0, 0.0))
             rows[lab] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
@@ -567,7 +569,7 @@ def dominant_kernel(ranked):
     return max(ranked, key=lambda n: ranked[n]["ms_per_step"]) if ranked else None
 
 
-def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016), cpu=True):
+def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016), cpu=True, all_layers=True):
     """Per-config GPU timings (not the bench line): every merge round of one layer of each
     seeded workload through kvs_score_merge (one call per round), timed with
     events on the library's stream over `reps` repetitions after one warm-up.  Configs with
@@ -642,7 +644,7 @@ def per_config(dev, which, reps=5, chunk_sweep=(256, 512, 1024, 2016), cpu=True)
                "merge_algorithmic_MB_per_layer": round(alg / 1e6, 2),
                "merge_GBps": round(alg / (ms * 1e-3) / 1e9, 1),
                "kernel_us_per_layer": per_kernel}
-        if cfg.layers > 1:
+        if all_layers and cfg.layers > 1:
             # all layers measured back to back (the line above scales one isolated layer)
             al = all_layer_timing(cfg, dev, plan)
             best = min(al["merge_ms_all_layers_one_stream"], al["merge_ms_all_layers_two_streams"])
@@ -984,6 +986,9 @@ def main():
                     help="time the spectral split (32K tokens, d_model 4096, 128 modes) instead of the bench line")
     ap.add_argument("--diag", action="store_true",
                     help="time the exact-gradient diagnostics on a C2 layer instead of the bench line")
+    ap.add_argument("--no-all-layers", action="store_true",
+                    help="with --per-config: time one layer only, not every layer back to back (a profiled run "
+                         "then sees no kernels of two streams overlapping)")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="with --per-config 6: time only the 512-token-chunk loop (no chunk-size sweep)")
     ap.add_argument("--per-config", type=str, default=None, metavar="1,2,3,4,5,6",
@@ -1027,7 +1032,8 @@ def main():
         return
     if args.per_config:
         per_config(dev, [int(x) for x in args.per_config.split(",")],
-                   chunk_sweep=() if args.no_chunk_sweep else (256, 512, 1024, 2016), cpu=not args.no_cpu_baseline)
+                   chunk_sweep=() if args.no_chunk_sweep else (256, 512, 1024, 2016), cpu=not args.no_cpu_baseline,
+                   all_layers=not args.no_all_layers)
         return
     cfg = configs.C2
     if args.copy_calibration:
